@@ -1,0 +1,293 @@
+"""Pins for the fp64 oracle: values the pages print, closed forms, special
+cases that reduce to simpler recurrences, and identities between independent
+formulations.  CPU only.
+
+Each test names the passage it pins.  Page tags:
+  [LA-KDA]  "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制", blog-3d3.pages.dev/posts/150
+  [K3-ATTN] "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构",
+            forceinjection.github.io/.../kimi_k3_attention.html
+  [K3-NOTES] "Kimi K3", llm.rainlin.net/llm-inference/kimi-k3
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+BIG = 1.0e4   # a logit this large saturates the logistic exactly in float64
+
+
+def _rand_case(rng, T, H, dk, dv, unit_k=True):
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    z = rng.standard_normal((T, H, dk))
+    b = rng.standard_normal((T, H))
+    A = rng.uniform(-1, 1, H)
+    h0 = 0.3 * rng.standard_normal((H, dk, dv))
+    return q, k, v, z, b, A, h0
+
+
+# ---------------------------------------------------------------- printed values
+
+def test_linear_attention_worked_example(golden_dir):
+    """[LA-KDA §3]: (k,v) = (2,5), (3,7), q3 = 4 -> S2 = 31, o3 = 124.
+    Erasure off, alpha = 1 (z = -BIG), beta = 1 (b = +BIG).  The third token
+    carries k3 = 0 so that o3 reads the state built by the first two."""
+    g = json.load(open(os.path.join(golden_dir, "linear_attention_1d.json")))
+    k = np.array([g["k"][0], g["k"][1], 0.0]).reshape(3, 1, 1)
+    v = np.array([g["v"][0], g["v"][1], 0.0]).reshape(3, 1, 1)
+    q = np.array([1.0, 1.0, g["q3"]]).reshape(3, 1, 1)
+    z = np.full((3, 1, 1), -BIG)
+    b = np.full((3, 1), BIG)
+    o, S = oracle.recurrence(q, k, v, z, b, np.zeros(1), erase=False)
+    assert o[1, 0, 0] == g["S2"]          # q2 = 1 reads S2 directly
+    assert o[2, 0, 0] == g["o3"]
+    assert S[0, 0, 0] == g["S2"]
+
+
+def test_delta_rule_hand_check(golden_dir):
+    """[LA-KDA §7.4]: k = (1,1), v = (5,7), beta = (0.5, 0.4), S0 = 0 ->
+    S1 = 2.5, S2 = 4.3 token by token; u = (2.5, 1.8) from the triangular solve.
+    alpha = 1 via z = -BIG.  beta comes through the logistic of its logit."""
+    g = json.load(open(os.path.join(golden_dir, "delta_rule_chunk_c2.json")))
+    beta = np.array(g["beta"])
+    blog = np.log(beta / (1 - beta)).reshape(2, 1)
+    k = np.array(g["k"]).reshape(2, 1, 1)
+    v = np.array(g["v"]).reshape(2, 1, 1)
+    q = np.ones((2, 1, 1))
+    z = np.full((2, 1, 1), -BIG)
+    o, S = oracle.recurrence(q, k, v, z, blog, np.zeros(1))
+    assert o[0, 0, 0] == pytest.approx(g["S1"], abs=1e-14)
+    assert o[1, 0, 0] == pytest.approx(g["S2"], abs=1e-14)
+    oc, Sc, inter = oracle.chunkwise(q, k, v, z, blog, np.zeros(1), chunk=2, keep=True)
+    u = inter[0][0]["Vt"][:, 0]                 # S0 = 0, so V~ = U
+    assert u == pytest.approx(g["u"], abs=1e-14)
+    assert Sc[0, 0, 0] == pytest.approx(g["S2"], abs=1e-14)
+
+
+# ------------------------------------------------------------------ the gate
+
+def test_gate_closed_forms():
+    """[LA-KDA §5.4]: g = -5 sigmoid(e^A z) lies in (-5, 0); z = 0 gives -2.5;
+    the limits are alpha -> 1 and alpha -> e^-5; A enters only as e^A * z."""
+    A = np.array([0.0, math.log(2.0), -1.0])
+    z = np.zeros((1, 3, 4))
+    assert np.all(oracle.gate_log_decay(z, A) == -2.5)
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((50, 3, 8)) * 4
+    g = oracle.gate_log_decay(z, A)
+    assert np.all(g < 0) and np.all(g > -5)
+    # e^A z: A = ln 2 must equal doubling z with A = 0
+    assert np.allclose(oracle.gate_log_decay(z[:, 1:2], A[1:2]),
+                       oracle.gate_log_decay(2 * z[:, 1:2], np.zeros(1)), rtol=0, atol=1e-15)
+    lim = oracle.gate_log_decay(np.array([[[-BIG, BIG]]]), np.zeros(1))
+    assert np.exp(lim[0, 0, 0]) == 1.0
+    assert np.exp(lim[0, 0, 1]) == pytest.approx(math.exp(-5.0), rel=1e-15)
+    # monotone decreasing in z
+    zz = np.linspace(-20, 20, 401).reshape(-1, 1, 1)
+    gg = oracle.gate_log_decay(zz, np.zeros(1)).ravel()
+    assert np.all(np.diff(gg) < 0)
+
+
+def test_beta_saturation():
+    """beta = sigmoid(b) in (0,1) ([LA-KDA §5.1]) or [0,1] ([K3-ATTN §2.1]);
+    saturated logits give exactly 0 and 1 in float64."""
+    bb = oracle.beta_of(np.array([-BIG, 0.0, BIG]))
+    assert bb[0] == 0.0 and bb[1] == 0.5 and bb[2] == 1.0
+
+
+# ---------------------------------------------------- family special cases
+
+def test_linear_attention_limit():
+    """[LA-KDA §3]: erasure off and alpha = 1 leave S_t = S_0 + sum beta_i k_i v_i^T,
+    so o_t = S_0^T q_t + sum_{i<=t} beta_i (q_t . k_i) v_i."""
+    rng = np.random.default_rng(2)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 23, 2, 5, 3)
+    z = np.full_like(z, -BIG)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0, erase=False)
+    beta = 1 / (1 + np.exp(-b))
+    for t in range(23):
+        for h in range(2):
+            ref = h0[h].T @ q[t, h]
+            for i in range(t + 1):
+                ref = ref + beta[i, h] * (q[t, h] @ k[i, h]) * v[i, h]
+            assert np.allclose(o[t, h], ref, atol=1e-12)
+
+
+def test_gated_linear_attention_limit():
+    """[LA-KDA §4] (GLA row) and the expansion of [LA-KDA §7.2]: without erasure,
+    S_t = Diag(gamma_t) S_0 + sum_{i<=t} Diag(gamma_t / gamma_i) beta_i k_i v_i^T
+    with gamma_t = alpha_1 * ... * alpha_t."""
+    rng = np.random.default_rng(3)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 19, 2, 4, 3)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0, erase=False)
+    alpha = np.exp(-5 / (1 + np.exp(-np.exp(A)[None, :, None] * z)))
+    beta = 1 / (1 + np.exp(-b))
+    for h in range(2):
+        for t in range(19):
+            gam_t = np.prod(alpha[: t + 1, h], axis=0)
+            St = gam_t[:, None] * h0[h]
+            for i in range(t + 1):
+                ratio = np.prod(alpha[i + 1: t + 1, h], axis=0)
+                St = St + beta[i, h] * np.outer(ratio * k[i, h], v[i, h])
+            assert np.allclose(o[t, h], St.T @ q[t, h], atol=1e-12)
+
+
+def test_deltanet_limit_matches_printed_chunk_equations():
+    """[LA-KDA §7.3] for alpha = 1, one chunk spanning the sequence:
+    (I + B L) U = B (V - K S_0), L = StrictLowerTri(K K^T);
+    O = Q S_0 + Tril(Q K^T) U;  S_C = S_0 + K^T U."""
+    rng = np.random.default_rng(4)
+    T, H, dk, dv = 11, 1, 6, 4
+    q, k, v, z, b, A, h0 = _rand_case(rng, T, H, dk, dv)
+    z = np.full_like(z, -BIG)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0)
+    Q, K, V, S0 = q[:, 0], k[:, 0], v[:, 0], h0[0]
+    Bm = np.diag(1 / (1 + np.exp(-b[:, 0])))
+    L = np.tril(K @ K.T, -1)
+    U = np.linalg.solve(np.eye(T) + Bm @ L, Bm @ (V - K @ S0))
+    assert np.allclose(o[:, 0], Q @ S0 + np.tril(Q @ K.T) @ U, atol=1e-12)
+    assert np.allclose(S[0], S0 + K.T @ U, atol=1e-12)
+
+
+def test_exact_recall_after_full_write():
+    """[K3-ATTN §2.1] calls (I - beta k k^T) a generalised Householder map that
+    removes the old component along k.  With beta = 1 and |k| = 1 the new state
+    returns v exactly at key k, whatever alpha and S_{t-1}: S_t^T k_t = v_t."""
+    rng = np.random.default_rng(5)
+    T, H, dk, dv = 9, 3, 7, 5
+    q, k, v, z, b, A, h0 = _rand_case(rng, T, H, dk, dv)
+    b = np.full_like(b, BIG)
+    o, _ = oracle.recurrence(k, k, v, z, b, A, h0)   # read with q_t = k_t
+    assert np.allclose(o, v, atol=1e-12)
+
+
+def test_pure_decay_when_beta_is_zero():
+    """beta = 0 writes nothing: S_t = Diag(prod alpha) S_0 ([LA-KDA §5.2] with
+    the delta and write terms scaled by beta)."""
+    rng = np.random.default_rng(6)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 13, 2, 4, 3)
+    b = np.full_like(b, -BIG)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0)
+    alpha = np.exp(-5 / (1 + np.exp(-np.exp(A)[None, :, None] * z)))
+    for t in range(13):
+        gam = np.prod(alpha[: t + 1], axis=0)
+        St = gam[:, :, None] * h0
+        assert np.allclose(o[t], np.einsum("hkv,hk->hv", St, q[t]), atol=1e-14)
+
+
+# ------------------------------------------------------------------ identities
+
+@pytest.mark.parametrize("seed", [7, 8])
+def test_three_step_dplr_equals_matrix_form(seed):
+    """The three-step DPLR update of [K3-ATTN §2.2], the delta form of
+    [K3-NOTES] and the explicit d_k x d_k transition of [LA-KDA §5.2] agree."""
+    rng = np.random.default_rng(seed)
+    args = _rand_case(rng, 17, 2, 6, 5)
+    o1, S1 = oracle.recurrence(*args)
+    o2, S2 = oracle.recurrence_dplr(*args)
+    o3, S3 = oracle.recurrence_matrix(*args)
+    for o, S in ((o2, S2), (o3, S3)):
+        assert np.allclose(o, o1, atol=1e-13) and np.allclose(S, S1, atol=1e-13)
+
+
+@pytest.mark.parametrize("T,chunk", [(70, 16), (64, 16), (5, 16), (37, 8), (130, 64)])
+def test_chunkwise_equals_recurrence(T, chunk):
+    """[LA-KDA §7]: the chunked form reaches the token recurrence's result,
+    with a ragged last chunk, with and without an initial state."""
+    rng = np.random.default_rng(T + chunk)
+    q, k, v, z, b, A, h0 = _rand_case(rng, T, 2, 8, 6)
+    for init in (None, h0):
+        o1, S1 = oracle.recurrence(q, k, v, z, b, A, init)
+        o2, S2 = oracle.chunkwise(q, k, v, z, b, A, init, chunk=chunk)
+        assert np.abs(o1 - o2).max() < 1e-12
+        assert np.abs(S1 - S2).max() < 1e-12
+
+
+def test_chunkwise_slow_decay_long_memory():
+    """Near-1 decay (very negative z) keeps the initial state alive across many
+    chunks; the chunked form must still agree."""
+    rng = np.random.default_rng(9)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 96, 1, 8, 8)
+    z = z - 6.0
+    o1, S1 = oracle.recurrence(q, k, v, z, b, A, h0)
+    o2, S2 = oracle.chunkwise(q, k, v, z, b, A, h0, chunk=16)
+    assert np.abs(S1).max() > 1e-2
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(S1 - S2).max() < 1e-12
+
+
+def test_linear_in_values_and_initial_state():
+    """For fixed q, k, z, b, A the outputs and final state are linear in (V, S_0):
+    every operation on the pages is linear in the state and in v."""
+    rng = np.random.default_rng(10)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 21, 2, 5, 4)
+    v2 = rng.standard_normal(v.shape)
+    h2 = rng.standard_normal(h0.shape)
+    a1, a2 = 0.7, -1.3
+    o1, S1 = oracle.recurrence(q, k, v, z, b, A, h0)
+    o2, S2 = oracle.recurrence(q, k, v2, z, b, A, h2)
+    o3, S3 = oracle.recurrence(q, k, a1 * v + a2 * v2, z, b, A, a1 * h0 + a2 * h2)
+    assert np.allclose(o3, a1 * o1 + a2 * o2, atol=1e-12)
+    assert np.allclose(S3, a1 * S1 + a2 * S2, atol=1e-12)
+
+
+def test_value_columns_are_independent():
+    """Permuting the d_v columns of v and S_0 permutes those of o and S."""
+    rng = np.random.default_rng(11)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 15, 2, 4, 6)
+    perm = rng.permutation(6)
+    o1, S1 = oracle.recurrence(q, k, v, z, b, A, h0)
+    o2, S2 = oracle.recurrence(q, k, v[..., perm], z, b, A, h0[..., perm])
+    assert np.allclose(o2, o1[..., perm], atol=1e-14)
+    assert np.allclose(S2, S1[..., perm], atol=1e-14)
+
+
+def test_resume_from_returned_state():
+    """Running T1 tokens then T2 tokens from the returned state equals one run
+    over T1 + T2 ([K3-NOTES]: the state is stored and handed back)."""
+    rng = np.random.default_rng(12)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 40, 2, 5, 4)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0)
+    oa, Sa = oracle.recurrence(q[:25], k[:25], v[:25], z[:25], b[:25], A, h0)
+    ob, Sb = oracle.recurrence(q[25:], k[25:], v[25:], z[25:], b[25:], A, Sa)
+    assert np.allclose(np.concatenate([oa, ob]), o, atol=1e-13)
+    assert np.allclose(Sb, S, atol=1e-13)
+
+
+def test_packed_equals_separate_and_empty_sequence():
+    """A packed batch restarts at every offset; an empty sequence returns its
+    initial state unchanged."""
+    rng = np.random.default_rng(13)
+    lens = [5, 0, 17, 1]
+    T = sum(lens)
+    q, k, v, z, b, A, _ = _rand_case(rng, T, 2, 4, 3)
+    h0 = rng.standard_normal((len(lens), 2, 4, 3))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, S = oracle.packed(q[None], k[None], v[None], z[None], b[None], A, h0, cu)
+    for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+        if e == a:
+            assert np.array_equal(S[s], h0[s])
+            continue
+        o_s, S_s = oracle.recurrence(q[a:e], k[a:e], v[a:e], z[a:e], b[a:e], A, h0[s])
+        assert np.array_equal(o[a:e], o_s) and np.array_equal(S[s], S_s)
+
+
+def test_decode_step_equals_one_token_of_prefill():
+    """[K3-NOTES]: the recurrent call and the chunked call share state semantics;
+    one decode step equals one token of the recurrence."""
+    rng = np.random.default_rng(14)
+    N, H, dk, dv = 3, 2, 4, 5
+    q, k, v, z, b, A, _ = _rand_case(rng, N, H, dk, dv)
+    st = rng.standard_normal((N, H, dk, dv))
+    o, S = oracle.decode_step(q, k, v, z, b, A, st)
+    for n in range(N):
+        o1, S1 = oracle.recurrence(q[n:n + 1], k[n:n + 1], v[n:n + 1], z[n:n + 1],
+                                   b[n:n + 1], A, st[n])
+        assert np.allclose(o[n], o1[0], atol=1e-15) and np.allclose(S[n], S1, atol=1e-15)
