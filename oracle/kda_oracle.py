@@ -211,7 +211,7 @@ def chunkwise(q, k, v, z, b, A, h0=None, chunk=16, keep=False):
             Gam = np.exp(G)
             W = Tm @ (K * Gam)
             U = Tm @ V
-            S0 = S[h]
+            S0 = S[h].copy()
             Vt = U - W @ S0
             o[c0:c1, h] = (Q * Gam) @ S0 + Aqk @ Vt
             Kbar = K * np.exp(G[-1][None, :] - G)

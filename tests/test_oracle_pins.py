@@ -291,3 +291,14 @@ def test_decode_step_equals_one_token_of_prefill():
         o1, S1 = oracle.recurrence(q[n:n + 1], k[n:n + 1], v[n:n + 1], z[n:n + 1],
                                    b[n:n + 1], A, st[n])
         assert np.allclose(o[n], o1[0], atol=1e-15) and np.allclose(S[n], S1, atol=1e-15)
+
+
+def test_chunkwise_records_the_incoming_state():
+    """The recorded per-chunk S_0 is the state entering that chunk, i.e. the
+    recurrence's state after the preceding tokens."""
+    rng = np.random.default_rng(15)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 40, 1, 4, 4)
+    _, _, inter = oracle.chunkwise(q, k, v, z, b, A, h0, chunk=16, keep=True)
+    assert np.array_equal(inter[0][0]["S0"], h0[0])
+    _, S16 = oracle.recurrence(q[:16], k[:16], v[:16], z[:16], b[:16], A, h0)
+    assert np.allclose(inter[1][0]["S0"], S16[0], atol=1e-13)
