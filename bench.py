@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA core (libkda) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one kda_chunk_fwd over the long-context workload: B=1, H=12
+(one GPU's share of 96 heads), T=2^20 tokens, d_k=d_v=128, chunk 64, bf16
+q/k/v, fp32 gate and beta logits, fp32 initial state; inputs drawn on the
+device (seed 0) and resident in HBM before the timed region.  Value = tokens/s
+of the whole call (prep + intra + chain kernels), inputs already in HBM.
+
+Also reported: per-kernel durations from HIP events recorded by libkda on the
+stream its kernels run on (kda_chunk_fwd_timed), the roofline of the dominant
+kernel, the decode workload (256 sequences x 12 heads, 16 single-token
+steps), and the fp64 CPU oracle timed on a bounded prefix of the same
+workload.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (12 heads, d=128, 1M ctx) + MFMA%; decode tokens/s + HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+# algorithmic work per token and head of the prefill (d = 128, C = 64):
+#   bytes: q, k, v bf16 (3 x 256) + z fp32 (512) + beta logit (4) + o bf16 (256)
+#   flops: 6 d_k d_v + C (3 d_k + 2 d_v)
+PREFILL_BYTES = 1540
+PREFILL_FLOPS = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
+# the same bytes split by kernel: the intra kernel must read q, k, v, z, b;
+# the chain kernel must write o (the 64 KiB initial/final states per head are
+# added per launch)
+INTRA_BYTES = 1284
+CHAIN_BYTES = 256
+# decode: read + write one fp32 state (2 x 64 KiB) + 1540 B of per-token I/O
+DECODE_BYTES = 2 * 128 * 128 * 4 + PREFILL_BYTES
+
+
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def _event(h):
+    e = ctypes.c_void_p()
+    if h.hipEventCreate(ctypes.byref(e)) != 0:
+        raise RuntimeError("hipEventCreate failed")
+    return e
+
+
+def _elapsed(h, a, b) -> float:
+    ms = ctypes.c_float()
+    if h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return float(ms.value)
+
+
+def bench_prefill(args, kda, torch, KI):
+    case = KI.CONFIGS["long_1m"]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = KI.make_prefill(case, device=dev, seed=0)
+    torch.cuda.synchronize()
+    print(f"[bench] long_1m inputs drawn on the device in {time.time() - t0:.1f} s", flush=True)
+    B, T, H, dk, dv, N, C = d["B"], d["T"], d["H"], d["dk"], d["dv"], d["N"], d["chunk"]
+    L = kda.lib()
+    wsb = kda.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, C, torch.bfloat16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    h = _hip()
+    nsteps = args.warmup + args.steps
+    evs = [[_event(h) for _ in range(4)] for _ in range(nsteps)]
+    ptrs = (d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["z"].data_ptr(),
+            d["b"].data_ptr(), d["A"].data_ptr(), d["h0"].data_ptr(), None, B, T, H, dk, dv, N,
+            C, 1, o.data_ptr(), hT.data_ptr(), ws.data_ptr(), wsb)
+
+    def step(i):
+        arr = (ctypes.c_void_p * 4)(*[e.value for e in evs[i]])
+        rc = L.kda_chunk_fwd_timed(*ptrs, arr, 4, stream)
+        if rc != 0:
+            raise RuntimeError(L.kda_status_string(rc).decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {"prep": [], "intra": [], "chain": [], "call": []}
+    for i in range(args.warmup, nsteps):
+        e = evs[i]
+        per["prep"].append(_elapsed(h, e[0], e[1]))
+        per["intra"].append(_elapsed(h, e[1], e[2]))
+        per["chain"].append(_elapsed(h, e[2], e[3]))
+        per["call"].append(_elapsed(h, e[0], e[3]))
+    for row in evs:
+        for e in row:
+            h.hipEventDestroy(e)
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] prefill: {ms_per_step:.3f} ms/step wall; events (ms): "
+          + ", ".join(f"{k} {v:.3f}" for k, v in avg.items()), flush=True)
+    tokens = B * T
+    units = tokens * H
+    kernels = {
+        "fast_intra_kernel": {"ms": avg["intra"], "alg_bytes": INTRA_BYTES * units},
+        "fast_chain_kernel": {"ms": avg["chain"],
+                              "alg_bytes": CHAIN_BYTES * units + 2 * N * H * dk * dv * 4},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    achieved = kd["alg_bytes"] / (kd["ms"] * 1e-3) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None}
+    call_gbs = PREFILL_BYTES * units / (avg["call"] * 1e-3) / 1e9
+    call_tfs = PREFILL_FLOPS * units / (avg["call"] * 1e-3) / 1e12
+    extra = {
+        "call_ms_events": round(avg["call"], 4),
+        "kernels_ms": {k: round(v, 4) for k, v in avg.items() if k != "call"},
+        "path_alg_GBps": round(call_gbs, 1),
+        "path_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
+        "path_alg_TFLOPs": round(call_tfs, 2),
+        "mfma_frac_algorithmic": round(call_tfs / MFMA_BF16_PEAK_TFS, 4),
+    }
+    cpu_inputs = {k: d[k][:, :args.cpu_tokens].cpu() for k in ("q", "k", "v", "z", "b")}
+    cpu_inputs.update(A=d["A"].cpu(), h0=d["h0"].cpu())
+    del ws, o, hT, d
+    torch.cuda.empty_cache()
+    return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, cpu_inputs
+
+
+def bench_decode(args, kda, torch, KI):
+    case = KI.CONFIGS["decode_256"]
+    dev = torch.device("cuda:0")
+    run = KI.make_decode(case, device=dev, seed=0)
+    A, st = run["A"], run["state"]
+    steps = run["steps"]
+    for s in steps[:2]:                       # warm-up on a scratch copy
+        kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, st.clone())
+    torch.cuda.synchronize()
+    times = []
+    for rep in range(args.decode_reps):
+        for s in steps:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, st)
+            b.record()
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in times]
+    ms.sort()
+    med = ms[len(ms) // 2]
+    mean = sum(ms) / len(ms)
+    units = run["N"] * run["H"]
+    gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
+    return {
+        "workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v",
+        "steps_timed": len(ms),
+        "ms_per_step_mean": round(mean, 4),
+        "ms_per_step_median": round(med, 4),
+        "tokens_per_s": round(run["N"] / (mean * 1e-3), 1),
+        "alg_GBps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
+                "algorithmic bytes and may exceed the HBM rate",
+    }
+
+
+def cpu_baseline(inp, torch):
+    import oracle
+    n = inp["q"].shape[1]
+    t0 = time.perf_counter()
+    oracle.recurrence(inp["q"][0], inp["k"][0], inp["v"][0], inp["z"][0], inp["b"][0], inp["A"],
+                      inp["h0"][0])
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of long_1m, all 12 heads, fp64 numpy token "
+                      f"recurrence, single thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-reps", type=int, default=4, help="passes over the 16 decode steps")
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_77_amd as kda
+    import kda_inputs as KI
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.lib()
+
+    value, ms, roof, extra, cpu_inp = bench_prefill(args, kda, torch, KI)
+    dec = None if args.no_decode else bench_decode(args, kda, torch, KI)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_inp, torch)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_1m: B=1, H=12, T=1048576, d_k=d_v=128, chunk=64, bf16 "
+                               "q/k/v, fp32 logits and state, seed 0",
+                   "B": 1, "T": 1 << 20, "H": 12, "dk": 128, "dv": 128, "chunk": 64},
+        "roofline": roof, "cpu_baseline": cpu, "prefill": extra, "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+"""Python binding of libkda, the MI355X Kimi Delta Attention (KDA) core.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so (built in-tree by `python -m gated_delta_rule_77_amd.build`).
+PyTorch supplies device memory and the current stream.  There is no fallback:
+if the library is not built, or a tensor is not on a GPU, the call raises.
+
+Names follow the C ABI in include/kda.h:
+    kda_chunk_fwd(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
+                  chunk_size=64, output_final_state=True, workspace=None) -> (o, hT)
+    kda_recurrent_step(q, k, v, g, beta, A, state) -> o     (state updated in place)
+    kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
+`g` are the raw per-channel gate logits and `beta` the raw write-strength
+logits; both activations run inside the kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step",
+    "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
+    "kda_recurrent_step_supported", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+EXPORTED_SYMBOLS = (
+    "kda_status_string", "kda_chunk_fwd_supported", "kda_recurrent_step_supported",
+    "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_debug_floats",
+    "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step",
+)
+
+
+class KdaError(RuntimeError):
+    """A libkda call returned a non-OK status."""
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise KdaError(f"{lib_path} is not built; run `python -m gated_delta_rule_77_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    vp, f, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [i]
+    L.kda_chunk_fwd_supported.restype = i
+    L.kda_chunk_fwd_supported.argtypes = [i, i, i, i]
+    L.kda_recurrent_step_supported.restype = i
+    L.kda_recurrent_step_supported.argtypes = [i, i, i]
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    L.kda_chunk_fwd_debug_floats.restype = sz
+    L.kda_chunk_fwd_debug_floats.argtypes = [i, i, i, i, i, i, i,
+                                             ctypes.POINTER(sz), ctypes.POINTER(i)]
+    chunk_args = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, i, i, i, vp, f, vp, sz]
+    L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd.argtypes = chunk_args + [vp]
+    L.kda_chunk_fwd_debug.restype = i
+    L.kda_chunk_fwd_debug.argtypes = chunk_args + [f, f, vp]
+    L.kda_chunk_fwd_timed.restype = i
+    L.kda_chunk_fwd_timed.argtypes = chunk_args + [ctypes.POINTER(vp), i, vp]
+    L.kda_recurrent_step.restype = i
+    L.kda_recurrent_step.argtypes = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, vp]
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise KdaError(f"{what}: {lib().kda_status_string(rc).decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _req(t, name, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def kda_chunk_fwd_supported(dk: int, dv: int, chunk: int, dtype) -> bool:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return bool(lib().kda_chunk_fwd_supported(dk, dv, chunk, code))
+
+
+def kda_recurrent_step_supported(dk: int, dv: int, dtype) -> bool:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return bool(lib().kda_recurrent_step_supported(dk, dv, code))
+
+
+def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, code))
+
+
+def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens):
+    torch = _torch()
+    _req(q, "q")
+    dev = q.device
+    dt = q.dtype
+    _dtype_code(q)
+    _req(k, "k", dt, dev)
+    _req(v, "v", dt, dev)
+    _req(g, "g", torch.float32, dev)
+    _req(beta, "beta", torch.float32, dev)
+    _req(A, "A", torch.float32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or g.shape != q.shape:
+        raise ValueError("k, g must match q [B, T, H, dk] and v must be [B, T, H, dv]")
+    if beta.shape != (B, T, H) or A.shape != (H,):
+        raise ValueError("beta must be [B, T, H] and A must be [H]")
+    if cu_seqlens is not None:
+        _req(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if B != 1 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens needs B == 1 and a 1-D int32 tensor of N+1 offsets")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be [{N}, {H}, {dk}, {dv}]")
+    return B, T, H, dk, dv, N, dev, dt
+
+
+def kda_chunk_fwd(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
+                  chunk_size: int = 64, output_final_state: bool = True, workspace=None):
+    """Chunked prefill.  q, k [B, T, H, dk], v [B, T, H, dv] (bf16 or fp32);
+    g [B, T, H, dk] fp32 gate logits; beta [B, T, H] fp32 logits; A [H] fp32;
+    initial_state [N, H, dk, dv] fp32 or None; cu_seqlens int32 [N+1] or None.
+    Returns (o [B, T, H, dv], final_state [N, H, dk, dv] fp32 or None)."""
+    return _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size,
+                  output_final_state, workspace, debug=False)
+
+
+def kda_chunk_fwd_debug(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
+                        chunk_size: int = 64, workspace=None):
+    """kda_chunk_fwd plus per-chunk intermediates: returns (o, hT, dict) with
+    G [Cn, H, c, dk], Akk/Aqk/T [Cn, H, c, c], S0 [Cn, H, dk, dv] (fp32) and
+    the number of chunks actually used is not returned: chunks are numbered
+    sequence by sequence in token order, unused slots are left untouched."""
+    return _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size,
+                  True, workspace, debug=True)
+
+
+def _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size, output_final_state,
+           workspace, debug):
+    torch = _torch()
+    B, T, H, dk, dv, N, dev, dt = _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens)
+    code = _dtype_code(q)
+    L = lib()
+    need = int(L.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk_size, code))
+    if need == 0:
+        _check(2 if not L.kda_chunk_fwd_supported(dk, dv, chunk_size, code) else 1,
+               "kda_chunk_fwd_workspace_bytes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(initial_state),
+            _ptr(cu_seqlens), B, T, H, dk, dv, N, chunk_size, code, _ptr(o), _ptr(hT),
+            _ptr(workspace), workspace.numel())
+    if not debug:
+        _check(L.kda_chunk_fwd(*args, _stream(dev)), "kda_chunk_fwd")
+        return o, hT
+    st = ctypes.c_size_t(0)
+    cap = ctypes.c_int(0)
+    nf = int(L.kda_chunk_fwd_debug_floats(B, T, H, dk, dv, N, chunk_size, ctypes.byref(st),
+                                          ctypes.byref(cap)))
+    dbg = torch.zeros(max(nf, 1), dtype=torch.float32, device=dev)
+    dst = torch.zeros(max(int(st.value), 1), dtype=torch.float32, device=dev)
+    _check(L.kda_chunk_fwd_debug(*args, _ptr(dbg), _ptr(dst), _stream(dev)), "kda_chunk_fwd_debug")
+    Cn, c = cap.value, chunk_size
+    per = c * dk + 3 * c * c
+    d = dbg[: Cn * H * per].view(Cn, H, per)
+    inter = dict(
+        G=d[:, :, : c * dk].reshape(Cn, H, c, dk),
+        Akk=d[:, :, c * dk: c * dk + c * c].reshape(Cn, H, c, c),
+        Aqk=d[:, :, c * dk + c * c: c * dk + 2 * c * c].reshape(Cn, H, c, c),
+        T=d[:, :, c * dk + 2 * c * c:].reshape(Cn, H, c, c),
+        S0=dst[: Cn * H * dk * dv].view(Cn, H, dk, dv),
+        capacity=Cn,
+    )
+    return o, hT, inter
+
+
+def kda_recurrent_step(q, k, v, g, beta, A, state):
+    """One decode token per sequence: q, k [N, H, dk], v [N, H, dv] (bf16 or
+    fp32), g [N, H, dk] fp32, beta [N, H] fp32, A [H] fp32, state
+    [N, H, dk, dv] fp32 (updated in place).  Returns o [N, H, dv]."""
+    torch = _torch()
+    _req(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _req(k, "k", dt, dev)
+    _req(v, "v", dt, dev)
+    _req(g, "g", torch.float32, dev)
+    _req(beta, "beta", torch.float32, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(state, "state", torch.float32, dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, dv):
+        raise ValueError("k, g must match q [N, H, dk] and v must be [N, H, dv]")
+    if beta.shape != (N, H) or A.shape != (H,) or state.shape != (N, H, dk, dv):
+        raise ValueError("beta [N, H], A [H] and state [N, H, dk, dv] expected")
+    o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    rc = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                                  _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(dev))
+    _check(rc, "kda_recurrent_step")
+    return o

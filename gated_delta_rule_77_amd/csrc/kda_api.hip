@@ -1,0 +1,150 @@
+// C ABI of libkda: argument validation, workspace sizing and dispatch.
+// Declarations and the contract of every entry point are in include/kda.h.
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+using namespace kda;
+
+namespace {
+
+bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+bool chunk_shape_supported(int dk, int dv, int chunk) { return generic_supported(dk, dv, chunk); }
+
+// sizes shared by the prefill entry points; false on invalid arguments
+bool prefill_sizes_ok(int B, int T, int H, int dk, int dv, int N, int chunk) {
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || N < 0 || chunk < 1) return false;
+    if ((long long)B * T > 0x7fffffffLL) return false;            // token index fits int32
+    if ((long long)N * H > 0x7fffffffLL) return false;
+    return chunk_capacity(B, T, N, chunk) >= 0;
+}
+
+kda_status_t run_prefill(const void* q, const void* k, const void* v, const float* z,
+                         const float* b, const float* A, const float* h0, const int* cu,
+                         int B, int T, int H, int dk, int dv, int N, int chunk,
+                         kda_dtype_t dtype, void* o, float* hT, void* ws, size_t ws_bytes,
+                         float* dbg_intra, float* dbg_state, hipEvent_t* ev, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
+    if (cu) {
+        if (B != 1) return KDA_ERR_INVALID_ARG;
+    } else if (N != B) {
+        return KDA_ERR_INVALID_ARG;
+    }
+    if (!chunk_shape_supported(dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    const long long tokens = (long long)B * T;
+    if (tokens > 0 && (!q || !k || !v || !z || !b || !o)) return KDA_ERR_INVALID_ARG;
+    if (!A) return KDA_ERR_INVALID_ARG;
+    const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
+    const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, fast);
+    if (L.total == 0) return KDA_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return KDA_ERR_WORKSPACE;
+
+    ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.A = A; a.h0 = h0; a.cu = cu;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.C = chunk;
+    a.o = o; a.hT = hT; a.ws = static_cast<uint8_t*>(ws); a.L = L;
+    a.dbg_intra = dbg_intra; a.dbg_state = dbg_state; a.ev = ev;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = ev ? hipEventRecord(ev[0], a.stream) : hipSuccess;
+    if (e == hipSuccess) e = launch_prep(a);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], a.stream);
+    if (e == hipSuccess) e = fast ? launch_fast(a) : launch_generic(a, dtype == KDA_BF16);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], a.stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: shape or dtype not supported";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+int kda_chunk_fwd_supported(int dk, int dv, int chunk, kda_dtype_t dtype) {
+    return dtype_ok(dtype) && chunk_shape_supported(dk, dv, chunk) ? 1 : 0;
+}
+
+int kda_recurrent_step_supported(int dk, int dv, kda_dtype_t dtype) {
+    return dtype_ok(dtype) && decode_supported(dk, dv) ? 1 : 0;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk,
+                                     kda_dtype_t dtype) {
+    if (!dtype_ok(dtype) || !prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return 0;
+    if (!chunk_shape_supported(dk, dv, chunk)) return 0;
+    const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
+    return ws_layout(B, T, H, dk, dv, N, chunk, fast).total;
+}
+
+size_t kda_chunk_fwd_debug_floats(int B, int T, int H, int dk, int dv, int N, int chunk,
+                                  size_t* dbg_state_floats, int* chunk_capacity_out) {
+    if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return 0;
+    const int cap = chunk_capacity(B, T, N, chunk);
+    if (dbg_state_floats) *dbg_state_floats = (size_t)cap * H * dk * dv;
+    if (chunk_capacity_out) *chunk_capacity_out = cap;
+    return (size_t)cap * H * ((size_t)chunk * dk + 3 * (size_t)chunk * chunk);
+}
+
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_logits,
+                           const float* beta_logits, const float* A, const float* h0,
+                           const int* cu_seqlens, int B, int T, int H, int dk, int dv, int N,
+                           int chunk, kda_dtype_t dtype, void* o, float* hT, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                       stream);
+}
+
+kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const void* v,
+                                 const float* g_logits, const float* beta_logits, const float* A,
+                                 const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                 int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                 float* hT, void* workspace, size_t workspace_bytes,
+                                 float* dbg_intra, float* dbg_state, void* stream) {
+    return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, dbg_intra, dbg_state,
+                       nullptr, stream);
+}
+
+kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
+                                 const float* g_logits, const float* beta_logits, const float* A,
+                                 const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                 int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                 float* hT, void* workspace, size_t workspace_bytes,
+                                 void* const* events, int n_events, void* stream) {
+    if (!events || n_events < 4) return KDA_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; i++)
+        if (!events[i]) return KDA_ERR_INVALID_ARG;
+    hipEvent_t ev[4];
+    for (int i = 0; i < 4; i++) ev[i] = static_cast<hipEvent_t>(events[i]);
+    return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, ev,
+                       stream);
+}
+
+kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, const float* g_logits,
+                                const float* beta_logits, const float* A, float* state, void* o,
+                                int N, int H, int dk, int dv, kda_dtype_t dtype, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g_logits || !beta_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    hipError_t e = launch_decode(q, k, v, g_logits, beta_logits, A, state, o, N, H, dk, dv,
+                                 dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,552 @@
+// Chunked KDA prefill on MFMA: bf16 inputs, d_k = d_v = 128, chunk C = 64.
+//
+// Sources:
+//   [LA-KDA]  "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制", blog-3d3.pages.dev/posts/150
+//   [K3-ATTN] "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构"
+//
+// Per chunk (positions i, j in 0..63, channels c; G = in-chunk inclusive
+// cumulative log-decay; Gamma = e^G), the chunked form of [LA-KDA §7] with
+// the decay ([LA-KDA §7.2]) and the delta correction ([LA-KDA §7.3]):
+//   A_kk[i,j] = beta_i sum_c k_ic k_jc e^{G_ic - G_jc}   (j < i)
+//   A_qk[i,j] =        sum_c q_ic k_jc e^{G_ic - G_jc}   (j <= i)
+//   T  = (I + A_kk)^{-1} Diag(beta)          (the UT transform)
+//   W  = T (K . Gamma),  U = T V             (the WY pair; no S dependence)
+//   V~ = U - W S
+//   O  = (Q . Gamma) S + A_qk V~  =  Q' S + Y,   Q' = Q . Gamma - A_qk W,  Y = A_qk U
+//   S <- Diag(Gamma_C) S + Kbar^T V~,   Kbar = K . e^{G_C - G}
+// Only the two C x C matrices A_kk and A_qk are formed: the diagonal and the
+// low-rank terms share the same k ([K3-ATTN §2.2]).
+//
+// Two kernels:
+//   intra  one workgroup per (chunk, head), all chunks in parallel: gate,
+//          cumulative decay, A_kk and A_qk on MFMA, the fp32 triangular
+//          inverse, W, U, Q', Y and Kbar on MFMA.  It writes them as bf16
+//          operand fragments already in the order the chain kernel's lanes
+//          load them (one 16-byte load per lane per fragment).
+//   chain  one workgroup per (sequence, head, 16-column slice of the state):
+//          walks the sequence's chunks in order carrying its fp32 state
+//          slice; per chunk it forms V~, the output rows and the new state.
+//          Columns of the state evolve independently (the correction u_j
+//          depends only on column j), so 8 slices run as 8 chains.
+//
+// Exponent range: the lower bound g > -5 ([LA-KDA §5.4]) keeps every
+// reciprocal decay factor inside a 16-token sub-tile ([LA-KDA §8]) below
+// e^{80} < FLT_MAX.  A_kk/A_qk tiles of row block r use the cumulative decay
+// just before block r as reference: the row factor e^{G_i - G_ref} <= 1, the
+// column factor e^{G_ref - G_j} <= 1 off the diagonal and < e^{80} on it.
+// Gamma, Kbar and gamma_C only ever carry factors <= 1.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+using namespace fast;
+
+namespace {
+
+// acc += A (16x16, row-major, lda) * B (16x16, row-major, ldb), fp32 MFMA
+__device__ __forceinline__ f32x4 mm16_f32(f32x4 acc, const float* A, int lda, const float* B,
+                                          int ldb, int n16, int g4) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        acc = mfma_f32(A[n16 * lda + 4 * ks + g4], B[(4 * ks + g4) * ldb + n16], acc);
+    return acc;
+}
+
+__device__ __forceinline__ void load8f(const float* p, float* out) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <bool DBG>
+__global__ __launch_bounds__(256, 2)
+void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, const float* __restrict__ z,
+                       const float* __restrict__ bl, const float* __restrict__ A,
+                       const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
+                       uint8_t* __restrict__ recs, float* __restrict__ dbg)
+{
+    const int cid = blockIdx.x, h = blockIdx.y;
+    if (cid >= hdr[0]) return;
+    const int4 cd = chunks[cid];
+    const int tok0 = cd.y, len = cd.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
+    float* dbase = DBG ? dbg + ((size_t)cid * H + h) * (64 * 128 + 3 * 64 * 64) : nullptr;
+
+    __shared__ __align__(16) uint8_t smem[81920];
+    float* sG = reinterpret_cast<float*>(smem);               // [64][128] fp32
+    bf16* sQ = reinterpret_cast<bf16*>(smem + 32768);         // [64][128] bf16
+    bf16* sK = reinterpret_cast<bf16*>(smem + 49152);
+    bf16* sV = reinterpret_cast<bf16*>(smem + 65536);
+
+    const size_t tstride = (size_t)H * 128;   // elements between consecutive tokens
+    const size_t hoff = (size_t)h * 128;
+
+    // ---- 1. q, k, v tiles to LDS (rows past the sequence end are zero) ----
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int row = p * 16 + (tid >> 4), c8 = (tid & 15) * 8;
+        uint4 qq = make_uint4(0, 0, 0, 0), kk = qq, vv = qq;
+        if (row < len) {
+            const size_t off = (size_t)(tok0 + row) * tstride + hoff + c8;
+            qq = *reinterpret_cast<const uint4*>(q + off);
+            kk = *reinterpret_cast<const uint4*>(k + off);
+            vv = *reinterpret_cast<const uint4*>(v + off);
+        }
+        *reinterpret_cast<uint4*>(sQ + row * 128 + c8) = qq;
+        *reinterpret_cast<uint4*>(sK + row * 128 + c8) = kk;
+        *reinterpret_cast<uint4*>(sV + row * 128 + c8) = vv;
+    }
+    // ---- gate [LA-KDA §5.4] and in-chunk cumulative sum; padding rows: g = 0
+    {
+        const float ea = expf(A[h]);
+        const int c = tid & 127, half = tid >> 7;
+        float zr[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const int row = half * 32 + i;
+            zr[i] = row < len ? z[(size_t)(tok0 + row) * tstride + hoff + c] : 0.f;
+        }
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const int row = half * 32 + i;
+            run += row < len ? log_decay<false>(ea, zr[i]) : 0.f;
+            sG[row * 128 + c] = run;
+        }
+    }
+    __syncthreads();
+    if (tid >= 128) {
+        const int c = tid & 127;
+        const float base = sG[31 * 128 + c];
+#pragma unroll
+        for (int i = 32; i < 64; i++) sG[i * 128 + c] += base;
+    }
+    __syncthreads();
+    if (tid < 128) reinterpret_cast<float*>(rec + REC_G)[tid] = __expf(sG[63 * 128 + tid]);
+    if (DBG)
+        for (int idx = tid; idx < 8192; idx += 256) dbase[idx] = sG[idx];
+
+    // ---- 2a. A_kk and A_qk: wave w owns row block r = w, column blocks s <= r
+    f32x4 akk[4], aqk[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) { akk[s] = zero4(); aqk[s] = zero4(); }
+    {
+        const int r = w;
+        const int i = 16 * r + n16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            const int c0 = 32 * ks + 8 * g4;
+            float bref[8], gi[8];
+            if (r > 0) load8f(sG + (16 * r - 1) * 128 + c0, bref);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) bref[e] = 0.f;
+            }
+            load8f(sG + i * 128 + c0, gi);
+            const bf16x8 qi = *reinterpret_cast<const bf16x8*>(sQ + i * 128 + c0);
+            const bf16x8 ki = *reinterpret_cast<const bf16x8*>(sK + i * 128 + c0);
+            bf16x8 fq, fk;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float sc = __expf(gi[e] - bref[e]);
+                fq[e] = (bf16)((float)qi[e] * sc);
+                fk[e] = (bf16)((float)ki[e] * sc);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                if (s <= r) {
+                    const int j = 16 * s + n16;
+                    float gj[8];
+                    load8f(sG + j * 128 + c0, gj);
+                    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(sK + j * 128 + c0);
+                    bf16x8 fb;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) fb[e] = (bf16)((float)kj[e] * __expf(bref[e] - gj[e]));
+                    akk[s] = mfma_bf16(fk, fb, akk[s]);
+                    aqk[s] = mfma_bf16(fq, fb, aqk[s]);
+                }
+            }
+        }
+        // causal masks and the beta row scale of A_kk
+        float br[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 16 * r + 4 * g4 + e;
+            br[e] = row < len ? sigmoid_f<false>(bl[(size_t)(tok0 + row) * H + h]) : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            if (s <= r) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int ii = 4 * g4 + e;
+                    if (s == r) {
+                        if (n16 >= ii) akk[s][e] = 0.f;
+                        if (n16 > ii) aqk[s][e] = 0.f;
+                    }
+                    akk[s][e] *= br[e];
+                }
+            }
+        }
+    }
+
+    // ---- 2b. token-contiguous operands via an exact selection product ----
+    // MFMA(X rows as A operand, one-hot selector as B) returns X in the C
+    // layout: each lane then holds 4 consecutive tokens of one channel, which
+    // is the operand layout for products that contract over tokens.
+    bf16x8 sel[2];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        sel[0][e] = (bf16)((8 * g4 + e == n16) ? 1.f : 0.f);
+        sel[1][e] = (bf16)((8 * g4 + e == 16 + n16) ? 1.f : 0.f);
+    }
+    bf16x8 kgf[2][2], vf[2][2];     // [kstep][16-channel half] of this wave's 32 channels
+    f32x4 qinit[2][4];              // (Q . Gamma)^T tiles: [half][token block]
+    {
+        const int c0 = 32 * w + 8 * g4;
+        float gc[8];
+        load8f(sG + 63 * 128 + c0, gc);
+        f32x4 tkg[4][2], tv[4][2], tkb[4][2];
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            const int row = 16 * tt + n16;
+            float gr[8];
+            load8f(sG + row * 128 + c0, gr);
+            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(sK + row * 128 + c0);
+            const bf16x8 vv = *reinterpret_cast<const bf16x8*>(sV + row * 128 + c0);
+            bf16x8 akg, akb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float kf = (float)kk[e];
+                akg[e] = (bf16)(kf * __expf(gr[e]));
+                akb[e] = (bf16)(kf * __expf(gc[e] - gr[e]));
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                tkg[tt][cb] = mfma_bf16(akg, sel[cb], zero4());
+                tv[tt][cb] = mfma_bf16(vv, sel[cb], zero4());
+                tkb[tt][cb] = mfma_bf16(akb, sel[cb], zero4());
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                kgf[kb][cb] = pack_frag(tkg[2 * kb][cb], tkg[2 * kb + 1][cb]);
+                vf[kb][cb] = pack_frag(tv[2 * kb][cb], tv[2 * kb + 1][cb]);
+                *reinterpret_cast<bf16x8*>(rec + REC_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16) =
+                    pack_frag(tkb[2 * kb][cb], tkb[2 * kb + 1][cb]);
+            }
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                const int row = 16 * tb + n16, c = 32 * w + 16 * cb + 4 * g4;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    qinit[cb][tb][e] = (float)sQ[row * 128 + c + e] * __expf(sG[row * 128 + c + e]);
+            }
+    }
+    __syncthreads();   // q, k, v and G tiles are dead from here
+
+    // ---- 2c. A_kk, A_qk, beta to LDS ----
+    float* sAkk = reinterpret_cast<float*>(smem);             // [64][64]
+    float* sAqk = reinterpret_cast<float*>(smem + 16384);     // [64][64]
+    float* sN = reinterpret_cast<float*>(smem + 32768);       // [64][64]
+    float* sBeta = reinterpret_cast<float*>(smem + 49152);    // [64]
+    float* sP = reinterpret_cast<float*>(smem + 49408);       // [4][16][16]
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 16 * w + 4 * g4 + e, col = 16 * s + n16;
+            sAkk[row * 64 + col] = akk[s][e];
+            sAqk[row * 64 + col] = aqk[s][e];
+        }
+    for (int idx = tid; idx < 4096; idx += 256) sN[idx] = 0.f;
+    if (tid < 64) sBeta[tid] = tid < len ? sigmoid_f<false>(bl[(size_t)(tok0 + tid) * H + h]) : 0.f;
+    __syncthreads();
+    if (DBG)
+        for (int idx = tid; idx < 4096; idx += 256) {
+            dbase[8192 + idx] = sAkk[idx];
+            dbase[8192 + 4096 + idx] = sAqk[idx];
+        }
+
+    // ---- 3. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
+    // diagonal blocks: forward substitution, lane = (block, column)
+    if (w == 0) {
+        const int rb = g4, cc = n16;
+        const float* Ab = sAkk + (16 * rb) * 64 + 16 * rb;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float acc = (i == cc) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; m++) acc -= Ab[i * 64 + m] * x[m];
+            x[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) sN[(16 * rb + i) * 64 + 16 * rb + cc] = x[i];
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance d: N_rs = -N_rr sum_{m=s}^{r-1} A_rm N_ms
+    for (int d = 1; d < 4; d++) {
+        const bool act = w < 4 - d;
+        const int r = w + d, s = w;
+        if (act) {
+            f32x4 P = zero4();
+            for (int m = s; m < r; m++)
+                P = mm16_f32(P, sAkk + 16 * r * 64 + 16 * m, 64, sN + 16 * m * 64 + 16 * s, 64, n16, g4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sP[w * 256 + (4 * g4 + e) * 16 + n16] = P[e];
+        }
+        __syncthreads();
+        if (act) {
+            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * 64 + 16 * r, 64, sP + w * 256, 16, n16, g4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sN[(16 * r + 4 * g4 + e) * 64 + 16 * s + n16] = -R[e];
+        }
+        __syncthreads();
+    }
+    if (DBG)
+        for (int idx = tid; idx < 4096; idx += 256)
+            dbase[8192 + 8192 + idx] = sN[idx] * sBeta[idx & 63];
+
+    // ---- 4. products over tokens (wave w: channels [32w, 32w + 32)) ----
+    // k-slot order of every token-contracting fragment: lane group g, slot e
+    // holds token 32*kb + 4g + e (e < 4) or 32*kb + 16 + 4g + (e - 4) (e >= 4),
+    // matching two stacked C tiles.
+    bf16x8 tf[4][2], af[4][2];      // T and A_qk row fragments [row block][kstep]
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const int row = 16 * tb + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
+            const float4 n0 = *reinterpret_cast<const float4*>(sN + row * 64 + j0);
+            const float4 n1 = *reinterpret_cast<const float4*>(sN + row * 64 + j1);
+            const float4 b0 = *reinterpret_cast<const float4*>(sBeta + j0);
+            const float4 b1 = *reinterpret_cast<const float4*>(sBeta + j1);
+            const f32x4 t0 = {n0.x * b0.x, n0.y * b0.y, n0.z * b0.z, n0.w * b0.w};
+            const f32x4 t1 = {n1.x * b1.x, n1.y * b1.y, n1.z * b1.z, n1.w * b1.w};
+            tf[tb][kb] = pack_frag(t0, t1);
+            const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * 64 + j0);
+            const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * 64 + j1);
+            const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
+            af[tb][kb] = pack_frag(x0, x1);
+        }
+
+    // W^T = (K . Gamma)^T T^T: tiles [channel][token], stored negated as the
+    // chain's A operand (wave tb of the chain, k-step w)
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++) {
+        f32x4 wt0 = zero4(), wt1 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            wt0 = mfma_bf16(kgf[kb][0], tf[tb][kb], wt0);
+            wt1 = mfma_bf16(kgf[kb][1], tf[tb][kb], wt1);
+        }
+        *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
+    }
+    // W = T (K . Gamma) in the C layout, kept as negated token-slot fragments
+    bf16x8 wcf[2][2];
+    {
+        f32x4 wc[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                wc[tb][cb] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) wc[tb][cb] = mfma_bf16(tf[tb][kb], kgf[kb][cb], wc[tb][cb]);
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) wcf[kb][cb] = pack_frag_neg(wc[2 * kb][cb], wc[2 * kb + 1][cb]);
+    }
+    // U = T V: chain tiles (slice 2w + cb, wave tb) and token-slot fragments
+    bf16x8 uf[2][2];
+    {
+        f32x4 u[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                u[tb][cb] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) u[tb][cb] = mfma_bf16(tf[tb][kb], vf[kb][cb], u[tb][cb]);
+                *reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(u[tb][cb]);
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) uf[kb][cb] = pack_frag(u[2 * kb][cb], u[2 * kb + 1][cb]);
+    }
+    // Y = A_qk U
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+            f32x4 y = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) y = mfma_bf16(af[tb][kb], uf[kb][cb], y);
+            *reinterpret_cast<bf16x4*>(rec + REC_Y + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(y);
+        }
+    // Q'^T = (Q . Gamma)^T - W^T A_qk^T
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++) {
+        f32x4 q0 = qinit[0][tb], q1 = qinit[1][tb];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            q0 = mfma_bf16(wcf[kb][0], af[tb][kb], q0);
+            q1 = mfma_bf16(wcf[kb][1], af[tb][kb], q1);
+        }
+        *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag(q0, q1);
+    }
+}
+
+// Workgroup = (sequence, head, slice of 16 state columns); 4 waves.
+// Wave w computes V~ and O rows [16w, 16w + 16) of every chunk and owns
+// state rows [32w, 32w + 32) of the slice as two fp32 C tiles.  Each chunk:
+//   V~ = U - W S,  O = Y + Q' S      (B operand: the bf16 copy of S in LDS)
+//   S <- Diag(gamma_C) S + Kbar^T V~ (B operand: V~ gathered through LDS)
+// The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
+__global__ __launch_bounds__(256, 1)
+void fast_chain_kernel(const uint8_t* __restrict__ recs, const int2* __restrict__ seqs,
+                       const int4* __restrict__ chunks, const float* __restrict__ h0,
+                       int N, int H, bf16* __restrict__ o, float* __restrict__ hT,
+                       float* __restrict__ dbgS)
+{
+    // blocks 8 apart land on the same XCD: the 8 slices of one (sequence,
+    // head) share the chunk records through that XCD's L2
+    const int id = blockIdx.x;
+    const int p = (id >> 6) * 8 + (id & 7);
+    const int sg = (id >> 3) & 7;
+    if (p >= N * H) return;
+    const int n = p / H, h = p % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int col = 16 * sg + n16;
+
+    __shared__ __align__(16) bf16 sS[4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[4 * 64 * 4];
+
+    f32x4 accS[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 32 * w + 16 * b + 4 * g4 + e;
+            accS[b][e] = h0 ? h0[((size_t)p * 128 + row) * 128 + col] : 0.f;
+        }
+    *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
+    __syncthreads();
+
+    const int2 sd = seqs[n];
+    for (int ci = 0; ci < sd.y; ci++) {
+        const int cid = sd.x + ci;
+        const int4 cd = chunks[cid];
+        const int tok0 = cd.y, len = cd.z;
+        const uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
+        bf16x8 wf[4], qf[4], kf[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            wf[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
+            qf[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+                kf[b][kb] = *reinterpret_cast<const bf16x8*>(rec + REC_K + (((w * 2 + b) * 2 + kb) * 64 + lane) * 16);
+        const bf16x4 ut = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sg * 4 + w) * 64 + lane) * 8);
+        const bf16x4 yt = *reinterpret_cast<const bf16x4*>(rec + REC_Y + ((sg * 4 + w) * 64 + lane) * 8);
+        const float* gC = reinterpret_cast<const float*>(rec + REC_G);
+        const float4 gc0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
+        const float4 gc1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
+
+        if (dbgS) {
+#pragma unroll
+            for (int b = 0; b < 2; b++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = 32 * w + 16 * b + 4 * g4 + e;
+                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col] = accS[b][e];
+                }
+        }
+        bf16x8 sf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) sf[ks] = *reinterpret_cast<const bf16x8*>(sS + (ks * 64 + lane) * 8);
+        f32x4 accV = unpack4(ut), accO = unpack4(yt);
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            accV = mfma_bf16(wf[ks], sf[ks], accV);
+            accO = mfma_bf16(qf[ks], sf[ks], accO);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 16 * w + 4 * g4 + e;
+            if (row < len) o[((size_t)(tok0 + row) * H + h) * 128 + col] = (bf16)accO[e];
+        }
+        *reinterpret_cast<bf16x4*>(sVt + (w * 64 + lane) * 4) = pack4(accV);
+        __syncthreads();
+        bf16x8 vfr[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+            vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((2 * kb) * 64 + lane) * 4),
+                               *reinterpret_cast<const bf16x4*>(sVt + ((2 * kb + 1) * 64 + lane) * 4));
+        accS[0][0] *= gc0.x; accS[0][1] *= gc0.y; accS[0][2] *= gc0.z; accS[0][3] *= gc0.w;
+        accS[1][0] *= gc1.x; accS[1][1] *= gc1.y; accS[1][2] *= gc1.z; accS[1][3] *= gc1.w;
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) accS[b] = mfma_bf16(kf[b][kb], vfr[kb], accS[b]);
+        *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
+        __syncthreads();
+    }
+    if (hT) {
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 32 * w + 16 * b + 4 * g4 + e;
+                hT[((size_t)p * 128 + row) * 128 + col] = accS[b][e];
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fast(const ChunkArgs& a) {
+    const int* hdr = reinterpret_cast<const int*>(a.ws);
+    const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
+    const int2* seqs = reinterpret_cast<const int2*>(a.ws + a.L.off_seqs);
+    uint8_t* recs = a.ws + a.L.off_recs;
+    const dim3 gi((unsigned)a.L.cap, (unsigned)a.H);
+    if (a.dbg_intra)
+        hipLaunchKernelGGL(fast_intra_kernel<true>, gi, dim3(256), 0, a.stream,
+                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
+                           hdr, chunks, a.H, recs, a.dbg_intra);
+    else
+        hipLaunchKernelGGL(fast_intra_kernel<false>, gi, dim3(256), 0, a.stream,
+                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
+                           hdr, chunks, a.H, recs, (float*)nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
+    const int P = a.N * a.H;
+    const unsigned nblk = (unsigned)(((P + 7) / 8) * 64);
+    hipLaunchKernelGGL(fast_chain_kernel, dim3(nblk), dim3(256), 0, a.stream,
+                       (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
+                       a.dbg_state);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,89 @@
+// Host-side declarations shared by the libkda translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// ---------------------------------------------------------------- workspace
+//
+// [0, 256)                 header: int32 total number of chunks
+// chunk table              cap x int4 (sequence, first token, length, 0)
+// sequence table           N x int2  (first chunk id, number of chunks)
+// chunk records            cap x H records of rec_bytes each
+//
+// Chunks are numbered sequence by sequence in token order; `cap` bounds their
+// number for both layouts: B*ceil(T/C) + N.
+struct WsLayout {
+    int cap;
+    size_t off_chunks, off_seqs, off_recs, rec_bytes, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int chunk_capacity(int B, int T, int N, int C) {
+    long long per = (T + (long long)C - 1) / C;
+    long long cap = (long long)B * per + N;
+    return cap > 0x7fffffffLL ? -1 : (int)cap;
+}
+
+// fp32 record of the generic path: W [C][DK], U [C][DV], Qg [C][DK],
+// Kb [C][DK], Aqk [C][C], gamma_C [DK]
+inline size_t generic_rec_floats(int dk, int dv, int C) {
+    return (size_t)C * dk * 3 + (size_t)C * dv + (size_t)C * C + dk;
+}
+
+// record of the MFMA path (bf16 operand fragments + fp32 gamma_C); offsets in
+// bytes, see kda_chunk_fast.hip for the fragment orders
+namespace fast {
+constexpr int C = 64, DK = 128, DV = 128;
+constexpr int REC_W = 0;        // -W^T  fragments [4 wave][4 kstep][64 lane][8] bf16
+constexpr int REC_Q = 16384;    // Q'^T  fragments [4 wave][4 kstep][64 lane][8] bf16
+constexpr int REC_K = 32768;    // Kbar^T fragments [4 wave][2 half][2 kstep][64 lane][8] bf16
+constexpr int REC_U = 49152;    // U tiles  [8 slice][4 wave][64 lane][4] bf16
+constexpr int REC_Y = 65536;    // Y tiles  [8 slice][4 wave][64 lane][4] bf16
+constexpr int REC_G = 81920;    // gamma_C [128] fp32
+constexpr int REC_BYTES = 82432;
+}  // namespace fast
+
+inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
+    return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
+}
+
+inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, bool fast) {
+    WsLayout L{};
+    L.cap = chunk_capacity(B, T, N, C);
+    if (L.cap < 0) { L.total = 0; return L; }
+    L.off_chunks = 256;
+    L.off_seqs = align_up(L.off_chunks + (size_t)L.cap * 16, 256);
+    L.off_recs = align_up(L.off_seqs + (size_t)(N > 0 ? N : 1) * 8, 256);
+    L.rec_bytes = fast ? (size_t)fast::REC_BYTES : generic_rec_floats(dk, dv, C) * 4;
+    L.total = L.off_recs + (size_t)L.cap * H * L.rec_bytes;
+    return L;
+}
+
+struct ChunkArgs {
+    const void* q; const void* k; const void* v;
+    const float* z; const float* b; const float* A;
+    const float* h0; const int* cu;
+    int B, T, H, dk, dv, N, C;
+    void* o; float* hT;
+    uint8_t* ws; WsLayout L;
+    float* dbg_intra; float* dbg_state;
+    hipEvent_t* ev;            // 4 events recorded around the kernels, or null
+    hipStream_t stream;
+};
+
+// launchers (return hipError_t of the launches)
+hipError_t launch_prep(const ChunkArgs& a);
+hipError_t launch_fast(const ChunkArgs& a);
+hipError_t launch_generic(const ChunkArgs& a, int dtype_bf16);
+bool generic_supported(int dk, int dv, int C);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* z,
+                         const float* b, const float* A, float* state, void* o,
+                         int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s);
+bool decode_supported(int dk, int dv);
+
+}  // namespace kda

@@ -1,0 +1,97 @@
+// Chunk bookkeeping for kda_chunk_fwd, done on the device so the host never
+// reads cu_seqlens.  Chunks restart at every sequence start and are numbered
+// sequence by sequence in token order; a sequence shorter than a multiple of
+// the chunk size ends in a short chunk.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+__device__ __forceinline__ void seq_extent(const int* cu, int s, int Tfix, int Ttot,
+                                           int& start, int& len) {
+    if (cu) {
+        int a = cu[s], e = cu[s + 1];
+        a = min(max(a, 0), Ttot);
+        e = min(max(e, a), Ttot);
+        start = a;
+        len = e - a;
+    } else {
+        start = s * Tfix;
+        len = Tfix;
+    }
+}
+
+// One workgroup: per-sequence chunk counts, their exclusive prefix sum
+// (clamped to the capacity) and the total.
+__global__ __launch_bounds__(1024)
+void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
+                     int* __restrict__ hdr, int2* __restrict__ seqs)
+{
+    __shared__ int s_scan[1024];
+    const int t = threadIdx.x;
+    long long carry = 0;
+    for (int base = 0; base < N; base += 1024) {
+        const int s = base + t;
+        int start = 0, len = 0;
+        if (s < N) seq_extent(cu, s, Tfix, Ttot, start, len);
+        const int nch = (len + C - 1) / C;
+        s_scan[t] = nch;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int x = t >= off ? s_scan[t - off] : 0;
+            __syncthreads();
+            s_scan[t] += x;
+            __syncthreads();
+        }
+        if (s < N) {
+            const long long first = carry + s_scan[t] - nch;
+            const int f = (int)min(first, (long long)cap);
+            const int nc = (int)max(0LL, min((long long)nch, (long long)cap - f));
+            seqs[s] = make_int2(f, nc);
+        }
+        carry += s_scan[1023];
+        __syncthreads();
+    }
+    if (t == 0) hdr[0] = (int)min(carry, (long long)cap);
+}
+
+// One thread per chunk slot: locate the owning sequence by binary search
+// over the first-chunk ids and record (sequence, first token, length).
+__global__ __launch_bounds__(256)
+void prep_chunk_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
+                       const int* __restrict__ hdr, const int2* __restrict__ seqs,
+                       int4* __restrict__ chunks)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= cap) return;
+    const int total = hdr[0];
+    if (c >= total) { chunks[c] = make_int4(-1, 0, 0, 0); return; }
+    // largest s with seqs[s].x <= c; empty sequences share the next one's id,
+    // so the largest such s is the non-empty owner
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seqs[mid].x <= c) lo = mid; else hi = mid - 1;
+    }
+    int start, len;
+    seq_extent(cu, lo, Tfix, Ttot, start, len);
+    const int j = c - seqs[lo].x;
+    chunks[c] = make_int4(lo, start + j * C, min(C, len - j * C), 0);
+}
+
+hipError_t launch_prep(const ChunkArgs& a) {
+    int* hdr = reinterpret_cast<int*>(a.ws);
+    int4* chunks = reinterpret_cast<int4*>(a.ws + a.L.off_chunks);
+    int2* seqs = reinterpret_cast<int2*>(a.ws + a.L.off_seqs);
+    const int Ttot = a.cu ? a.T : a.B * a.T;
+    hipLaunchKernelGGL(prep_seq_kernel, dim3(1), dim3(1024), 0, a.stream,
+                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, hdr, seqs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned nb = (unsigned)((a.L.cap + 255) / 256);
+    hipLaunchKernelGGL(prep_chunk_kernel, dim3(nb), dim3(256), 0, a.stream,
+                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, (const int*)hdr, (const int2*)seqs, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace kda

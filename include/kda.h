@@ -1,0 +1,201 @@
+/*
+ * kda.h -- C ABI of libkda, the Kimi Delta Attention (KDA) core for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes (per sequence and head, S in R^{d_k x d_v}, fp32):
+ *
+ *   alpha_t = exp(-5 * sigmoid(exp(A_h) * z_t))   per channel     (1)
+ *   beta_t  = sigmoid(b_t)                                           (2)
+ *   S_t     = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+ *             + beta_t k_t v_t^T                                     (3)
+ *   o_t     = S_t^T q_t                                              (4)
+ *
+ * Sources (web pages):
+ *   [LA-KDA]   "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制",
+ *              blog-3d3.pages.dev/posts/150
+ *   [K3-ATTN]  "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构",
+ *              forceinjection.github.io/09_inference_system/vllm/module_analysis/kimi_k3_attention.html
+ *   [K3-NOTES] "Kimi K3", llm.rainlin.net/llm-inference/kimi-k3
+ * (1) is the lower-bounded sigmoid decay of [LA-KDA §5.4]; (2) the write
+ * strength of [LA-KDA §5.3]; (3) the recurrence of [LA-KDA §5.2] and
+ * [K3-ATTN §2.1]; (4) the read-out of [LA-KDA §5.5].  The prefill entry point
+ * uses the chunked form of [LA-KDA §7] with 16-token sub-tiles ([LA-KDA §8]);
+ * the decode entry point uses the three-step DPLR update of [K3-ATTN §2.2].
+ * Both take the same raw logits and produce the same state semantics, as the
+ * chunked and recurrent call sites on [K3-NOTES] ("KDA Prefill 与 Decode
+ * Kernel") require.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
+ *     the stated row-major layout and 16-byte aligned.  The library never
+ *     allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; nothing synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-OK status means nothing was enqueued, except KDA_ERR_HIP, which
+ *     reports a failed launch.  No exception crosses the ABI.
+ *   - The library holds no mutable global state: calls on different streams
+ *     may run concurrently if their buffers do not overlap.
+ *   - No query scale is applied: o = S^T q exactly (no formula on the pages
+ *     carries one); a caller wanting 1/sqrt(d_k) scales q first.  q and k are
+ *     used as given (the pages normalise them upstream, [LA-KDA §5.3]).
+ *   - NaN or Inf inputs propagate; they are not detected.
+ */
+#ifndef LIBKDA_KDA_H
+#define LIBKDA_KDA_H
+
+#include <stddef.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative or inconsistent size   */
+    KDA_ERR_UNSUPPORTED = 2,   /* (d_k, d_v, chunk, dtype) not compiled in      */
+    KDA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required     */
+    KDA_ERR_HIP = 4            /* a kernel launch failed                         */
+} kda_status_t;
+
+/* Element type of q, k, v and o.  Gate logits, beta logits, A and states are
+ * always fp32. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+KDA_API const char* kda_status_string(kda_status_t s);
+
+/*
+ * Supported shapes.
+ *   kda_chunk_fwd:      d_k == d_v in {16, 32, 64, 128}, chunk in {16, 64},
+ *                       dtype fp32 or bf16.  bf16 with d_k = d_v = 128 and
+ *                       chunk = 64 runs the MFMA path; every other supported
+ *                       combination runs an fp32-arithmetic path.
+ *   kda_recurrent_step: d_k == d_v in {16, 32, 64, 128}, fp32 or bf16.
+ * Returns 1 when the combination is compiled in, 0 otherwise.
+ */
+KDA_API int kda_chunk_fwd_supported(int dk, int dv, int chunk, kda_dtype_t dtype);
+KDA_API int kda_recurrent_step_supported(int dk, int dv, kda_dtype_t dtype);
+
+/*
+ * Workspace size in bytes for kda_chunk_fwd with these sizes (N = number of
+ * sequences: N == B without cu_seqlens, the length of cu_seqlens minus one
+ * with it).  The bound covers both layouts.  Returns 0 for unsupported or
+ * invalid sizes.  The workspace is scratch device memory owned by the caller;
+ * its contents need no initialisation and are meaningless afterwards, except
+ * through kda_chunk_fwd_debug.
+ */
+KDA_API size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                     int chunk, kda_dtype_t dtype);
+
+/*
+ * Prefill: run the recurrence (1)-(4) over whole sequences, chunk by chunk.
+ *
+ *   q, k         [B, T, H, dk]  dtype
+ *   v            [B, T, H, dv]  dtype
+ *   g_logits     [B, T, H, dk]  fp32  raw per-channel gate logits z
+ *   beta_logits  [B, T, H]      fp32  raw write-strength logits b
+ *   A            [H]            fp32  per-head A_h of (1)
+ *   h0           [N, H, dk, dv] fp32  initial states, or NULL for zeros
+ *   cu_seqlens   [N+1]          int32 device offsets, or NULL
+ *   o            [B, T, H, dv]  dtype output
+ *   hT           [N, H, dk, dv] fp32  final states, or NULL to skip; may be
+ *                                     the same pointer as h0 (in place)
+ *
+ * Without cu_seqlens the batch holds N = B sequences of T tokens each.  With
+ * cu_seqlens, B must be 1, the T tokens are N packed sequences and sequence s
+ * is tokens [cu_seqlens[s], cu_seqlens[s+1]).  The offsets stay on the device
+ * (the host never reads them); they must satisfy 0 = cu[0] <= cu[1] <= ... <=
+ * cu[N] = T.  Offsets that break this are clamped into [0, T] so that no
+ * access leaves the buffers, and the results are then unspecified.
+ * The state restarts at every sequence from that sequence's h0.  An empty
+ * sequence (or T = 0) yields hT = h0 (zeros without h0).  Chunks restart at
+ * every sequence start; a sequence whose length is not a multiple of `chunk`
+ * ends in a shorter chunk.
+ *
+ * Workspace: at least kda_chunk_fwd_workspace_bytes(...) bytes, 256-byte
+ * aligned.
+ */
+KDA_API kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* g_logits, const float* beta_logits,
+                           const float* A, const float* h0, const int* cu_seqlens,
+                           int B, int T, int H, int dk, int dv, int N, int chunk,
+                           kda_dtype_t dtype, void* o, float* hT,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic variant of kda_chunk_fwd: identical results, plus per-chunk
+ * intermediates of the chunked form ([LA-KDA §7]) for stage-level checks.
+ * With Cn = the workspace's chunk capacity (returned through *chunk_capacity
+ * by kda_chunk_fwd_debug_floats) and c the chunk length:
+ *   dbg_intra  [Cn, H, c*dk + 3*c*c] fp32, per chunk and head in this order:
+ *              G [c, dk] (in-chunk cumulative log-decay, inclusive),
+ *              A_kk [c, c] (beta-scaled, strictly lower), A_qk [c, c] (lower),
+ *              T [c, c] = (I + A_kk)^{-1} Diag(beta);  may be NULL
+ *   dbg_state  [Cn, H, dk, dv] fp32, the state entering each chunk; may be NULL
+ * Chunks are numbered sequence by sequence in token order.
+ */
+KDA_API size_t kda_chunk_fwd_debug_floats(int B, int T, int H, int dk, int dv, int N,
+                                  int chunk, size_t* dbg_state_floats,
+                                  int* chunk_capacity);
+KDA_API kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const void* v,
+                                 const float* g_logits, const float* beta_logits,
+                                 const float* A, const float* h0,
+                                 const int* cu_seqlens, int B, int T, int H,
+                                 int dk, int dv, int N, int chunk,
+                                 kda_dtype_t dtype, void* o, float* hT,
+                                 void* workspace, size_t workspace_bytes,
+                                 float* dbg_intra, float* dbg_state, void* stream);
+
+/*
+ * Diagnostic variant of kda_chunk_fwd that also records caller-created HIP
+ * events on `stream` around its kernels, so a caller can time each stage on
+ * the stream the kernels run on: events[0] before the chunk bookkeeping,
+ * events[1] after it, events[2] after the intra-chunk kernel (gate, A_kk,
+ * A_qk, triangular inverse, W, U), events[3] after the state-chain kernel
+ * (inter-chunk state and outputs).  `events` points to n_events >= 4
+ * hipEvent_t handles (as void*).  Results are identical to kda_chunk_fwd.
+ */
+KDA_API kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
+                                         const float* g_logits, const float* beta_logits,
+                                         const float* A, const float* h0,
+                                         const int* cu_seqlens, int B, int T, int H,
+                                         int dk, int dv, int N, int chunk,
+                                         kda_dtype_t dtype, void* o, float* hT,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* const* events, int n_events, void* stream);
+
+/*
+ * Decode: one token per sequence, state updated in place.
+ *
+ *   q, k         [N, H, dk]       dtype
+ *   v            [N, H, dv]       dtype
+ *   g_logits     [N, H, dk]       fp32
+ *   beta_logits  [N, H]           fp32
+ *   A            [H]              fp32
+ *   state        [N, H, dk, dv]   fp32, read and overwritten
+ *   o            [N, H, dv]       dtype
+ *
+ * Each (sequence, head) state is read once and written once: with
+ * S' = Diag(alpha) S, the step forms p = S'^T k and r = S'^T q in one pass,
+ * then u = beta (v - p), S = S' + k u^T and o = r + (q . k) u, which equals
+ * S^T q after the update ([K3-ATTN §2.2], three steps with no d_k x d_k matrix).
+ * N = 0 is a no-op.  No workspace.
+ */
+KDA_API kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v,
+                                const float* g_logits, const float* beta_logits,
+                                const float* A, float* state, void* o,
+                                int N, int H, int dk, int dv, kda_dtype_t dtype,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_KDA_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/kda.h declares, and rejects bad arguments before
+anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import gated_delta_rule_77_amd as kda
+    if not os.path.exists(kda.lib_path):
+        from gated_delta_rule_77_amd import build
+        build.build()
+    return kda.lib()
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_symbols():
+    import gated_delta_rule_77_amd as kda
+    assert _declared_symbols() == sorted(kda.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, word in [(0, "KDA_OK"), (1, "INVALID"), (2, "UNSUPPORTED"), (3, "WORKSPACE"), (4, "HIP")]:
+        assert word in L.kda_status_string(code).decode()
+    assert L.kda_status_string(99)
+
+
+def test_supported_sets(L):
+    assert L.kda_chunk_fwd_supported(128, 128, 64, 1) == 1
+    assert L.kda_chunk_fwd_supported(16, 16, 16, 0) == 1
+    assert L.kda_chunk_fwd_supported(128, 64, 64, 1) == 0
+    assert L.kda_chunk_fwd_supported(96, 96, 64, 1) == 0
+    assert L.kda_chunk_fwd_supported(128, 128, 32, 1) == 0
+    assert L.kda_chunk_fwd_supported(128, 128, 64, 7) == 0
+    assert L.kda_recurrent_step_supported(128, 128, 1) == 1
+    assert L.kda_recurrent_step_supported(128, 128, 0) == 1
+    assert L.kda_recurrent_step_supported(256, 256, 1) == 0
+
+
+def test_workspace_bytes(L):
+    # capacity = B * ceil(T / C) + N chunk records of 82432 bytes per head on the MFMA path
+    n = L.kda_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 1, 64, 1)
+    assert n >= (64 + 1) * 16 * 82432
+    assert n < (64 + 1) * 16 * 82432 + 8192
+    assert L.kda_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 64, 1, 64, 1) == 0
+    assert L.kda_chunk_fwd_workspace_bytes(-1, 4096, 16, 128, 128, 1, 64, 1) == 0
+    assert L.kda_chunk_fwd_workspace_bytes(1, 64, 2, 16, 16, 1, 16, 0) > 0
+
+
+def _chunk(L, **kw):
+    a = dict(q=None, k=None, v=None, z=None, b=None, A=None, h0=None, cu=None, B=1, T=64, H=2,
+             dk=16, dv=16, N=1, chunk=16, dtype=0, o=None, hT=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    fn = L.kda_chunk_fwd
+    fn.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    i = ctypes.c_int
+    fn.argtypes = [vp] * 8 + [i] * 8 + [vp, vp, vp, ctypes.c_size_t, vp]
+    return fn(a["q"], a["k"], a["v"], a["z"], a["b"], a["A"], a["h0"], a["cu"], a["B"], a["T"],
+              a["H"], a["dk"], a["dv"], a["N"], a["chunk"], a["dtype"], a["o"], a["hT"], a["ws"],
+              a["wsb"], a["stream"])
+
+
+FAKE = 1 << 20   # never dereferenced: validation fails before any launch
+
+
+def test_chunk_fwd_rejects_bad_arguments(L):
+    full = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, b=FAKE, A=FAKE, o=FAKE)
+    assert _chunk(L, **full, T=-1) == 1
+    assert _chunk(L, **full, H=0) == 1
+    assert _chunk(L, **full, dtype=5) == 1
+    assert _chunk(L, **full, N=2) == 1                 # N must equal B without cu_seqlens
+    assert _chunk(L, **full, cu=FAKE, B=2, N=2) == 1   # cu_seqlens needs B == 1
+    assert _chunk(L, **full, dk=96, dv=96) == 2
+    assert _chunk(L, **full, chunk=32) == 2
+    assert _chunk(L, **dict(full, q=None)) == 1
+    assert _chunk(L, **dict(full, A=None)) == 1
+    assert _chunk(L, **full, ws=None) == 3
+    assert _chunk(L, **full, ws=FAKE, wsb=16) == 3
+    assert _chunk(L, **full, ws=FAKE + 8, wsb=1 << 40) == 3    # misaligned workspace
+    assert _chunk(L, N=0, B=0) == 1                    # B must be >= 1
+    assert _chunk(L, B=1, N=1, T=8, q=None, k=None, v=None, z=None, b=None, o=None,
+                  A=None) == 1
+
+
+def test_recurrent_step_rejects_bad_arguments(L):
+    fn = L.kda_recurrent_step
+    fn.restype = ctypes.c_int
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn.argtypes = [vp] * 8 + [i] * 5 + [vp]
+    ok = [FAKE] * 8
+    assert fn(*ok, 4, 2, 96, 96, 1, None) == 2
+    assert fn(*ok, 4, 2, 128, 64, 1, None) == 2
+    assert fn(*ok, -1, 2, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, 0, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, 2, 128, 128, 3, None) == 1
+    assert fn(*([None] + ok[1:]), 4, 2, 128, 128, 1, None) == 1
+    assert fn(*([None] * 8), 0, 2, 128, 128, 1, None) == 0   # N = 0 is a no-op
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import gated_delta_rule_77_amd as kda
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1), torch.zeros(1))
+    with pytest.raises(ValueError):
+        kda.kda_recurrent_step(x[0], x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(1),
+                               torch.zeros(4, 1, 16, 16))
