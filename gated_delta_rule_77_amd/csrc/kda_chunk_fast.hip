@@ -60,6 +60,14 @@ __device__ __forceinline__ void load8f(const float* p, float* out) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// LDS row strides (elements), padded so that 16-byte fragment reads whose
+// rows vary across lanes fall on distinct banks: 272-byte bf16 rows, 528-byte
+// fp32 rows of G, 272-byte rows of the 64x64 fp32 matrices.
+constexpr int kLdK = 136;   // bf16 k tile [64][kLdK]
+constexpr int kLdG = 132;   // fp32 G tile [64][kLdG]
+constexpr int kLdA = 68;    // fp32 64x64 matrices [64][kLdA]
+constexpr int kSmemIntra = 56576;
+
 template <bool DBG>
 __global__ __launch_bounds__(256, 2)
 void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -78,29 +86,40 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
     float* dbase = DBG ? dbg + ((size_t)cid * H + h) * (64 * 128 + 3 * 64 * 64) : nullptr;
 
-    __shared__ __align__(16) uint8_t smem[81920];
-    float* sG = reinterpret_cast<float*>(smem);               // [64][128] fp32
-    bf16* sQ = reinterpret_cast<bf16*>(smem + 32768);         // [64][128] bf16
-    bf16* sK = reinterpret_cast<bf16*>(smem + 49152);
-    bf16* sV = reinterpret_cast<bf16*>(smem + 65536);
+    __shared__ __align__(16) uint8_t smem[kSmemIntra];
+    float* sG = reinterpret_cast<float*>(smem);                       // [64][kLdG]
+    bf16* sK = reinterpret_cast<bf16*>(smem + 64 * kLdG * 4);         // [64][kLdK]
 
     const size_t tstride = (size_t)H * 128;   // elements between consecutive tokens
     const size_t hoff = (size_t)h * 128;
+    auto tok = [&](int row) { return (size_t)(tok0 + row) * tstride + hoff; };
+    const uint4 zero16 = make_uint4(0, 0, 0, 0);
 
-    // ---- 1. q, k, v tiles to LDS (rows past the sequence end are zero) ----
+    // ---- 1. loads: k tile to LDS; q and v fragments straight to registers
+    //      (every q/v element is used by exactly one lane); rows past the end
+    //      of the sequence read as zero
 #pragma unroll
     for (int p = 0; p < 4; p++) {
         const int row = p * 16 + (tid >> 4), c8 = (tid & 15) * 8;
-        uint4 qq = make_uint4(0, 0, 0, 0), kk = qq, vv = qq;
-        if (row < len) {
-            const size_t off = (size_t)(tok0 + row) * tstride + hoff + c8;
-            qq = *reinterpret_cast<const uint4*>(q + off);
-            kk = *reinterpret_cast<const uint4*>(k + off);
-            vv = *reinterpret_cast<const uint4*>(v + off);
+        const uint4 kk = row < len ? *reinterpret_cast<const uint4*>(k + tok(row) + c8) : zero16;
+        *reinterpret_cast<uint4*>(sK + row * kLdK + c8) = kk;
+    }
+    uint4 qa_raw[4], v_raw[4];       // q rows 16w + n (A operand), v rows 16tt + n (channels 32w + 8g)
+    uint2 qt_raw[2][4];              // q rows 16tb + n, channels 32w + 16cb + 4g (transposed tiles)
+    {
+        const int rq = 16 * w + n16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            qa_raw[ks] = rq < len ? *reinterpret_cast<const uint4*>(q + tok(rq) + 32 * ks + 8 * g4) : zero16;
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            const int r = 16 * tt + n16;
+            v_raw[tt] = r < len ? *reinterpret_cast<const uint4*>(v + tok(r) + 32 * w + 8 * g4) : zero16;
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++)
+                qt_raw[cb][tt] = r < len ? *reinterpret_cast<const uint2*>(q + tok(r) + 32 * w + 16 * cb + 4 * g4)
+                                         : make_uint2(0, 0);
         }
-        *reinterpret_cast<uint4*>(sQ + row * 128 + c8) = qq;
-        *reinterpret_cast<uint4*>(sK + row * 128 + c8) = kk;
-        *reinterpret_cast<uint4*>(sV + row * 128 + c8) = vv;
     }
     // ---- gate [LA-KDA §5.4] and in-chunk cumulative sum; padding rows: g = 0
     {
@@ -110,27 +129,27 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             const int row = half * 32 + i;
-            zr[i] = row < len ? z[(size_t)(tok0 + row) * tstride + hoff + c] : 0.f;
+            zr[i] = row < len ? z[tok(row) + c] : 0.f;
         }
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             const int row = half * 32 + i;
             run += row < len ? log_decay<false>(ea, zr[i]) : 0.f;
-            sG[row * 128 + c] = run;
+            sG[row * kLdG + c] = run;
         }
     }
     __syncthreads();
     if (tid >= 128) {
         const int c = tid & 127;
-        const float base = sG[31 * 128 + c];
+        const float base = sG[31 * kLdG + c];
 #pragma unroll
-        for (int i = 32; i < 64; i++) sG[i * 128 + c] += base;
+        for (int i = 32; i < 64; i++) sG[i * kLdG + c] += base;
     }
     __syncthreads();
-    if (tid < 128) reinterpret_cast<float*>(rec + REC_G)[tid] = __expf(sG[63 * 128 + tid]);
+    if (tid < 128) reinterpret_cast<float*>(rec + REC_G)[tid] = __expf(sG[63 * kLdG + tid]);
     if (DBG)
-        for (int idx = tid; idx < 8192; idx += 256) dbase[idx] = sG[idx];
+        for (int idx = tid; idx < 8192; idx += 256) dbase[idx] = sG[(idx >> 7) * kLdG + (idx & 127)];
 
     // ---- 2a. A_kk and A_qk: wave w owns row block r = w, column blocks s <= r
     f32x4 akk[4], aqk[4];
@@ -143,14 +162,14 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int ks = 0; ks < 4; ks++) {
             const int c0 = 32 * ks + 8 * g4;
             float bref[8], gi[8];
-            if (r > 0) load8f(sG + (16 * r - 1) * 128 + c0, bref);
+            if (r > 0) load8f(sG + (16 * r - 1) * kLdG + c0, bref);
             else {
 #pragma unroll
                 for (int e = 0; e < 8; e++) bref[e] = 0.f;
             }
-            load8f(sG + i * 128 + c0, gi);
-            const bf16x8 qi = *reinterpret_cast<const bf16x8*>(sQ + i * 128 + c0);
-            const bf16x8 ki = *reinterpret_cast<const bf16x8*>(sK + i * 128 + c0);
+            load8f(sG + i * kLdG + c0, gi);
+            const bf16x8 qi = __builtin_bit_cast(bf16x8, qa_raw[ks]);
+            const bf16x8 ki = *reinterpret_cast<const bf16x8*>(sK + i * kLdK + c0);
             bf16x8 fq, fk;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -163,8 +182,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 if (s <= r) {
                     const int j = 16 * s + n16;
                     float gj[8];
-                    load8f(sG + j * 128 + c0, gj);
-                    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(sK + j * 128 + c0);
+                    load8f(sG + j * kLdG + c0, gj);
+                    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(sK + j * kLdK + c0);
                     bf16x8 fb;
 #pragma unroll
                     for (int e = 0; e < 8; e++) fb[e] = (bf16)((float)kj[e] * __expf(bref[e] - gj[e]));
@@ -211,15 +230,15 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     {
         const int c0 = 32 * w + 8 * g4;
         float gc[8];
-        load8f(sG + 63 * 128 + c0, gc);
+        load8f(sG + 63 * kLdG + c0, gc);
         f32x4 tkg[4][2], tv[4][2], tkb[4][2];
 #pragma unroll
         for (int tt = 0; tt < 4; tt++) {
             const int row = 16 * tt + n16;
             float gr[8];
-            load8f(sG + row * 128 + c0, gr);
-            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(sK + row * 128 + c0);
-            const bf16x8 vv = *reinterpret_cast<const bf16x8*>(sV + row * 128 + c0);
+            load8f(sG + row * kLdG + c0, gr);
+            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(sK + row * kLdK + c0);
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, v_raw[tt]);
             bf16x8 akg, akb;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -248,51 +267,54 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
                 const int row = 16 * tb + n16, c = 32 * w + 16 * cb + 4 * g4;
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    qinit[cb][tb][e] = (float)sQ[row * 128 + c + e] * __expf(sG[row * 128 + c + e]);
+                const bf16x4 qq = __builtin_bit_cast(bf16x4, qt_raw[cb][tb]);
+                const float4 gg = *reinterpret_cast<const float4*>(sG + row * kLdG + c);
+                qinit[cb][tb][0] = (float)qq[0] * __expf(gg.x);
+                qinit[cb][tb][1] = (float)qq[1] * __expf(gg.y);
+                qinit[cb][tb][2] = (float)qq[2] * __expf(gg.z);
+                qinit[cb][tb][3] = (float)qq[3] * __expf(gg.w);
             }
     }
-    __syncthreads();   // q, k, v and G tiles are dead from here
+    __syncthreads();   // the k and G tiles are dead from here
 
     // ---- 2c. A_kk, A_qk, beta to LDS ----
-    float* sAkk = reinterpret_cast<float*>(smem);             // [64][64]
-    float* sAqk = reinterpret_cast<float*>(smem + 16384);     // [64][64]
-    float* sN = reinterpret_cast<float*>(smem + 32768);       // [64][64]
-    float* sBeta = reinterpret_cast<float*>(smem + 49152);    // [64]
-    float* sP = reinterpret_cast<float*>(smem + 49408);       // [4][16][16]
+    float* sAkk = reinterpret_cast<float*>(smem);                     // [64][kLdA]
+    float* sAqk = sAkk + 64 * kLdA;
+    float* sN = sAqk + 64 * kLdA;
+    float* sBeta = sN + 64 * kLdA;                                    // [64]
+    float* sP = sBeta + 64;                                           // [4][16][16]
 #pragma unroll
     for (int s = 0; s < 4; s++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int row = 16 * w + 4 * g4 + e, col = 16 * s + n16;
-            sAkk[row * 64 + col] = akk[s][e];
-            sAqk[row * 64 + col] = aqk[s][e];
+            sAkk[row * kLdA + col] = akk[s][e];
+            sAqk[row * kLdA + col] = aqk[s][e];
         }
-    for (int idx = tid; idx < 4096; idx += 256) sN[idx] = 0.f;
+    for (int idx = tid; idx < 4096; idx += 256) sN[(idx >> 6) * kLdA + (idx & 63)] = 0.f;
     if (tid < 64) sBeta[tid] = tid < len ? sigmoid_f<false>(bl[(size_t)(tok0 + tid) * H + h]) : 0.f;
     __syncthreads();
     if (DBG)
         for (int idx = tid; idx < 4096; idx += 256) {
-            dbase[8192 + idx] = sAkk[idx];
-            dbase[8192 + 4096 + idx] = sAqk[idx];
+            dbase[8192 + idx] = sAkk[(idx >> 6) * kLdA + (idx & 63)];
+            dbase[8192 + 4096 + idx] = sAqk[(idx >> 6) * kLdA + (idx & 63)];
         }
 
     // ---- 3. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
     // diagonal blocks: forward substitution, lane = (block, column)
     if (w == 0) {
         const int rb = g4, cc = n16;
-        const float* Ab = sAkk + (16 * rb) * 64 + 16 * rb;
+        const float* Ab = sAkk + (16 * rb) * kLdA + 16 * rb;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             float acc = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; m++) acc -= Ab[i * 64 + m] * x[m];
+            for (int m = 0; m < i; m++) acc -= Ab[i * kLdA + m] * x[m];
             x[i] = acc;
         }
 #pragma unroll
-        for (int i = 0; i < 16; i++) sN[(16 * rb + i) * 64 + 16 * rb + cc] = x[i];
+        for (int i = 0; i < 16; i++) sN[(16 * rb + i) * kLdA + 16 * rb + cc] = x[i];
     }
     __syncthreads();
     // off-diagonal blocks by distance d: N_rs = -N_rr sum_{m=s}^{r-1} A_rm N_ms
@@ -302,21 +324,22 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         if (act) {
             f32x4 P = zero4();
             for (int m = s; m < r; m++)
-                P = mm16_f32(P, sAkk + 16 * r * 64 + 16 * m, 64, sN + 16 * m * 64 + 16 * s, 64, n16, g4);
+                P = mm16_f32(P, sAkk + 16 * r * kLdA + 16 * m, kLdA, sN + 16 * m * kLdA + 16 * s, kLdA,
+                             n16, g4);
 #pragma unroll
             for (int e = 0; e < 4; e++) sP[w * 256 + (4 * g4 + e) * 16 + n16] = P[e];
         }
         __syncthreads();
         if (act) {
-            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * 64 + 16 * r, 64, sP + w * 256, 16, n16, g4);
+            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * kLdA + 16 * r, kLdA, sP + w * 256, 16, n16, g4);
 #pragma unroll
-            for (int e = 0; e < 4; e++) sN[(16 * r + 4 * g4 + e) * 64 + 16 * s + n16] = -R[e];
+            for (int e = 0; e < 4; e++) sN[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = -R[e];
         }
         __syncthreads();
     }
     if (DBG)
         for (int idx = tid; idx < 4096; idx += 256)
-            dbase[8192 + 8192 + idx] = sN[idx] * sBeta[idx & 63];
+            dbase[8192 + 8192 + idx] = sN[(idx >> 6) * kLdA + (idx & 63)] * sBeta[idx & 63];
 
     // ---- 4. products over tokens (wave w: channels [32w, 32w + 32)) ----
     // k-slot order of every token-contracting fragment: lane group g, slot e
@@ -328,15 +351,15 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             const int row = 16 * tb + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
-            const float4 n0 = *reinterpret_cast<const float4*>(sN + row * 64 + j0);
-            const float4 n1 = *reinterpret_cast<const float4*>(sN + row * 64 + j1);
+            const float4 n0 = *reinterpret_cast<const float4*>(sN + row * kLdA + j0);
+            const float4 n1 = *reinterpret_cast<const float4*>(sN + row * kLdA + j1);
             const float4 b0 = *reinterpret_cast<const float4*>(sBeta + j0);
             const float4 b1 = *reinterpret_cast<const float4*>(sBeta + j1);
             const f32x4 t0 = {n0.x * b0.x, n0.y * b0.y, n0.z * b0.z, n0.w * b0.w};
             const f32x4 t1 = {n1.x * b1.x, n1.y * b1.y, n1.z * b1.z, n1.w * b1.w};
             tf[tb][kb] = pack_frag(t0, t1);
-            const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * 64 + j0);
-            const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * 64 + j1);
+            const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j0);
+            const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j1);
             const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
             af[tb][kb] = pack_frag(x0, x1);
         }
@@ -411,12 +434,90 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 }
 
+// Operands of one chunk for one chain wave, loaded from the chunk record.
+struct ChainFrags {
+    bf16x8 w[4], q[4], k[4];   // -W^T, Q'^T (k-steps 0..3); Kbar^T [half][kstep]
+    bf16x4 u, y;               // U and Y tiles of this slice
+    float4 g0, g1;             // gamma_C for the wave's two row tiles
+};
+
+__device__ __forceinline__ void load_chain_frags(ChainFrags& f, const uint8_t* __restrict__ recs,
+                                                 int cid, int H, int h, int w, int sg, int lane,
+                                                 int g4) {
+    const uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
+        f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
+        f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 4 + ks) * 64 + lane) * 16);
+    }
+    f.u = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sg * 4 + w) * 64 + lane) * 8);
+    f.y = *reinterpret_cast<const bf16x4*>(rec + REC_Y + ((sg * 4 + w) * 64 + lane) * 8);
+    const float* gC = reinterpret_cast<const float*>(rec + REC_G);
+    f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
+    f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
+}
+
+// One chunk of the chain for one wave: V~, the output rows and the state update.
+template <bool DBG>
+__device__ __forceinline__ void chain_step(const ChainFrags& f, int cid, int tok0, int len,
+                                           f32x4 (&accS)[2],
+                                           bf16* sS, bf16* sVt, bf16* __restrict__ o,
+                                           float* __restrict__ dbgS, int H, int h, int w,
+                                           int lane, int g4, int col) {
+    if (DBG) {
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 32 * w + 16 * b + 4 * g4 + e;
+                dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col] = accS[b][e];
+            }
+    }
+    bf16x8 sf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) sf[ks] = *reinterpret_cast<const bf16x8*>(sS + (ks * 64 + lane) * 8);
+    f32x4 accV = unpack4(f.u);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[ks], accV);
+    *reinterpret_cast<bf16x4*>(sVt + (w * 64 + lane) * 4) = pack4(accV);
+    f32x4 accO = unpack4(f.y);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) accO = mfma_bf16(f.q[ks], sf[ks], accO);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int row = 16 * w + 4 * g4 + e;
+        if (row < len) o[((size_t)(tok0 + row) * H + h) * 128 + col] = (bf16)accO[e];
+    }
+    __syncthreads();
+    bf16x8 vfr[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+        vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((2 * kb) * 64 + lane) * 4),
+                           *reinterpret_cast<const bf16x4*>(sVt + ((2 * kb + 1) * 64 + lane) * 4));
+    accS[0][0] *= f.g0.x; accS[0][1] *= f.g0.y; accS[0][2] *= f.g0.z; accS[0][3] *= f.g0.w;
+    accS[1][0] *= f.g1.x; accS[1][1] *= f.g1.y; accS[1][2] *= f.g1.z; accS[1][3] *= f.g1.w;
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) accS[b] = mfma_bf16(f.k[b * 2 + kb], vfr[kb], accS[b]);
+    *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
+    __syncthreads();
+}
+
 // Workgroup = (sequence, head, slice of 16 state columns); 4 waves.
 // Wave w computes V~ and O rows [16w, 16w + 16) of every chunk and owns
 // state rows [32w, 32w + 32) of the slice as two fp32 C tiles.  Each chunk:
 //   V~ = U - W S,  O = Y + Q' S      (B operand: the bf16 copy of S in LDS)
 //   S <- Diag(gamma_C) S + Kbar^T V~ (B operand: V~ gathered through LDS)
 // The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
+// The chunk loop is serial, so the record loads of chunk c + kDepth - 1 are
+// issued while chunk c is computed (a register ring of kDepth operand sets).
+// The prefetch is unconditional (its index is clamped to the last chunk) so
+// that every path issues the same loads and the wait counts stay exact.
+constexpr int kDepth = 3;
+
+template <bool DBG>
 __global__ __launch_bounds__(256, 1)
 void fast_chain_kernel(const uint8_t* __restrict__ recs, const int2* __restrict__ seqs,
                        const int4* __restrict__ chunks, const float* __restrict__ h0,
@@ -447,70 +548,44 @@ void fast_chain_kernel(const uint8_t* __restrict__ recs, const int2* __restrict_
             accS[b][e] = h0 ? h0[((size_t)p * 128 + row) * 128 + col] : 0.f;
         }
     *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
-    __syncthreads();
 
     const int2 sd = seqs[n];
-    for (int ci = 0; ci < sd.y; ci++) {
-        const int cid = sd.x + ci;
-        const int4 cd = chunks[cid];
-        const int tok0 = cd.y, len = cd.z;
-        const uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
-        bf16x8 wf[4], qf[4], kf[2][2];
+    const int c0 = sd.x, nch = sd.y;
+    // the chunks of a sequence are consecutive and 64 tokens apart, so their
+    // token ranges follow from the first and the last one (no table reads,
+    // and no scalar loads, inside the loop)
+    int seq_tok0 = 0, seq_len = 0;
+    ChainFrags F[kDepth];
+    if (nch > 0) {
+        const int4 first = chunks[c0], last = chunks[c0 + nch - 1];
+        seq_tok0 = first.y;
+        seq_len = last.y + last.z - first.y;
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            wf[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
-            qf[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
-        }
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-                kf[b][kb] = *reinterpret_cast<const bf16x8*>(rec + REC_K + (((w * 2 + b) * 2 + kb) * 64 + lane) * 16);
-        const bf16x4 ut = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sg * 4 + w) * 64 + lane) * 8);
-        const bf16x4 yt = *reinterpret_cast<const bf16x4*>(rec + REC_Y + ((sg * 4 + w) * 64 + lane) * 8);
-        const float* gC = reinterpret_cast<const float*>(rec + REC_G);
-        const float4 gc0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
-        const float4 gc1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
-
-        if (dbgS) {
-#pragma unroll
-            for (int b = 0; b < 2; b++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int row = 32 * w + 16 * b + 4 * g4 + e;
-                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col] = accS[b][e];
-                }
-        }
-        bf16x8 sf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) sf[ks] = *reinterpret_cast<const bf16x8*>(sS + (ks * 64 + lane) * 8);
-        f32x4 accV = unpack4(ut), accO = unpack4(yt);
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            accV = mfma_bf16(wf[ks], sf[ks], accV);
-            accO = mfma_bf16(qf[ks], sf[ks], accO);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 16 * w + 4 * g4 + e;
-            if (row < len) o[((size_t)(tok0 + row) * H + h) * 128 + col] = (bf16)accO[e];
-        }
-        *reinterpret_cast<bf16x4*>(sVt + (w * 64 + lane) * 4) = pack4(accV);
-        __syncthreads();
-        bf16x8 vfr[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-            vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((2 * kb) * 64 + lane) * 4),
-                               *reinterpret_cast<const bf16x4*>(sVt + ((2 * kb + 1) * 64 + lane) * 4));
-        accS[0][0] *= gc0.x; accS[0][1] *= gc0.y; accS[0][2] *= gc0.z; accS[0][3] *= gc0.w;
-        accS[1][0] *= gc1.x; accS[1][1] *= gc1.y; accS[1][2] *= gc1.z; accS[1][3] *= gc1.w;
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++) accS[b] = mfma_bf16(kf[b][kb], vfr[kb], accS[b]);
-        *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
-        __syncthreads();
+        for (int u = 0; u < kDepth - 1; u++)
+            load_chain_frags(F[u], recs, c0 + min(u, nch - 1), H, h, w, sg, lane, g4);
     }
+    __syncthreads();
+
+    const int nfull = nch / kDepth * kDepth;
+    for (int ci = 0; ci < nfull; ci += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; u++) {
+            const int pf = min(ci + u + kDepth - 1, nch - 1);
+            load_chain_frags(F[(u + kDepth - 1) % kDepth], recs, c0 + pf, H, h, w, sg, lane, g4);
+            const int t0 = (ci + u) * C;
+            chain_step<DBG>(F[u], c0 + ci + u, seq_tok0 + t0, seq_len - t0, accS, sS, sVt, o, dbgS,
+                            H, h, w, lane, g4, col);
+        }
+    }
+    // at most kDepth - 1 chunks remain; their operands are already in F[0..]
+#pragma unroll
+    for (int u = 0; u < kDepth - 1; u++)
+        if (nfull + u < nch) {
+            const int t0 = (nfull + u) * C;
+            chain_step<DBG>(F[u], c0 + nfull + u, seq_tok0 + t0, seq_len - t0, accS, sS, sVt, o,
+                            dbgS, H, h, w, lane, g4, col);
+        }
+
     if (hT) {
 #pragma unroll
         for (int b = 0; b < 2; b++)
@@ -543,9 +618,14 @@ hipError_t launch_fast(const ChunkArgs& a) {
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
     const int P = a.N * a.H;
     const unsigned nblk = (unsigned)(((P + 7) / 8) * 64);
-    hipLaunchKernelGGL(fast_chain_kernel, dim3(nblk), dim3(256), 0, a.stream,
-                       (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
-                       a.dbg_state);
+    if (a.dbg_state)
+        hipLaunchKernelGGL(fast_chain_kernel<true>, dim3(nblk), dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
+                           a.dbg_state);
+    else
+        hipLaunchKernelGGL(fast_chain_kernel<false>, dim3(nblk), dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
+                           (float*)nullptr);
     return hipGetLastError();
 }
 
