@@ -68,6 +68,23 @@ def _elapsed(h, a, b) -> float:
     return float(ms.value)
 
 
+def _traffic_for(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic_long_1m.json), or None when the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_long_1m.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha1(src).hexdigest() != rec.get("source_sha1"):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["hbm_bytes"])
+
+
 def bench_prefill(args, kda, torch, KI):
     case = KI.CONFIGS["long_1m"]
     dev = torch.device("cuda:0")
@@ -129,7 +146,7 @@ def bench_prefill(args, kda, torch, KI):
     achieved = kd["alg_bytes"] / (kd["ms"] * 1e-3) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None}
+            "traffic": _traffic_for(dom)}
     call_gbs = PREFILL_BYTES * units / (avg["call"] * 1e-3) / 1e9
     call_tfs = PREFILL_FLOPS * units / (avg["call"] * 1e-3) / 1e12
     extra = {
@@ -206,6 +223,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="copy a buffer of this many MiB once before timing (a known-size "
+                         "kernel for calibrating the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -220,6 +240,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     kda.lib()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written", flush=True)
+        del src, dst
 
     value, ms, roof, extra, cpu_inp = bench_prefill(args, kda, torch, KI)
     dec = None if args.no_decode else bench_decode(args, kda, torch, KI)
