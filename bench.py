@@ -101,14 +101,14 @@ def bench_prefill(args, kda, torch, KI):
     stream = torch.cuda.current_stream(dev).cuda_stream
     h = _hip()
     nsteps = args.warmup + args.steps
-    evs = [[_event(h) for _ in range(4)] for _ in range(nsteps)]
+    evs = [[_event(h) for _ in range(6)] for _ in range(nsteps)]
     ptrs = (d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["z"].data_ptr(),
             d["b"].data_ptr(), d["A"].data_ptr(), d["h0"].data_ptr(), None, B, T, H, dk, dv, N,
             C, 1, o.data_ptr(), hT.data_ptr(), ws.data_ptr(), wsb)
 
     def step(i):
-        arr = (ctypes.c_void_p * 4)(*[e.value for e in evs[i]])
-        rc = L.kda_chunk_fwd_timed(*ptrs, arr, 4, stream)
+        arr = (ctypes.c_void_p * 6)(*[e.value for e in evs[i]])
+        rc = L.kda_chunk_fwd_timed(*ptrs, arr, 6, stream)
         if rc != 0:
             raise RuntimeError(L.kda_status_string(rc).decode())
 
@@ -120,11 +120,15 @@ def bench_prefill(args, kda, torch, KI):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {"prep": [], "intra": [], "chain": [], "call": []}
+    per = {"prep": [], "intra": [], "transition": [], "compose": [], "output": [], "chain": [],
+           "call": []}
     for i in range(args.warmup, nsteps):
         e = evs[i]
         per["prep"].append(_elapsed(h, e[0], e[1]))
         per["intra"].append(_elapsed(h, e[1], e[2]))
+        per["transition"].append(_elapsed(h, e[2], e[4]))
+        per["compose"].append(_elapsed(h, e[4], e[5]))
+        per["output"].append(_elapsed(h, e[5], e[3]))
         per["chain"].append(_elapsed(h, e[2], e[3]))
         per["call"].append(_elapsed(h, e[0], e[3]))
     for row in evs:
@@ -138,8 +142,8 @@ def bench_prefill(args, kda, torch, KI):
     units = tokens * H
     kernels = {
         "fast_intra_kernel": {"ms": avg["intra"], "alg_bytes": INTRA_BYTES * units},
-        "fast_chain_kernel": {"ms": avg["chain"],
-                              "alg_bytes": CHAIN_BYTES * units + 2 * N * H * dk * dv * 4},
+        "seg_chain_kernel<out>": {"ms": avg["output"],
+                                  "alg_bytes": CHAIN_BYTES * units + 2 * N * H * dk * dv * 4},
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
@@ -151,7 +155,7 @@ def bench_prefill(args, kda, torch, KI):
     call_tfs = PREFILL_FLOPS * units / (avg["call"] * 1e-3) / 1e12
     extra = {
         "call_ms_events": round(avg["call"], 4),
-        "kernels_ms": {k: round(v, 4) for k, v in avg.items() if k != "call"},
+        "kernels_ms": {k: round(v, 4) for k, v in avg.items() if k not in ("call", "chain")},
         "path_alg_GBps": round(call_gbs, 1),
         "path_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
         "path_alg_TFLOPs": round(call_tfs, 2),

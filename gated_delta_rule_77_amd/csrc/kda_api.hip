@@ -23,7 +23,8 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
                          const float* b, const float* A, const float* h0, const int* cu,
                          int B, int T, int H, int dk, int dv, int N, int chunk,
                          kda_dtype_t dtype, void* o, float* hT, void* ws, size_t ws_bytes,
-                         float* dbg_intra, float* dbg_state, hipEvent_t* ev, void* stream) {
+                         float* dbg_intra, float* dbg_state, hipEvent_t* ev, int n_ev,
+                         void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
     if (cu) {
@@ -47,6 +48,7 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.C = chunk;
     a.o = o; a.hT = hT; a.ws = static_cast<uint8_t*>(ws); a.L = L;
     a.dbg_intra = dbg_intra; a.dbg_state = dbg_state; a.ev = ev;
+    a.ev5 = (ev && n_ev >= 6) ? ev + 4 : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     hipError_t e = ev ? hipEventRecord(ev[0], a.stream) : hipSuccess;
     if (e == hipSuccess) e = launch_prep(a);
@@ -102,7 +104,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            int chunk, kda_dtype_t dtype, void* o, float* hT, void* workspace,
                            size_t workspace_bytes, void* stream) {
     return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
-                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, nullptr, 0,
                        stream);
 }
 
@@ -114,7 +116,7 @@ kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const void* v,
                                  float* dbg_intra, float* dbg_state, void* stream) {
     return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
                        chunk, dtype, o, hT, workspace, workspace_bytes, dbg_intra, dbg_state,
-                       nullptr, stream);
+                       nullptr, 0, stream);
 }
 
 kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
@@ -124,12 +126,14 @@ kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
                                  float* hT, void* workspace, size_t workspace_bytes,
                                  void* const* events, int n_events, void* stream) {
     if (!events || n_events < 4) return KDA_ERR_INVALID_ARG;
-    for (int i = 0; i < 4; i++)
+    const int n = n_events >= 6 ? 6 : 4;
+    hipEvent_t ev[6];
+    for (int i = 0; i < n; i++) {
         if (!events[i]) return KDA_ERR_INVALID_ARG;
-    hipEvent_t ev[4];
-    for (int i = 0; i < 4; i++) ev[i] = static_cast<hipEvent_t>(events[i]);
+        ev[i] = static_cast<hipEvent_t>(events[i]);
+    }
     return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
-                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, ev,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, ev, n,
                        stream);
 }
 

@@ -434,166 +434,287 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 }
 
-// Operands of one chunk for one chain wave, loaded from the chunk record.
+// ---------------------------------------------------------------------------
+// The chain over chunks, split into segments.
+//
+// A segment's chunks map its incoming state affinely: S_end = M S_start + R,
+// with R the state reached from zero and M the product of the per-chunk
+// transitions (the context-parallel composition of [LA-KDA §7.5], here
+// across the CUs of one GPU).  Three launches:
+//   mode kTrans  every segment but a sequence's last runs the chain on the
+//                augmented state [R | M] (R from 0 with the real U, M from I
+//                with U = 0): 256 columns, 4 workgroups of 64 columns;
+//   compose      per (sequence, head, 16 columns): S_start(j+1) = M_j S_start(j) + R_j
+//                in fp32, sequentially over the (few) segments;
+//   mode kOut    every segment re-runs from S_start with outputs; the
+//                sequence's last segment writes the final state.
+// Columns of the state evolve independently (the correction u_j depends only
+// on column j), so any column range can run alone.
+//
+// Workgroup = (segment, head, 64-column group); 4 waves.  Wave w computes
+// V~ and O rows [16w, 16w + 16) and owns state rows [32w, 32w + 32) of its 64
+// columns as four pairs of fp32 C tiles.  Per chunk and 16-column slice:
+//   V~ = U - W S,  O = Y + Q' S      (B operand: bf16 copy of S in LDS)
+//   S <- Diag(gamma_C) S + Kbar^T V~ (B operand: V~ gathered through LDS)
+// Every -W, Q', Kbar fragment a wave loads feeds all four slices.
+// The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
+constexpr int kNS = 4;        // 16-column slices per workgroup
+constexpr int kDepth = 3;     // record prefetch ring depth (chunks)
+constexpr int kOut = 0, kTrans = 1;
+
 struct ChainFrags {
     bf16x8 w[4], q[4], k[4];   // -W^T, Q'^T (k-steps 0..3); Kbar^T [half][kstep]
-    bf16x4 u, y;               // U and Y tiles of this slice
+    bf16x4 u[kNS], y[kNS];     // U and Y tiles of the workgroup's slices
     float4 g0, g1;             // gamma_C for the wave's two row tiles
 };
 
+template <int MODE, bool HAS_U>
 __device__ __forceinline__ void load_chain_frags(ChainFrags& f, const uint8_t* __restrict__ recs,
-                                                 int cid, int H, int h, int w, int sg, int lane,
+                                                 int cid, int H, int h, int w, int sg0, int lane,
                                                  int g4) {
     const uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
         f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
-        f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
         f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 4 + ks) * 64 + lane) * 16);
+        if (MODE == kOut)
+            f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
     }
-    f.u = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sg * 4 + w) * 64 + lane) * 8);
-    f.y = *reinterpret_cast<const bf16x4*>(rec + REC_Y + ((sg * 4 + w) * 64 + lane) * 8);
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++) {
+        if (HAS_U)
+            f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + (((sg0 + sl) * 4 + w) * 64 + lane) * 8);
+        if (MODE == kOut)
+            f.y[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_Y + (((sg0 + sl) * 4 + w) * 64 + lane) * 8);
+    }
     const float* gC = reinterpret_cast<const float*>(rec + REC_G);
     f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
 }
 
-// One chunk of the chain for one wave: V~, the output rows and the state update.
-template <bool DBG>
+// One chunk for one wave over its kNS slices.
+template <int MODE, bool HAS_U, bool DBG>
 __device__ __forceinline__ void chain_step(const ChainFrags& f, int cid, int tok0, int len,
-                                           f32x4 (&accS)[2],
-                                           bf16* sS, bf16* sVt, bf16* __restrict__ o,
-                                           float* __restrict__ dbgS, int H, int h, int w,
-                                           int lane, int g4, int col) {
+                                           f32x4 (&accS)[kNS][2], bf16* sS, bf16* sVt,
+                                           bf16* __restrict__ o, float* __restrict__ dbgS, int H,
+                                           int h, int w, int lane, int g4, int col0) {
     if (DBG) {
 #pragma unroll
-        for (int b = 0; b < 2; b++)
+        for (int sl = 0; sl < kNS; sl++)
+#pragma unroll
+            for (int b = 0; b < 2; b++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = 32 * w + 16 * b + 4 * g4 + e;
+                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col0 + 16 * sl] = accS[sl][b][e];
+                }
+    }
+    bf16x8 sf[kNS][4];
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++)
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            sf[sl][ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl * 4 + ks) * 64 + lane) * 8);
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++) {
+        f32x4 accV = HAS_U ? unpack4(f.u[sl]) : zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[sl][ks], accV);
+        *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
+    }
+    if (MODE == kOut) {
+#pragma unroll
+        for (int sl = 0; sl < kNS; sl++) {
+            f32x4 accO = unpack4(f.y[sl]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) accO = mfma_bf16(f.q[ks], sf[sl][ks], accO);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int row = 32 * w + 16 * b + 4 * g4 + e;
-                dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col] = accS[b][e];
+                const int row = 16 * w + 4 * g4 + e;
+                if (row < len)
+                    o[((size_t)(tok0 + row) * H + h) * 128 + col0 + 16 * sl] = (bf16)accO[e];
             }
-    }
-    bf16x8 sf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) sf[ks] = *reinterpret_cast<const bf16x8*>(sS + (ks * 64 + lane) * 8);
-    f32x4 accV = unpack4(f.u);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[ks], accV);
-    *reinterpret_cast<bf16x4*>(sVt + (w * 64 + lane) * 4) = pack4(accV);
-    f32x4 accO = unpack4(f.y);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) accO = mfma_bf16(f.q[ks], sf[ks], accO);
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const int row = 16 * w + 4 * g4 + e;
-        if (row < len) o[((size_t)(tok0 + row) * H + h) * 128 + col] = (bf16)accO[e];
+        }
     }
     __syncthreads();
-    bf16x8 vfr[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-        vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((2 * kb) * 64 + lane) * 4),
-                           *reinterpret_cast<const bf16x4*>(sVt + ((2 * kb + 1) * 64 + lane) * 4));
-    accS[0][0] *= f.g0.x; accS[0][1] *= f.g0.y; accS[0][2] *= f.g0.z; accS[0][3] *= f.g0.w;
-    accS[1][0] *= f.g1.x; accS[1][1] *= f.g1.y; accS[1][2] *= f.g1.z; accS[1][3] *= f.g1.w;
+    for (int sl = 0; sl < kNS; sl++) {
+        bf16x8 vfr[2];
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+        for (int kb = 0; kb < 2; kb++)
+            vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb) * 64 + lane) * 4),
+                               *reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb + 1) * 64 + lane) * 4));
+        f32x4& s0 = accS[sl][0];
+        f32x4& s1 = accS[sl][1];
+        s0[0] *= f.g0.x; s0[1] *= f.g0.y; s0[2] *= f.g0.z; s0[3] *= f.g0.w;
+        s1[0] *= f.g1.x; s1[1] *= f.g1.y; s1[2] *= f.g1.z; s1[3] *= f.g1.w;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) accS[b] = mfma_bf16(f.k[b * 2 + kb], vfr[kb], accS[b]);
-    *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
+        for (int kb = 0; kb < 2; kb++) {
+            s0 = mfma_bf16(f.k[kb], vfr[kb], s0);
+            s1 = mfma_bf16(f.k[2 + kb], vfr[kb], s1);
+        }
+        *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(s0, s1);
+    }
     __syncthreads();
 }
 
-// Workgroup = (sequence, head, slice of 16 state columns); 4 waves.
-// Wave w computes V~ and O rows [16w, 16w + 16) of every chunk and owns
-// state rows [32w, 32w + 32) of the slice as two fp32 C tiles.  Each chunk:
-//   V~ = U - W S,  O = Y + Q' S      (B operand: the bf16 copy of S in LDS)
-//   S <- Diag(gamma_C) S + Kbar^T V~ (B operand: V~ gathered through LDS)
-// The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
-// The chunk loop is serial, so the record loads of chunk c + kDepth - 1 are
-// issued while chunk c is computed (a register ring of kDepth operand sets).
-// The prefetch is unconditional (its index is clamped to the last chunk) so
-// that every path issues the same loads and the wait counts stay exact.
-constexpr int kDepth = 3;
-
-template <bool DBG>
-__global__ __launch_bounds__(256, 1)
-void fast_chain_kernel(const uint8_t* __restrict__ recs, const int2* __restrict__ seqs,
-                       const int4* __restrict__ chunks, const float* __restrict__ h0,
-                       int N, int H, bf16* __restrict__ o, float* __restrict__ hT,
-                       float* __restrict__ dbgS)
-{
-    // blocks 8 apart land on the same XCD: the 8 slices of one (sequence,
-    // head) share the chunk records through that XCD's L2
-    const int id = blockIdx.x;
-    const int p = (id >> 6) * 8 + (id & 7);
-    const int sg = (id >> 3) & 7;
-    if (p >= N * H) return;
-    const int n = p / H, h = p % H;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n16 = lane & 15, g4 = lane >> 4;
-    const int col = 16 * sg + n16;
-
-    __shared__ __align__(16) bf16 sS[4 * 64 * 8];
-    __shared__ __align__(16) bf16 sVt[4 * 64 * 4];
-
-    f32x4 accS[2];
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 32 * w + 16 * b + 4 * g4 + e;
-            accS[b][e] = h0 ? h0[((size_t)p * 128 + row) * 128 + col] : 0.f;
-        }
-    *reinterpret_cast<bf16x8*>(sS + (w * 64 + lane) * 8) = pack_frag(accS[0], accS[1]);
-
-    const int2 sd = seqs[n];
-    const int c0 = sd.x, nch = sd.y;
-    // the chunks of a sequence are consecutive and 64 tokens apart, so their
-    // token ranges follow from the first and the last one (no table reads,
-    // and no scalar loads, inside the loop)
-    int seq_tok0 = 0, seq_len = 0;
+template <int MODE, bool HAS_U, bool DBG>
+__device__ __forceinline__ void run_segment(const uint8_t* __restrict__ recs, int c0, int nch,
+                                            int seg_tok0, int seg_len, f32x4 (&accS)[kNS][2],
+                                            bf16* sS, bf16* sVt, bf16* __restrict__ o,
+                                            float* __restrict__ dbgS, int H, int h, int w, int sg0,
+                                            int lane, int g4, int col0) {
     ChainFrags F[kDepth];
     if (nch > 0) {
-        const int4 first = chunks[c0], last = chunks[c0 + nch - 1];
-        seq_tok0 = first.y;
-        seq_len = last.y + last.z - first.y;
 #pragma unroll
         for (int u = 0; u < kDepth - 1; u++)
-            load_chain_frags(F[u], recs, c0 + min(u, nch - 1), H, h, w, sg, lane, g4);
+            load_chain_frags<MODE, HAS_U>(F[u], recs, c0 + min(u, nch - 1), H, h, w, sg0, lane, g4);
     }
     __syncthreads();
-
     const int nfull = nch / kDepth * kDepth;
     for (int ci = 0; ci < nfull; ci += kDepth) {
 #pragma unroll
         for (int u = 0; u < kDepth; u++) {
+            // unconditional prefetch (index clamped) keeps the wait counts exact
             const int pf = min(ci + u + kDepth - 1, nch - 1);
-            load_chain_frags(F[(u + kDepth - 1) % kDepth], recs, c0 + pf, H, h, w, sg, lane, g4);
+            load_chain_frags<MODE, HAS_U>(F[(u + kDepth - 1) % kDepth], recs, c0 + pf, H, h, w, sg0,
+                                          lane, g4);
             const int t0 = (ci + u) * C;
-            chain_step<DBG>(F[u], c0 + ci + u, seq_tok0 + t0, seq_len - t0, accS, sS, sVt, o, dbgS,
-                            H, h, w, lane, g4, col);
+            chain_step<MODE, HAS_U, DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS,
+                                         sVt, o, dbgS, H, h, w, lane, g4, col0);
         }
     }
-    // at most kDepth - 1 chunks remain; their operands are already in F[0..]
 #pragma unroll
     for (int u = 0; u < kDepth - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            chain_step<DBG>(F[u], c0 + nfull + u, seq_tok0 + t0, seq_len - t0, accS, sS, sVt, o,
-                            dbgS, H, h, w, lane, g4, col);
+            chain_step<MODE, HAS_U, DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS,
+                                         sS, sVt, o, dbgS, H, h, w, lane, g4, col0);
         }
+}
 
-    if (hT) {
+// grid: ceil(seg_cap * H / 8) * 8 * G blocks, G = 64-column groups (2 for
+// kOut, 4 for kTrans); blocks 8 apart share an XCD, so the G groups of one
+// (segment, head) read its chunk records through the same L2.
+template <int MODE, bool DBG>
+__global__ __launch_bounds__(256, 1)
+void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
+                      const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
+                      const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
+                      float* __restrict__ rm, bf16* __restrict__ o, float* __restrict__ hT,
+                      float* __restrict__ dbgS)
+{
+    constexpr int G = MODE == kOut ? 2 : 4;
+    const int id = blockIdx.x;
+    const int p = (id / (8 * G)) * 8 + (id & 7);
+    const int grp = (id >> 3) % G;
+    const int seg_id = p / H, h = p % H;
+    if (seg_id >= hdr[1]) return;
+    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
+    const int n = sg.x, c0 = sg.y, nch = sg.z, jseg = sg.w;
+    const int2 ss = seqsegs[n];
+    const bool last = jseg == ss.y - 1;
+    if (MODE == kTrans && last) return;    // the last segment's transition is never needed
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int col0 = 64 * grp + n16;       // column of slice 0 (0..255 in [R | M])
+
+    __shared__ __align__(16) bf16 sS[kNS * 4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[kNS * 4 * 64 * 4];
+
+    f32x4 accS[kNS][2];
+    const float* st = sstart + ((size_t)seg_id * H + h) * 128 * 128;
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int row = 32 * w + 16 * b + 4 * g4 + e;
-                hT[((size_t)p * 128 + row) * 128 + col] = accS[b][e];
+                const int col = col0 + 16 * sl;
+                float x;
+                if (MODE == kOut) x = st[row * 128 + col];
+                else x = (grp >= 2 && row == col - 128) ? 1.f : 0.f;
+                accS[sl][b][e] = x;
             }
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++)
+        *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(accS[sl][0], accS[sl][1]);
+
+    int seg_tok0 = 0, seg_len = 0;
+    if (nch > 0) {
+        const int4 first = chunks[c0], lastc = chunks[c0 + nch - 1];
+        seg_tok0 = first.y;
+        seg_len = lastc.y + lastc.z - first.y;
+    }
+    const int sg0 = (grp & 1) * kNS;       // first 16-column slice of U/Y (R part and outputs)
+    if (MODE == kOut || grp < 2)
+        run_segment<MODE, true, DBG>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, o, dbgS, H, h,
+                                     w, sg0, lane, g4, col0);
+    else
+        run_segment<MODE, false, false>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, o, dbgS,
+                                        H, h, w, sg0, lane, g4, col0);
+
+#pragma unroll
+    for (int sl = 0; sl < kNS; sl++)
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 32 * w + 16 * b + 4 * g4 + e;
+                const int col = col0 + 16 * sl;
+                if (MODE == kTrans)
+                    rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = accS[sl][b][e];
+                else if (last && hT)
+                    hT[(((size_t)n * H + h) * 128 + row) * 128 + col] = accS[sl][b][e];
+            }
+}
+
+// Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and
+// S_start(j+1) = M_j S_start(j) + R_j.  A sequence without chunks gets
+// hT = h0 here.  Thread t owns column 16*slice + (t & 15), rows 8*(t >> 4) + r.
+__global__ __launch_bounds__(256)
+void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ h0,
+                    const float* __restrict__ rm, float* __restrict__ sstart,
+                    float* __restrict__ hT, int N, int H)
+{
+    const int bid = blockIdx.x;
+    const int sl = bid & 7, p = bid >> 3;
+    const int n = p / H, h = p % H;
+    const int t = threadIdx.x;
+    const int c = 16 * sl + (t & 15), r0 = 8 * (t >> 4);
+    __shared__ float sSt[128][17];
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        x[r] = h0 ? h0[((size_t)p * 128 + r0 + r) * 128 + c] : 0.f;
+    const int2 ss = seqsegs[n];
+    if (ss.y == 0) {
+        if (hT)
+#pragma unroll
+            for (int r = 0; r < 8; r++) hT[((size_t)p * 128 + r0 + r) * 128 + c] = x[r];
+        return;
+    }
+    for (int j = 0; j < ss.y; j++) {
+        const size_t seg = (size_t)(ss.x + j);
+#pragma unroll
+        for (int r = 0; r < 8; r++) sstart[((seg * H + h) * 128 + r0 + r) * 128 + c] = x[r];
+        if (j == ss.y - 1) break;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 8; r++) sSt[r0 + r][t & 15] = x[r];
+        __syncthreads();
+        const float* RM = rm + (seg * H + h) * 128 * 256;
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const float* Mrow = RM + (size_t)(r0 + r) * 256 + 128;
+            float acc = RM[(size_t)(r0 + r) * 256 + c];
+#pragma unroll 8
+            for (int k = 0; k < 128; k++) acc += Mrow[k] * sSt[k][t & 15];
+            x[r] = acc;
+        }
     }
 }
 
@@ -602,8 +723,11 @@ void fast_chain_kernel(const uint8_t* __restrict__ recs, const int2* __restrict_
 hipError_t launch_fast(const ChunkArgs& a) {
     const int* hdr = reinterpret_cast<const int*>(a.ws);
     const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
-    const int2* seqs = reinterpret_cast<const int2*>(a.ws + a.L.off_seqs);
+    const int2* seqsegs = reinterpret_cast<const int2*>(a.ws + a.L.off_seqsegs);
+    const int4* segs = reinterpret_cast<const int4*>(a.ws + a.L.off_segs);
     uint8_t* recs = a.ws + a.L.off_recs;
+    float* sstart = reinterpret_cast<float*>(a.ws + a.L.off_sstart);
+    float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
     const dim3 gi((unsigned)a.L.cap, (unsigned)a.H);
     if (a.dbg_intra)
         hipLaunchKernelGGL(fast_intra_kernel<true>, gi, dim3(256), 0, a.stream,
@@ -616,16 +740,26 @@ hipError_t launch_fast(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
-    const int P = a.N * a.H;
-    const unsigned nblk = (unsigned)(((P + 7) / 8) * 64);
+
+    const long long pairs = (long long)a.L.seg_cap * a.H;
+    const unsigned blk8 = (unsigned)((pairs + 7) / 8);
+    hipLaunchKernelGGL((seg_chain_kernel<kTrans, false>), dim3(blk8 * 8 * 4), dim3(256), 0, a.stream,
+                       (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
+                       rm, (bf16*)nullptr, (float*)nullptr, (float*)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(compose_kernel, dim3((unsigned)(a.N * a.H * 8)), dim3(256), 0, a.stream,
+                       seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     if (a.dbg_state)
-        hipLaunchKernelGGL(fast_chain_kernel<true>, dim3(nblk), dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
-                           a.dbg_state);
+        hipLaunchKernelGGL((seg_chain_kernel<kOut, true>), dim3(blk8 * 8 * 2), dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
+                           rm, (bf16*)a.o, a.hT, a.dbg_state);
     else
-        hipLaunchKernelGGL(fast_chain_kernel<false>, dim3(nblk), dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, seqs, chunks, a.h0, a.N, a.H, (bf16*)a.o, a.hT,
-                           (float*)nullptr);
+        hipLaunchKernelGGL((seg_chain_kernel<kOut, false>), dim3(blk8 * 8 * 2), dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
+                           rm, (bf16*)a.o, a.hT, (float*)nullptr);
     return hipGetLastError();
 }
 

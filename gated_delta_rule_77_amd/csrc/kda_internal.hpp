@@ -17,8 +17,11 @@ namespace kda {
 // Chunks are numbered sequence by sequence in token order; `cap` bounds their
 // number for both layouts: B*ceil(T/C) + N.
 struct WsLayout {
-    int cap;
-    size_t off_chunks, off_seqs, off_recs, rec_bytes, total;
+    int cap;                 // chunk capacity
+    int seg_chunks;          // chunks per segment of the MFMA chain (0 on the fp32 path)
+    int seg_cap;             // segment capacity
+    size_t off_chunks, off_seqs, off_seqsegs, off_segs, off_recs, rec_bytes;
+    size_t off_sstart, off_rm, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -52,15 +55,42 @@ inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
     return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
 }
 
+// Chunks per segment of the MFMA chain: enough segments that the chain
+// phases have about two workgroups per CU on a large problem, at least 16
+// chunks (1024 tokens) per segment.
+inline int pick_seg_chunks(int cap, int H) {
+    long long target_items = 512;              // (segment, head, 64-column group) items
+    long long per = ((long long)cap * H * 2 + target_items - 1) / target_items;
+    if (per < 16) per = 16;
+    if (per > cap) per = cap > 0 ? cap : 1;
+    return (int)per;
+}
+
+// Workspace layout (all offsets 256-byte aligned):
+// [0, 256)   header: int32 total chunks, int32 total segments
+// chunks     cap x int4 (sequence, first token, length, 0)
+// seqs       N x int2 (first chunk id, number of chunks)
+// seqsegs    N x int2 (first segment id, number of segments)      [MFMA path]
+// segs       seg_cap x int4 (sequence, first chunk id, chunks, index in sequence)
+// recs       cap x H chunk records
+// sstart     seg_cap x H x 128 x 128 fp32: state entering each segment
+// rm         seg_cap x H x 128 x 256 fp32: [R | M] of each segment
 inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, bool fast) {
     WsLayout L{};
     L.cap = chunk_capacity(B, T, N, C);
     if (L.cap < 0) { L.total = 0; return L; }
+    const size_t n1 = (size_t)(N > 0 ? N : 1);
     L.off_chunks = 256;
     L.off_seqs = align_up(L.off_chunks + (size_t)L.cap * 16, 256);
-    L.off_recs = align_up(L.off_seqs + (size_t)(N > 0 ? N : 1) * 8, 256);
+    L.off_seqsegs = align_up(L.off_seqs + n1 * 8, 256);
+    L.seg_chunks = fast ? pick_seg_chunks(L.cap, H) : 0;
+    L.seg_cap = fast ? (L.cap + L.seg_chunks - 1) / L.seg_chunks + (N > 0 ? N : 1) : 0;
+    L.off_segs = align_up(L.off_seqsegs + n1 * 8, 256);
+    L.off_recs = align_up(L.off_segs + (size_t)L.seg_cap * 16, 256);
     L.rec_bytes = fast ? (size_t)fast::REC_BYTES : generic_rec_floats(dk, dv, C) * 4;
-    L.total = L.off_recs + (size_t)L.cap * H * L.rec_bytes;
+    L.off_sstart = align_up(L.off_recs + (size_t)L.cap * H * L.rec_bytes, 256);
+    L.off_rm = align_up(L.off_sstart + (size_t)L.seg_cap * H * 128 * 128 * 4, 256);
+    L.total = L.off_rm + (size_t)L.seg_cap * H * 128 * 256 * 4;
     return L;
 }
 
@@ -73,6 +103,7 @@ struct ChunkArgs {
     uint8_t* ws; WsLayout L;
     float* dbg_intra; float* dbg_state;
     hipEvent_t* ev;            // 4 events recorded around the kernels, or null
+    hipEvent_t* ev5;           // 2 more: after the transition and compose phases, or null
     hipStream_t stream;
 };
 

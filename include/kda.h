@@ -160,7 +160,10 @@ KDA_API kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const voi
  * events[1] after it, events[2] after the intra-chunk kernel (gate, A_kk,
  * A_qk, triangular inverse, W, U), events[3] after the state-chain kernel
  * (inter-chunk state and outputs).  `events` points to n_events >= 4
- * hipEvent_t handles (as void*).  Results are identical to kda_chunk_fwd.
+ * hipEvent_t handles (as void*).  With n_events >= 6 on the MFMA path,
+ * events[4] is recorded after the segment-transition kernel and events[5]
+ * after the segment-composition kernel (both between events[2] and
+ * events[3]).  Results are identical to kda_chunk_fwd.
  */
 KDA_API kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
                                          const float* g_logits, const float* beta_logits,

@@ -53,10 +53,13 @@ def test_supported_sets(L):
 
 
 def test_workspace_bytes(L):
-    # capacity = B * ceil(T / C) + N chunk records of 82432 bytes per head on the MFMA path
+    # the workspace holds per-(chunk, head) records (tens of KiB each on the MFMA
+    # path) for a capacity of B * ceil(T / C) + N chunks, plus per-segment states
     n = L.kda_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 1, 64, 1)
-    assert n >= (64 + 1) * 16 * 82432
-    assert n < (64 + 1) * 16 * 82432 + 8192
+    assert n >= (64 + 1) * 16 * 65536
+    assert n < (64 + 1) * 16 * 256 * 1024
+    n2 = L.kda_chunk_fwd_workspace_bytes(1, 8192, 16, 128, 128, 1, 64, 1)
+    assert n2 > n
     assert L.kda_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 64, 1, 64, 1) == 0
     assert L.kda_chunk_fwd_workspace_bytes(-1, 4096, 16, 128, 128, 1, 64, 1) == 0
     assert L.kda_chunk_fwd_workspace_bytes(1, 64, 2, 16, 16, 1, 16, 0) > 0
