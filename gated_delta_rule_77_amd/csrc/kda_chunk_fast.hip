@@ -673,47 +673,86 @@ void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
 }
 
 // Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and
-// S_start(j+1) = M_j S_start(j) + R_j.  A sequence without chunks gets
-// hT = h0 here.  Thread t owns column 16*slice + (t & 15), rows 8*(t >> 4) + r.
+// S_start(j+1) = M_j S_start(j) + R_j, sequentially over the segments.  A
+// sequence without chunks gets hT = h0 here.  M_j is staged in LDS; wave w
+// computes state rows [32w, 32w + 32) with fp32 MFMA, each lane holding the
+// C-tile elements (rows 32w + 16b + 4g + e, column 16*slice + n).
+// grid: ceil(N*H / 8) * 64 blocks; the 8 slices of one (sequence, head) are
+// 8 blocks apart (same XCD), so they read M_j and R_j through one L2.
 __global__ __launch_bounds__(256)
 void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ h0,
                     const float* __restrict__ rm, float* __restrict__ sstart,
                     float* __restrict__ hT, int N, int H)
 {
-    const int bid = blockIdx.x;
-    const int sl = bid & 7, p = bid >> 3;
+    const int id = blockIdx.x;
+    const int p = (id >> 6) * 8 + (id & 7);
+    const int sl = (id >> 3) & 7;
+    if (p >= N * H) return;
     const int n = p / H, h = p % H;
-    const int t = threadIdx.x;
-    const int c = 16 * sl + (t & 15), r0 = 8 * (t >> 4);
-    __shared__ float sSt[128][17];
-    float x[8];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int col = 16 * sl + n16;
+    __shared__ __align__(16) float sM[128 * 132];
+    __shared__ float sSt[128 * 17];
+
+    f32x4 x[2];
 #pragma unroll
-    for (int r = 0; r < 8; r++)
-        x[r] = h0 ? h0[((size_t)p * 128 + r0 + r) * 128 + c] : 0.f;
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 32 * w + 16 * b + 4 * g4 + e;
+            x[b][e] = h0 ? h0[((size_t)p * 128 + row) * 128 + col] : 0.f;
+        }
     const int2 ss = seqsegs[n];
     if (ss.y == 0) {
         if (hT)
 #pragma unroll
-            for (int r = 0; r < 8; r++) hT[((size_t)p * 128 + r0 + r) * 128 + c] = x[r];
+            for (int b = 0; b < 2; b++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = 32 * w + 16 * b + 4 * g4 + e;
+                    hT[((size_t)p * 128 + row) * 128 + col] = x[b][e];
+                }
         return;
     }
     for (int j = 0; j < ss.y; j++) {
         const size_t seg = (size_t)(ss.x + j);
 #pragma unroll
-        for (int r = 0; r < 8; r++) sstart[((seg * H + h) * 128 + r0 + r) * 128 + c] = x[r];
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 32 * w + 16 * b + 4 * g4 + e;
+                sstart[((seg * H + h) * 128 + row) * 128 + col] = x[b][e];
+            }
         if (j == ss.y - 1) break;
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < 8; r++) sSt[r0 + r][t & 15] = x[r];
-        __syncthreads();
         const float* RM = rm + (seg * H + h) * 128 * 256;
+        __syncthreads();                       // previous step done with sM, sSt
 #pragma unroll
-        for (int r = 0; r < 8; r++) {
-            const float* Mrow = RM + (size_t)(r0 + r) * 256 + 128;
-            float acc = RM[(size_t)(r0 + r) * 256 + c];
+        for (int i = 0; i < 16; i++) {         // M = columns 128..255 of [R | M]
+            const int idx = i * 256 + tid;     // float4 index over 128 rows x 32 float4
+            const int row = idx >> 5, c4 = idx & 31;
+            *reinterpret_cast<float4*>(sM + row * 132 + 4 * c4) =
+                *reinterpret_cast<const float4*>(RM + (size_t)row * 256 + 128 + 4 * c4);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) sSt[(32 * w + 16 * b + 4 * g4 + e) * 17 + n16] = x[b][e];
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 32 * w + 16 * b + 4 * g4 + e;
+                acc[e] = RM[(size_t)row * 256 + col];
+            }
+            const float* Ab = sM + (32 * w + 16 * b + n16) * 132;
 #pragma unroll 8
-            for (int k = 0; k < 128; k++) acc += Mrow[k] * sSt[k][t & 15];
-            x[r] = acc;
+            for (int ks = 0; ks < 32; ks++)
+                acc = mfma_f32(Ab[4 * ks + g4], sSt[(4 * ks + g4) * 17 + n16], acc);
+            x[b] = acc;
         }
     }
 }
@@ -748,7 +787,8 @@ hipError_t launch_fast(const ChunkArgs& a) {
                        rm, (bf16*)nullptr, (float*)nullptr, (float*)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(compose_kernel, dim3((unsigned)(a.N * a.H * 8)), dim3(256), 0, a.stream,
+    const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
+    hipLaunchKernelGGL(compose_kernel, dim3(cblk), dim3(256), 0, a.stream,
                        seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;

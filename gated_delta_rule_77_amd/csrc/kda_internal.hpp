@@ -55,12 +55,15 @@ inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
     return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
 }
 
-// Chunks per segment of the MFMA chain: enough segments that the chain
-// phases have about two workgroups per CU on a large problem, at least 16
-// chunks (1024 tokens) per segment.
+// Chunks per segment of the MFMA chain.  The output phase runs one
+// workgroup per (segment, head, 64-column group) and one workgroup fits a CU,
+// so the sequence is cut into about 512 / (2 H) segments: two full rounds of
+// 256 CUs on a long single sequence.  At least 16 chunks (1024 tokens) per
+// segment.
 inline int pick_seg_chunks(int cap, int H) {
-    long long target_items = 512;              // (segment, head, 64-column group) items
-    long long per = ((long long)cap * H * 2 + target_items - 1) / target_items;
+    long long nseg = 512 / (2LL * H);
+    if (nseg < 1) nseg = 1;
+    long long per = (cap + nseg - 1) / nseg;
     if (per < 16) per = 16;
     if (per > cap) per = cap > 0 ? cap : 1;
     return (int)per;
