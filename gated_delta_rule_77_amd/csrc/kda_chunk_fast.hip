@@ -345,7 +345,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // k-slot order of every token-contracting fragment: lane group g, slot e
     // holds token 32*kb + 4g + e (e < 4) or 32*kb + 16 + 4g + (e - 4) (e >= 4),
     // matching two stacked C tiles.
-    bf16x8 tf[4][2], af[4][2];      // T and A_qk row fragments [row block][kstep]
+    bf16x8 tf[4][2];                // T row fragments [row block][kstep]
 #pragma unroll
     for (int tb = 0; tb < 4; tb++)
 #pragma unroll
@@ -358,11 +358,16 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             const f32x4 t0 = {n0.x * b0.x, n0.y * b0.y, n0.z * b0.z, n0.w * b0.w};
             const f32x4 t1 = {n1.x * b1.x, n1.y * b1.y, n1.z * b1.z, n1.w * b1.w};
             tf[tb][kb] = pack_frag(t0, t1);
-            const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j0);
-            const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j1);
-            const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
-            af[tb][kb] = pack_frag(x0, x1);
         }
+    // A_qk rows of token block w, same k-slot order, to the record
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        const int row = 16 * w + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
+        const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j0);
+        const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j1);
+        const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
+        *reinterpret_cast<bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16) = pack_frag(x0, x1);
+    }
 
     // W^T = (K . Gamma)^T T^T: tiles [channel][token], stored negated as the
     // chain's A operand (wave tb of the chain, k-step w)
@@ -376,62 +381,21 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
     }
-    // W = T (K . Gamma) in the C layout, kept as negated token-slot fragments
-    bf16x8 wcf[2][2];
-    {
-        f32x4 wc[4][2];
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++)
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) {
-                wc[tb][cb] = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) wc[tb][cb] = mfma_bf16(tf[tb][kb], kgf[kb][cb], wc[tb][cb]);
-            }
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) wcf[kb][cb] = pack_frag_neg(wc[2 * kb][cb], wc[2 * kb + 1][cb]);
-    }
-    // U = T V: chain tiles (slice 2w + cb, wave tb) and token-slot fragments
-    bf16x8 uf[2][2];
-    {
-        f32x4 u[4][2];
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++)
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) {
-                u[tb][cb] = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) u[tb][cb] = mfma_bf16(tf[tb][kb], vf[kb][cb], u[tb][cb]);
-                *reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(u[tb][cb]);
-            }
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) uf[kb][cb] = pack_frag(u[2 * kb][cb], u[2 * kb + 1][cb]);
-    }
-    // Y = A_qk U
+    // U = T V: tiles (slice 2w + cb, token block tb)
 #pragma unroll
     for (int tb = 0; tb < 4; tb++)
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
-            f32x4 y = zero4();
+            f32x4 u = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) y = mfma_bf16(af[tb][kb], uf[kb][cb], y);
-            *reinterpret_cast<bf16x4*>(rec + REC_Y + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(y);
+            for (int kb = 0; kb < 2; kb++) u = mfma_bf16(tf[tb][kb], vf[kb][cb], u);
+            *reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(u);
         }
-    // Q'^T = (Q . Gamma)^T - W^T A_qk^T
+    // (Q . Gamma)^T: tiles [channel][token] as A operand fragments (k-step w)
 #pragma unroll
-    for (int tb = 0; tb < 4; tb++) {
-        f32x4 q0 = qinit[0][tb], q1 = qinit[1][tb];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            q0 = mfma_bf16(wcf[kb][0], af[tb][kb], q0);
-            q1 = mfma_bf16(wcf[kb][1], af[tb][kb], q1);
-        }
-        *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag(q0, q1);
-    }
+    for (int tb = 0; tb < 4; tb++)
+        *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tb * 4 + w) * 64 + lane) * 16) =
+            pack_frag(qinit[0][tb], qinit[1][tb]);
 }
 
 // ---------------------------------------------------------------------------
@@ -443,102 +407,110 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // across the CUs of one GPU).  Three launches:
 //   mode kTrans  every segment but a sequence's last runs the chain on the
 //                augmented state [R | M] (R from 0 with the real U, M from I
-//                with U = 0): 256 columns, 4 workgroups of 64 columns;
+//                with U = 0): 256 columns;
 //   compose      per (sequence, head, 16 columns): S_start(j+1) = M_j S_start(j) + R_j
 //                in fp32, sequentially over the (few) segments;
 //   mode kOut    every segment re-runs from S_start with outputs; the
 //                sequence's last segment writes the final state.
-// Columns of the state evolve independently (the correction u_j depends only
-// on column j), so any column range can run alone.
 //
-// Workgroup = (segment, head, 64-column group); 4 waves.  Wave w computes
-// V~ and O rows [16w, 16w + 16) and owns state rows [32w, 32w + 32) of its 64
-// columns as four pairs of fp32 C tiles.  Per chunk and 16-column slice:
-//   V~ = U - W S,  O = Y + Q' S      (B operand: bf16 copy of S in LDS)
-//   S <- Diag(gamma_C) S + Kbar^T V~ (B operand: V~ gathered through LDS)
-// Every -W, Q', Kbar fragment a wave loads feeds all four slices.
+// Workgroup = (segment, head[, half]), 4 waves, 128 columns: each record
+// byte is read once per workgroup.  Wave w computes V~ and O rows [16w, 16w + 16) and
+// owns state rows [32w, 32w + 32) as NS pairs of fp32 C tiles (one pair per
+// 16-column slice).  Per chunk:
+//   V~ = U - W S,  O = (Q . Gamma) S + A_qk V~   (B operands: bf16 copy of S
+//                                                  and V~ gathered in LDS)
+//   S <- Diag(gamma_C) S + Kbar^T V~
 // The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
-constexpr int kNS = 4;        // 16-column slices per workgroup
-constexpr int kDepth = 3;     // record prefetch ring depth (chunks)
 constexpr int kOut = 0, kTrans = 1;
 
+template <int MODE> struct ChainCfg;
+template <> struct ChainCfg<kTrans> { static constexpr int NS = 8, DEPTH = 3; };
+template <> struct ChainCfg<kOut>   { static constexpr int NS = 8,  DEPTH = 3; };
+
+template <int MODE, bool HAS_U>
 struct ChainFrags {
-    bf16x8 w[4], q[4], k[4];   // -W^T, Q'^T (k-steps 0..3); Kbar^T [half][kstep]
-    bf16x4 u[kNS], y[kNS];     // U and Y tiles of the workgroup's slices
-    float4 g0, g1;             // gamma_C for the wave's two row tiles
+    bf16x8 w[4], k[4];                      // -W^T (k-steps 0..3); Kbar^T [half][kstep]
+    bf16x8 q[MODE == kOut ? 4 : 1];         // (Q . Gamma)^T (k-steps 0..3)
+    bf16x8 a[MODE == kOut ? 2 : 1];         // A_qk rows (k-steps 0..1)
+    bf16x4 u[HAS_U ? 8 : 1];                // U tiles of the 8 slices
+    float4 g0, g1;                          // gamma_C for the wave's two row tiles
 };
 
 template <int MODE, bool HAS_U>
-__device__ __forceinline__ void load_chain_frags(ChainFrags& f, const uint8_t* __restrict__ recs,
-                                                 int cid, int H, int h, int w, int sg0, int lane,
+__device__ __forceinline__ void load_chain_frags(ChainFrags<MODE, HAS_U>& f,
+                                                 const uint8_t* __restrict__ rec, int w, int lane,
                                                  int g4) {
-    const uint8_t* rec = recs + ((size_t)cid * H + h) * REC_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
         f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
         f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 4 + ks) * 64 + lane) * 16);
-        if (MODE == kOut)
+        if constexpr (MODE == kOut)
             f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
     }
+    if constexpr (MODE == kOut) {
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++) {
-        if (HAS_U)
-            f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + (((sg0 + sl) * 4 + w) * 64 + lane) * 8);
-        if (MODE == kOut)
-            f.y[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_Y + (((sg0 + sl) * 4 + w) * 64 + lane) * 8);
+        for (int kb = 0; kb < 2; kb++)
+            f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16);
+    }
+    if constexpr (HAS_U) {
+#pragma unroll
+        for (int sl = 0; sl < 8; sl++)
+            f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sl * 4 + w) * 64 + lane) * 8);
     }
     const float* gC = reinterpret_cast<const float*>(rec + REC_G);
     f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
 }
 
-// One chunk for one wave over its kNS slices.
+constexpr int kLdO = 136;   // bf16 output staging rows [64][kLdO]
+
+// One chunk for one wave over all NS slices.
 template <int MODE, bool HAS_U, bool DBG>
-__device__ __forceinline__ void chain_step(const ChainFrags& f, int cid, int tok0, int len,
-                                           f32x4 (&accS)[kNS][2], bf16* sS, bf16* sVt,
-                                           bf16* __restrict__ o, float* __restrict__ dbgS, int H,
-                                           int h, int w, int lane, int g4, int col0) {
+__device__ __forceinline__ void chain_step(const ChainFrags<MODE, HAS_U>& f, int cid, int tok0, int len,
+                                           f32x4 (&accS)[ChainCfg<MODE>::NS][2], bf16* sS,
+                                           bf16* sVt, bf16* sO, bf16* __restrict__ o,
+                                           float* __restrict__ dbgS, int H, int h, int w,
+                                           int lane, int n16, int g4, int tid) {
+    constexpr int NS = ChainCfg<MODE>::NS;
     if (DBG) {
 #pragma unroll
-        for (int sl = 0; sl < kNS; sl++)
+        for (int sl = 0; sl < NS; sl++)
 #pragma unroll
             for (int b = 0; b < 2; b++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int row = 32 * w + 16 * b + 4 * g4 + e;
-                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + col0 + 16 * sl] = accS[sl][b][e];
+                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * sl + n16] = accS[sl][b][e];
                 }
     }
-    bf16x8 sf[kNS][4];
+    f32x4 accO[MODE == kOut ? NS : 1];
+    // V~ (and the (Q . Gamma) S part of O), four slices at a time
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++)
+    for (int b4 = 0; b4 < NS / 4; b4++) {
+        bf16x8 sf[4][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            sf[sl][ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl * 4 + ks) * 64 + lane) * 8);
+        for (int s4 = 0; s4 < 4; s4++)
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++) {
-        f32x4 accV = HAS_U ? unpack4(f.u[sl]) : zero4();
+            for (int ks = 0; ks < 4; ks++)
+                sf[s4][ks] = *reinterpret_cast<const bf16x8*>(sS + (((4 * b4 + s4) * 4 + ks) * 64 + lane) * 8);
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[sl][ks], accV);
-        *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
-    }
-    if (MODE == kOut) {
+        for (int s4 = 0; s4 < 4; s4++) {
+            const int sl = 4 * b4 + s4;
+            f32x4 accV = HAS_U ? unpack4(f.u[sl]) : zero4();
 #pragma unroll
-        for (int sl = 0; sl < kNS; sl++) {
-            f32x4 accO = unpack4(f.y[sl]);
+            for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
+            *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
+            if constexpr (MODE == kOut) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) accO = mfma_bf16(f.q[ks], sf[sl][ks], accO);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = 16 * w + 4 * g4 + e;
-                if (row < len)
-                    o[((size_t)(tok0 + row) * H + h) * 128 + col0 + 16 * sl] = (bf16)accO[e];
+                for (int ks = 0; ks < 4; ks++) acc = mfma_bf16(f.q[ks], sf[s4][ks], acc);
+                accO[sl] = acc;
             }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++) {
+    for (int sl = 0; sl < NS; sl++) {
         bf16x8 vfr[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -554,48 +526,69 @@ __device__ __forceinline__ void chain_step(const ChainFrags& f, int cid, int tok
             s1 = mfma_bf16(f.k[2 + kb], vfr[kb], s1);
         }
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(s0, s1);
+        if constexpr (MODE == kOut) {
+            f32x4 acc = accO[sl];
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) acc = mfma_bf16(f.a[kb], vfr[kb], acc);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sO[(16 * w + 4 * g4 + e) * kLdO + 16 * sl + n16] = (bf16)acc[e];
+        }
     }
     __syncthreads();
+    if constexpr (MODE == kOut) {
+        // 64 rows x 256 bytes of O, 16 bytes per lane
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
+            if (row < len)
+                *reinterpret_cast<uint4*>(o + ((size_t)(tok0 + row) * H + h) * 128 + c8) =
+                    *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
+        }
+    }
 }
 
 template <int MODE, bool HAS_U, bool DBG>
 __device__ __forceinline__ void run_segment(const uint8_t* __restrict__ recs, int c0, int nch,
-                                            int seg_tok0, int seg_len, f32x4 (&accS)[kNS][2],
-                                            bf16* sS, bf16* sVt, bf16* __restrict__ o,
-                                            float* __restrict__ dbgS, int H, int h, int w, int sg0,
-                                            int lane, int g4, int col0) {
-    ChainFrags F[kDepth];
+                                            int seg_tok0, int seg_len,
+                                            f32x4 (&accS)[ChainCfg<MODE>::NS][2], bf16* sS,
+                                            bf16* sVt, bf16* sO, bf16* __restrict__ o,
+                                            float* __restrict__ dbgS, int H, int h, int w,
+                                            int lane, int n16, int g4, int tid) {
+    constexpr int D = ChainCfg<MODE>::DEPTH;
+    auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
+    ChainFrags<MODE, HAS_U> F[D];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < kDepth - 1; u++)
-            load_chain_frags<MODE, HAS_U>(F[u], recs, c0 + min(u, nch - 1), H, h, w, sg0, lane, g4);
+        for (int u = 0; u < D - 1; u++) load_chain_frags<MODE, HAS_U>(F[u], rec(min(u, nch - 1)), w, lane, g4);
     }
     __syncthreads();
-    const int nfull = nch / kDepth * kDepth;
-    for (int ci = 0; ci < nfull; ci += kDepth) {
+    const int nfull = nch / D * D;
+    for (int ci = 0; ci < nfull; ci += D) {
 #pragma unroll
-        for (int u = 0; u < kDepth; u++) {
+        for (int u = 0; u < D; u++) {
             // unconditional prefetch (index clamped) keeps the wait counts exact
-            const int pf = min(ci + u + kDepth - 1, nch - 1);
-            load_chain_frags<MODE, HAS_U>(F[(u + kDepth - 1) % kDepth], recs, c0 + pf, H, h, w, sg0,
-                                          lane, g4);
+            const int pf = min(ci + u + D - 1, nch - 1);
+            load_chain_frags<MODE, HAS_U>(F[(u + D - 1) % D], rec(pf), w, lane, g4);
             const int t0 = (ci + u) * C;
-            chain_step<MODE, HAS_U, DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS,
-                                         sVt, o, dbgS, H, h, w, lane, g4, col0);
+            chain_step<MODE, HAS_U, DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
+                                  o, dbgS, H, h, w, lane, n16, g4, tid);
         }
     }
 #pragma unroll
-    for (int u = 0; u < kDepth - 1; u++)
+    for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            chain_step<MODE, HAS_U, DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS,
-                                         sS, sVt, o, dbgS, H, h, w, lane, g4, col0);
+            chain_step<MODE, HAS_U, DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt,
+                                  sO, o, dbgS, H, h, w, lane, n16, g4, tid);
         }
 }
 
-// grid: ceil(seg_cap * H / 8) * 8 * G blocks, G = 64-column groups (2 for
-// kOut, 4 for kTrans); blocks 8 apart share an XCD, so the G groups of one
-// (segment, head) read its chunk records through the same L2.
+// kOut grid: seg_cap * H blocks, block = (segment, head), 128 columns.
+// kTrans grid: ceil(seg_cap * H / 8) * 16 blocks, block = (segment, head,
+// half): half 0 carries R (columns 0..127 of [R | M], with U), half 1 carries
+// M (columns 128..255, identity start, U = 0).  The two halves of a
+// (segment, head) are 8 blocks apart, on one XCD, and read the same W and
+// Kbar fragments through its L2.
 template <int MODE, bool DBG>
 __global__ __launch_bounds__(256, 1)
 void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
@@ -604,10 +597,10 @@ void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
                       float* __restrict__ rm, bf16* __restrict__ o, float* __restrict__ hT,
                       float* __restrict__ dbgS)
 {
-    constexpr int G = MODE == kOut ? 2 : 4;
+    constexpr int NS = ChainCfg<MODE>::NS;
     const int id = blockIdx.x;
-    const int p = (id / (8 * G)) * 8 + (id & 7);
-    const int grp = (id >> 3) % G;
+    const int p = MODE == kOut ? id : (id >> 4) * 8 + (id & 7);
+    const int half = MODE == kOut ? 0 : (id >> 3) & 1;
     const int seg_id = p / H, h = p % H;
     if (seg_id >= hdr[1]) return;
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
@@ -619,28 +612,28 @@ void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int col0 = 64 * grp + n16;       // column of slice 0 (0..255 in [R | M])
 
-    __shared__ __align__(16) bf16 sS[kNS * 4 * 64 * 8];
-    __shared__ __align__(16) bf16 sVt[kNS * 4 * 64 * 4];
+    __shared__ __align__(16) bf16 sS[NS * 4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[NS * 4 * 64 * 4];
+    __shared__ __align__(16) bf16 sO[MODE == kOut ? 64 * kLdO : 8];
 
-    f32x4 accS[kNS][2];
+    f32x4 accS[NS][2];
     const float* st = sstart + ((size_t)seg_id * H + h) * 128 * 128;
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++)
+    for (int sl = 0; sl < NS; sl++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int row = 32 * w + 16 * b + 4 * g4 + e;
-                const int col = col0 + 16 * sl;
+                const int col = 16 * sl + n16;
                 float x;
                 if (MODE == kOut) x = st[row * 128 + col];
-                else x = (grp >= 2 && row == col - 128) ? 1.f : 0.f;
+                else x = (half == 1 && row == col) ? 1.f : 0.f;
                 accS[sl][b][e] = x;
             }
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++)
+    for (int sl = 0; sl < NS; sl++)
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(accS[sl][0], accS[sl][1]);
 
     int seg_tok0 = 0, seg_len = 0;
@@ -649,24 +642,23 @@ void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
         seg_tok0 = first.y;
         seg_len = lastc.y + lastc.z - first.y;
     }
-    const int sg0 = (grp & 1) * kNS;       // first 16-column slice of U/Y (R part and outputs)
-    if (MODE == kOut || grp < 2)
-        run_segment<MODE, true, DBG>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, o, dbgS, H, h,
-                                     w, sg0, lane, g4, col0);
-    else
-        run_segment<MODE, false, false>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, o, dbgS,
-                                        H, h, w, sg0, lane, g4, col0);
+    if (MODE == kOut || half == 0)
+        run_segment<MODE, true, DBG>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, sO, o, dbgS,
+                                     H, h, w, lane, n16, g4, tid);
+    else if constexpr (MODE == kTrans)
+        run_segment<MODE, false, false>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, sO, o,
+                                        dbgS, H, h, w, lane, n16, g4, tid);
 
 #pragma unroll
-    for (int sl = 0; sl < kNS; sl++)
+    for (int sl = 0; sl < NS; sl++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int row = 32 * w + 16 * b + 4 * g4 + e;
-                const int col = col0 + 16 * sl;
+                const int col = 16 * sl + n16;
                 if (MODE == kTrans)
-                    rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = accS[sl][b][e];
+                    rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + 128 * half + col] = accS[sl][b][e];
                 else if (last && hT)
                     hT[(((size_t)n * H + h) * 128 + row) * 128 + col] = accS[sl][b][e];
             }
@@ -781,8 +773,8 @@ hipError_t launch_fast(const ChunkArgs& a) {
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
 
     const long long pairs = (long long)a.L.seg_cap * a.H;
-    const unsigned blk8 = (unsigned)((pairs + 7) / 8);
-    hipLaunchKernelGGL((seg_chain_kernel<kTrans, false>), dim3(blk8 * 8 * 4), dim3(256), 0, a.stream,
+    const dim3 gc((unsigned)pairs), gt((unsigned)((pairs + 7) / 8 * 16));
+    hipLaunchKernelGGL((seg_chain_kernel<kTrans, false>), gt, dim3(256), 0, a.stream,
                        (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
                        rm, (bf16*)nullptr, (float*)nullptr, (float*)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -793,11 +785,11 @@ hipError_t launch_fast(const ChunkArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     if (a.dbg_state)
-        hipLaunchKernelGGL((seg_chain_kernel<kOut, true>), dim3(blk8 * 8 * 2), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((seg_chain_kernel<kOut, true>), gc, dim3(256), 0, a.stream,
                            (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
                            rm, (bf16*)a.o, a.hT, a.dbg_state);
     else
-        hipLaunchKernelGGL((seg_chain_kernel<kOut, false>), dim3(blk8 * 8 * 2), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((seg_chain_kernel<kOut, false>), gc, dim3(256), 0, a.stream,
                            (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
                            rm, (bf16*)a.o, a.hT, (float*)nullptr);
     return hipGetLastError();

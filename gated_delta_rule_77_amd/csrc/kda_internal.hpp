@@ -42,26 +42,25 @@ inline size_t generic_rec_floats(int dk, int dv, int C) {
 // bytes, see kda_chunk_fast.hip for the fragment orders
 namespace fast {
 constexpr int C = 64, DK = 128, DV = 128;
-constexpr int REC_W = 0;        // -W^T  fragments [4 wave][4 kstep][64 lane][8] bf16
-constexpr int REC_Q = 16384;    // Q'^T  fragments [4 wave][4 kstep][64 lane][8] bf16
-constexpr int REC_K = 32768;    // Kbar^T fragments [4 wave][2 half][2 kstep][64 lane][8] bf16
-constexpr int REC_U = 49152;    // U tiles  [8 slice][4 wave][64 lane][4] bf16
-constexpr int REC_Y = 65536;    // Y tiles  [8 slice][4 wave][64 lane][4] bf16
-constexpr int REC_G = 81920;    // gamma_C [128] fp32
-constexpr int REC_BYTES = 82432;
+constexpr int REC_W = 0;        // -W^T fragments [4 token block][4 kstep][64 lane][8] bf16
+constexpr int REC_Q = 16384;    // (Q . Gamma)^T fragments, same layout
+constexpr int REC_K = 32768;    // Kbar^T fragments [4 row block][2 half][2 kstep][64 lane][8] bf16
+constexpr int REC_U = 49152;    // U tiles [8 slice][4 token block][64 lane][4] bf16
+constexpr int REC_A = 65536;    // A_qk row fragments [4 token block][2 kstep][64 lane][8] bf16
+constexpr int REC_G = 73728;    // gamma_C [128] fp32
+constexpr int REC_BYTES = 74240;
 }  // namespace fast
 
 inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
     return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
 }
 
-// Chunks per segment of the MFMA chain.  The output phase runs one
-// workgroup per (segment, head, 64-column group) and one workgroup fits a CU,
-// so the sequence is cut into about 512 / (2 H) segments: two full rounds of
-// 256 CUs on a long single sequence.  At least 16 chunks (1024 tokens) per
-// segment.
+// Chunks per segment of the MFMA chain.  Both chain launches run one
+// workgroup per (segment, head) and one workgroup fills a CU, so a long
+// sequence is cut into about 256 / H segments: one full round of 256 CUs.
+// At least 16 chunks (1024 tokens) per segment.
 inline int pick_seg_chunks(int cap, int H) {
-    long long nseg = 512 / (2LL * H);
+    long long nseg = 256 / (long long)H;
     if (nseg < 1) nseg = 1;
     long long per = (cap + nseg - 1) / nseg;
     if (per < 16) per = 16;
