@@ -61,13 +61,45 @@ __device__ __forceinline__ void load8f(const float* p, float* out) {
 }
 
 // LDS row strides (elements), padded so that 16-byte fragment reads whose
-// rows vary across lanes fall on distinct banks: 272-byte bf16 rows, 528-byte
-// fp32 rows of G, 272-byte rows of the 64x64 fp32 matrices.
-constexpr int kLdK = 136;   // bf16 k tile [64][kLdK]
-constexpr int kLdG = 132;   // fp32 G tile [64][kLdG]
+// rows vary across lanes fall on distinct banks: 528-byte fp32 rows of L and
+// K.F, 272-byte bf16 rows, 272-byte rows of the 64x64 fp32 matrices.
+constexpr int kLdG = 132;   // fp32 [64][kLdG]: L, then K.F in place
+constexpr int kLdK = 136;   // bf16 row operands [64][kLdK]
 constexpr int kLdA = 68;    // fp32 64x64 matrices [64][kLdA]
-constexpr int kSmemIntra = 56576;
+// per-channel factor rows (fp32 [128] each); L_s(r) = L at row 16r - 1
+// (0 for r = 0), L_e(r) = L at row 16r + 15, L_C = L at row 63:
+constexpr int kFX = 0;      // X(r,s) = 2^(L_s(r) - L_e(s)), row r(r+1)/2 + s, s <= r
+constexpr int kFY = 10;     // Y(r) = 2^L_s(r)
+constexpr int kFZ = 14;     // Z(r) = 2^(L_C - L_e(r))
+constexpr int kFL = 18;     // L_e(r) itself
+constexpr int kNFac = 22;
+constexpr int kOffRK = 64 * kLdG * 4;
+constexpr int kOffRQ = kOffRK + 64 * kLdK * 2;
+constexpr int kOffFac = kOffRQ + 64 * kLdK * 2;
+constexpr int kOffBeta = kOffFac + kNFac * 128 * 4;
+constexpr int kSmemIntra = kOffBeta + 64 * 4;            // 80128 bytes: two workgroups per CU
+static_assert(3 * 64 * kLdA * 4 + 4 * 256 * 4 <= kOffFac, "A_kk, A_qk, N and P alias L/K.F and the row operands");
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16x16 tile pairs (r, s), s <= r, numbered p = r(r+1)/2 + s; wave w takes
+// p in [pair_beg(w), pair_beg(w + 1)): 3, 3, 2 and 2 tiles.
+__device__ __forceinline__ int pair_beg(int w) { return w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : w == 3 ? 8 : 10; }
+__device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
+
+// One workgroup per (chunk, head), 4 waves.  Work on single elements is split
+// by channel: wave w owns channels [32w, 32w + 32) of all 64 tokens, lane
+// (n, g) token rows 16t + n (t = 0..3) and channels 32w + 8g .. 32w + 8g + 7,
+// which is the MFMA operand layout of k-step w.  Decay factors are powers of
+// two of L = G log2(e): per element E = 2^(L - L_s(r)) <= 1 (row factor) and
+// F = 2^(L_e(r) - L) <= 1 (column factor) for its 16-token block r; every
+// other exponent is a per-channel factor of the table above, so
+//   A_kk/A_qk tile (r, s):  rows (k|q) . E  with  columns (k . F) . X(r,s)
+//   K . Gamma = (k . E) . Y(r),  Q . Gamma = (q . E) . Y(r),  Kbar = (k . F) . Z(r)
+// (X(r,s) <= 1 off the diagonal, X(r,r) = 2^(L_s - L_e) < e^80 on it).
 template <bool DBG>
 __global__ __launch_bounds__(256, 2)
 void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -88,211 +120,223 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     __shared__ __align__(16) uint8_t smem[kSmemIntra];
     float* sG = reinterpret_cast<float*>(smem);                       // [64][kLdG]
-    bf16* sK = reinterpret_cast<bf16*>(smem + 64 * kLdG * 4);         // [64][kLdK]
+    bf16* sRK = reinterpret_cast<bf16*>(smem + kOffRK);               // [64][kLdK]
+    bf16* sRQ = reinterpret_cast<bf16*>(smem + kOffRQ);               // [64][kLdK]
+    float* sFac = reinterpret_cast<float*>(smem + kOffFac);           // [kNFac][128]
+    float* sBeta = reinterpret_cast<float*>(smem + kOffBeta);         // [64]
 
-    const size_t tstride = (size_t)H * 128;   // elements between consecutive tokens
-    const size_t hoff = (size_t)h * 128;
-    auto tok = [&](int row) { return (size_t)(tok0 + row) * tstride + hoff; };
-    const uint4 zero16 = make_uint4(0, 0, 0, 0);
+    // rows past the end of the sequence read the last valid row: they only
+    // meet rows and columns that beta = 0 and g = 0 switch off
+    const unsigned tstride = (unsigned)H * 128u;
+    const size_t base = (size_t)tok0 * tstride + (size_t)h * 128;
+    const int lastrow = len - 1;
+    auto roff = [&](int row) { return (unsigned)min(row, lastrow) * tstride; };
+    const int cw = 32 * w + 8 * g4;
 
-    // ---- 1. loads: k tile to LDS; q and v fragments straight to registers
-    //      (every q/v element is used by exactly one lane); rows past the end
-    //      of the sequence read as zero
+    // ---- 1. loads: q, k, v rows straight to registers (each element used by
+    //      one lane); gate [LA-KDA §5.4] and in-chunk cumulative sum in log2 units
+    uint4 kr[4], qr[4], vr[4];
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const int row = p * 16 + (tid >> 4), c8 = (tid & 15) * 8;
-        const uint4 kk = row < len ? *reinterpret_cast<const uint4*>(k + tok(row) + c8) : zero16;
-        *reinterpret_cast<uint4*>(sK + row * kLdK + c8) = kk;
+    for (int tt = 0; tt < 4; tt++) {
+        const unsigned off = roff(16 * tt + n16) + cw;
+        kr[tt] = *reinterpret_cast<const uint4*>(k + base + off);
+        qr[tt] = *reinterpret_cast<const uint4*>(q + base + off);
+        vr[tt] = *reinterpret_cast<const uint4*>(v + base + off);
     }
-    uint4 qa_raw[4], v_raw[4];       // q rows 16w + n (A operand), v rows 16tt + n (channels 32w + 8g)
-    uint2 qt_raw[2][4];              // q rows 16tb + n, channels 32w + 16cb + 4g (transposed tiles)
+    const int c = tid & 127, half = tid >> 7;
+    float lr[32];
     {
-        const int rq = 16 * w + n16;
+        const float a2 = -expf(A[h]) * kLog2e;     // e^{-e^A z} = 2^(a2 z)
+        const float c5 = kGMin * kLog2e;
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            qa_raw[ks] = rq < len ? *reinterpret_cast<const uint4*>(q + tok(rq) + 32 * ks + 8 * g4) : zero16;
-#pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            const int r = 16 * tt + n16;
-            v_raw[tt] = r < len ? *reinterpret_cast<const uint4*>(v + tok(r) + 32 * w + 8 * g4) : zero16;
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++)
-                qt_raw[cb][tt] = r < len ? *reinterpret_cast<const uint2*>(q + tok(r) + 32 * w + 16 * cb + 4 * g4)
-                                         : make_uint2(0, 0);
-        }
-    }
-    // ---- gate [LA-KDA §5.4] and in-chunk cumulative sum; padding rows: g = 0
-    {
-        const float ea = expf(A[h]);
-        const int c = tid & 127, half = tid >> 7;
-        float zr[32];
-#pragma unroll
-        for (int i = 0; i < 32; i++) {
-            const int row = half * 32 + i;
-            zr[i] = row < len ? z[tok(row) + c] : 0.f;
-        }
+        for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) {
-            const int row = half * 32 + i;
-            run += row < len ? log_decay<false>(ea, zr[i]) : 0.f;
+            const int row = 32 * half + i;
+            float sg = __builtin_amdgcn_rcpf(1.f + ex2(lr[i] * a2));
+            sg = row < len ? sg : 0.f;
+            run = fmaf(sg, c5, run);
+            lr[i] = run;
             sG[row * kLdG + c] = run;
         }
+        if (tid < 64) {
+            const float x = bl[(size_t)(tok0 + min(tid, lastrow)) * H + h];
+            sBeta[tid] = tid < len ? __builtin_amdgcn_rcpf(1.f + ex2(-x * kLog2e)) : 0.f;
+        }
     }
     __syncthreads();
-    if (tid >= 128) {
-        const int c = tid & 127;
-        const float base = sG[31 * kLdG + c];
-#pragma unroll
-        for (int i = 32; i < 64; i++) sG[i * kLdG + c] += base;
-    }
-    __syncthreads();
-    if (tid < 128) reinterpret_cast<float*>(rec + REC_G)[tid] = __expf(sG[63 * kLdG + tid]);
-    if (DBG)
-        for (int idx = tid; idx < 8192; idx += 256) dbase[idx] = sG[(idx >> 7) * kLdG + (idx & 127)];
-
-    // ---- 2a. A_kk and A_qk: wave w owns row block r = w, column blocks s <= r
-    f32x4 akk[4], aqk[4];
-#pragma unroll
-    for (int s = 0; s < 4; s++) { akk[s] = zero4(); aqk[s] = zero4(); }
+    // second half: add L at row 31; per-channel factors
     {
-        const int r = w;
-        const int i = 16 * r + n16;
+        float* F = sFac + c;
+        if (half == 0) {
+            const float L15 = lr[15], L31 = lr[31];
+            F[(kFX + 0) * 128] = ex2(-L15);
+            F[(kFX + 1) * 128] = 1.f;
+            F[(kFX + 2) * 128] = ex2(L15 - L31);
+            F[(kFX + 3) * 128] = ex2(L31 - L15);
+            F[(kFX + 4) * 128] = 1.f;
+            F[(kFX + 8) * 128] = 1.f;
+            F[(kFY + 0) * 128] = 1.f;
+            F[(kFY + 1) * 128] = ex2(L15);
+            F[(kFY + 2) * 128] = ex2(L31);
+            F[(kFZ + 3) * 128] = 1.f;
+            F[(kFL + 0) * 128] = L15;
+            F[(kFL + 1) * 128] = L31;
+        } else {
+            const float L15 = sG[15 * kLdG + c], L31 = sG[31 * kLdG + c];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const int c0 = 32 * ks + 8 * g4;
-            float bref[8], gi[8];
-            if (r > 0) load8f(sG + (16 * r - 1) * kLdG + c0, bref);
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; e++) bref[e] = 0.f;
+            for (int i = 0; i < 32; i++) {
+                lr[i] += L31;
+                sG[(32 + i) * kLdG + c] = lr[i];
             }
-            load8f(sG + i * kLdG + c0, gi);
-            const bf16x8 qi = __builtin_bit_cast(bf16x8, qa_raw[ks]);
-            const bf16x8 ki = *reinterpret_cast<const bf16x8*>(sK + i * kLdK + c0);
-            bf16x8 fq, fk;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float sc = __expf(gi[e] - bref[e]);
-                fq[e] = (bf16)((float)qi[e] * sc);
-                fk[e] = (bf16)((float)ki[e] * sc);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                if (s <= r) {
-                    const int j = 16 * s + n16;
-                    float gj[8];
-                    load8f(sG + j * kLdG + c0, gj);
-                    const bf16x8 kj = *reinterpret_cast<const bf16x8*>(sK + j * kLdK + c0);
-                    bf16x8 fb;
-#pragma unroll
-                    for (int e = 0; e < 8; e++) fb[e] = (bf16)((float)kj[e] * __expf(bref[e] - gj[e]));
-                    akk[s] = mfma_bf16(fk, fb, akk[s]);
-                    aqk[s] = mfma_bf16(fq, fb, aqk[s]);
-                }
-            }
-        }
-        // causal masks and the beta row scale of A_kk
-        float br[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 16 * r + 4 * g4 + e;
-            br[e] = row < len ? sigmoid_f<false>(bl[(size_t)(tok0 + row) * H + h]) : 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            if (s <= r) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int ii = 4 * g4 + e;
-                    if (s == r) {
-                        if (n16 >= ii) akk[s][e] = 0.f;
-                        if (n16 > ii) aqk[s][e] = 0.f;
-                    }
-                    akk[s][e] *= br[e];
-                }
-            }
+            const float L47 = lr[15], L63 = lr[31];
+            F[(kFX + 5) * 128] = ex2(L31 - L47);
+            F[(kFX + 6) * 128] = ex2(L47 - L15);
+            F[(kFX + 7) * 128] = ex2(L47 - L31);
+            F[(kFX + 9) * 128] = ex2(L47 - L63);
+            F[(kFY + 3) * 128] = ex2(L47);
+            F[(kFZ + 0) * 128] = ex2(L63 - L15);
+            F[(kFZ + 1) * 128] = ex2(L63 - L31);
+            F[(kFZ + 2) * 128] = ex2(L63 - L47);
+            F[(kFL + 2) * 128] = L47;
+            F[(kFL + 3) * 128] = L63;
+            reinterpret_cast<float*>(rec + REC_G)[c] = ex2(L63);
         }
     }
+    __syncthreads();
+    if (DBG) {
+        for (int idx = tid; idx < 8192; idx += 256) dbase[idx] = sG[(idx >> 7) * kLdG + (idx & 127)] * kLn2;
+        __syncthreads();
+    }
 
-    // ---- 2b. token-contiguous operands via an exact selection product ----
-    // MFMA(X rows as A operand, one-hot selector as B) returns X in the C
-    // layout: each lane then holds 4 consecutive tokens of one channel, which
-    // is the operand layout for products that contract over tokens.
+    // ---- 2. per element: row and column factors, the row operands, K.F, and
+    //      token-contiguous copies via an exact selection product: MFMA(X rows,
+    //      one-hot B) returns X in the C layout (4 consecutive tokens of one
+    //      channel per lane), MFMA(one-hot A, X rows) returns X^T in it
     bf16x8 sel[2];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         sel[0][e] = (bf16)((8 * g4 + e == n16) ? 1.f : 0.f);
         sel[1][e] = (bf16)((8 * g4 + e == 16 + n16) ? 1.f : 0.f);
     }
-    bf16x8 kgf[2][2], vf[2][2];     // [kstep][16-channel half] of this wave's 32 channels
-    f32x4 qinit[2][4];              // (Q . Gamma)^T tiles: [half][token block]
-    {
-        const int c0 = 32 * w + 8 * g4;
-        float gc[8];
-        load8f(sG + 63 * kLdG + c0, gc);
-        f32x4 tkg[4][2], tv[4][2], tkb[4][2];
+    bf16x8 kgf[2][2], vf[2][2];     // (K . Gamma)^T, V^T fragments [token kstep][16-channel half]
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            const int row = 16 * tt + n16;
-            float gr[8];
-            load8f(sG + row * kLdG + c0, gr);
-            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(sK + row * kLdK + c0);
-            const bf16x8 vv = __builtin_bit_cast(bf16x8, v_raw[tt]);
-            bf16x8 akg, akb;
+    for (int kb = 0; kb < 2; kb++) {
+        f32x4 tkg[2][2], tkb[2][2], tv[2][2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; t2++) {
+            const int tt = 2 * kb + t2, row = 16 * tt + n16;
+            float L8[8], Ls[8], Le[8], Y8[8], Z8[8];
+            load8f(sG + row * kLdG + cw, L8);
+            if (tt > 0) load8f(sFac + (kFL + tt - 1) * 128 + cw, Ls);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) Ls[e] = 0.f;
+            }
+            load8f(sFac + (kFL + tt) * 128 + cw, Le);
+            load8f(sFac + (kFY + tt) * 128 + cw, Y8);
+            load8f(sFac + (kFZ + tt) * 128 + cw, Z8);
+            const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[tt]);
+            const bf16x8 qq = __builtin_bit_cast(bf16x8, qr[tt]);
+            bf16x8 rk, rq, akg, akb, aq;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float kf = (float)kk[e];
-                akg[e] = (bf16)(kf * __expf(gr[e]));
-                akb[e] = (bf16)(kf * __expf(gc[e] - gr[e]));
+                const float E = ex2(L8[e] - Ls[e]), F = ex2(Le[e] - L8[e]);
+                const float kv = (float)kk[e], qv = (float)qq[e];
+                const float kE = kv * E, qE = qv * E, kF = kv * F;
+                rk[e] = (bf16)kE;
+                rq[e] = (bf16)qE;
+                akg[e] = (bf16)(kE * Y8[e]);
+                aq[e] = (bf16)(qE * Y8[e]);
+                akb[e] = (bf16)(kF * Z8[e]);
+                L8[e] = kF;
             }
+            // K.F over L: each lane rewrites only the elements it read
+            *reinterpret_cast<float4*>(sG + row * kLdG + cw) = make_float4(L8[0], L8[1], L8[2], L8[3]);
+            *reinterpret_cast<float4*>(sG + row * kLdG + cw + 4) = make_float4(L8[4], L8[5], L8[6], L8[7]);
+            *reinterpret_cast<bf16x8*>(sRK + row * kLdK + cw) = rk;
+            *reinterpret_cast<bf16x8*>(sRQ + row * kLdK + cw) = rq;
+            f32x4 qt[2];
 #pragma unroll
             for (int cb = 0; cb < 2; cb++) {
-                tkg[tt][cb] = mfma_bf16(akg, sel[cb], zero4());
-                tv[tt][cb] = mfma_bf16(vv, sel[cb], zero4());
-                tkb[tt][cb] = mfma_bf16(akb, sel[cb], zero4());
+                tkg[t2][cb] = mfma_bf16(akg, sel[cb], zero4());
+                tkb[t2][cb] = mfma_bf16(akb, sel[cb], zero4());
+                tv[t2][cb] = mfma_bf16(__builtin_bit_cast(bf16x8, vr[tt]), sel[cb], zero4());
+                qt[cb] = mfma_bf16(sel[cb], aq, zero4());
             }
+            // (Q . Gamma)^T tiles [channel][token] as the chain's A operand (k-step w)
+            *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tt * 4 + w) * 64 + lane) * 16) = pack_frag(qt[0], qt[1]);
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) {
-                kgf[kb][cb] = pack_frag(tkg[2 * kb][cb], tkg[2 * kb + 1][cb]);
-                vf[kb][cb] = pack_frag(tv[2 * kb][cb], tv[2 * kb + 1][cb]);
-                *reinterpret_cast<bf16x8*>(rec + REC_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16) =
-                    pack_frag(tkb[2 * kb][cb], tkb[2 * kb + 1][cb]);
-            }
-#pragma unroll
-        for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                const int row = 16 * tb + n16, c = 32 * w + 16 * cb + 4 * g4;
-                const bf16x4 qq = __builtin_bit_cast(bf16x4, qt_raw[cb][tb]);
-                const float4 gg = *reinterpret_cast<const float4*>(sG + row * kLdG + c);
-                qinit[cb][tb][0] = (float)qq[0] * __expf(gg.x);
-                qinit[cb][tb][1] = (float)qq[1] * __expf(gg.y);
-                qinit[cb][tb][2] = (float)qq[2] * __expf(gg.z);
-                qinit[cb][tb][3] = (float)qq[3] * __expf(gg.w);
-            }
+        for (int cb = 0; cb < 2; cb++) {
+            kgf[kb][cb] = pack_frag(tkg[0][cb], tkg[1][cb]);
+            vf[kb][cb] = pack_frag(tv[0][cb], tv[1][cb]);
+            *reinterpret_cast<bf16x8*>(rec + REC_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16) =
+                pack_frag(tkb[0][cb], tkb[1][cb]);
+        }
     }
-    __syncthreads();   // the k and G tiles are dead from here
+    __syncthreads();
 
-    // ---- 2c. A_kk, A_qk, beta to LDS ----
+    // ---- 3. A_kk and A_qk tiles [LA-KDA §7.2, §7.3], balanced over the waves
+    const int pb = pair_beg(w), pe = pair_beg(w + 1);
+    f32x4 akk[3], aqk[3];
+#pragma unroll
+    for (int sl = 0; sl < 3; sl++) {
+        akk[sl] = zero4();
+        aqk[sl] = zero4();
+        const int p = pb + sl;
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const int c0 = 32 * ks + 8 * g4;
+                const bf16x8 rk = *reinterpret_cast<const bf16x8*>(sRK + (16 * r + n16) * kLdK + c0);
+                const bf16x8 rq = *reinterpret_cast<const bf16x8*>(sRQ + (16 * r + n16) * kLdK + c0);
+                float kf[8], X8[8];
+                load8f(sG + (16 * s + n16) * kLdG + c0, kf);
+                load8f(sFac + (kFX + p) * 128 + c0, X8);
+                bf16x8 col;
+#pragma unroll
+                for (int e = 0; e < 8; e++) col[e] = (bf16)(kf[e] * X8[e]);
+                akk[sl] = mfma_bf16(rk, col, akk[sl]);
+                aqk[sl] = mfma_bf16(rq, col, aqk[sl]);
+            }
+        }
+    }
+    __syncthreads();   // L/K.F and the row operands are dead from here
+
     float* sAkk = reinterpret_cast<float*>(smem);                     // [64][kLdA]
     float* sAqk = sAkk + 64 * kLdA;
     float* sN = sAqk + 64 * kLdA;
-    float* sBeta = sN + 64 * kLdA;                                    // [64]
-    float* sP = sBeta + 64;                                           // [4][16][16]
+    float* sP = sN + 64 * kLdA;                                       // [4][16][16]
+    // causal masks and the beta row scale of A_kk; tiles above the diagonal are zero
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+    for (int sl = 0; sl < 3; sl++) {
+        const int p = pb + sl;
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 16 * w + 4 * g4 + e, col = 16 * s + n16;
-            sAkk[row * kLdA + col] = akk[s][e];
-            sAqk[row * kLdA + col] = aqk[s][e];
+            for (int e = 0; e < 4; e++) {
+                const int ii = 4 * g4 + e, row = 16 * r + ii, col = 16 * s + n16;
+                float vk = akk[sl][e], vq = aqk[sl][e];
+                if (s == r) {
+                    if (n16 >= ii) vk = 0.f;
+                    if (n16 > ii) vq = 0.f;
+                }
+                sAkk[row * kLdA + col] = vk * sBeta[row];
+                sAqk[row * kLdA + col] = vq;
+            }
         }
+    }
+    for (int idx = tid; idx < 6 * 256; idx += 256) {     // tiles (r, s), s > r
+        const int t = idx >> 8, e = idx & 255;
+        const int r = t < 3 ? 0 : t < 5 ? 1 : 2, s = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
+        const int row = 16 * r + (e >> 4), col = 16 * s + (e & 15);
+        sAkk[row * kLdA + col] = 0.f;
+        sAqk[row * kLdA + col] = 0.f;
+    }
     for (int idx = tid; idx < 4096; idx += 256) sN[(idx >> 6) * kLdA + (idx & 63)] = 0.f;
-    if (tid < 64) sBeta[tid] = tid < len ? sigmoid_f<false>(bl[(size_t)(tok0 + tid) * H + h]) : 0.f;
     __syncthreads();
     if (DBG)
         for (int idx = tid; idx < 4096; idx += 256) {
@@ -300,7 +344,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             dbase[8192 + 4096 + idx] = sAqk[(idx >> 6) * kLdA + (idx & 63)];
         }
 
-    // ---- 3. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
+    // ---- 4. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
     // diagonal blocks: forward substitution, lane = (block, column)
     if (w == 0) {
         const int rb = g4, cc = n16;
@@ -341,7 +385,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int idx = tid; idx < 4096; idx += 256)
             dbase[8192 + 8192 + idx] = sN[(idx >> 6) * kLdA + (idx & 63)] * sBeta[idx & 63];
 
-    // ---- 4. products over tokens (wave w: channels [32w, 32w + 32)) ----
+    // ---- 5. products over tokens (wave w: channels [32w, 32w + 32)) ----
     // k-slot order of every token-contracting fragment: lane group g, slot e
     // holds token 32*kb + 4g + e (e < 4) or 32*kb + 16 + 4g + (e - 4) (e >= 4),
     // matching two stacked C tiles.
@@ -368,9 +412,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
         *reinterpret_cast<bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16) = pack_frag(x0, x1);
     }
-
     // W^T = (K . Gamma)^T T^T: tiles [channel][token], stored negated as the
-    // chain's A operand (wave tb of the chain, k-step w)
+    // chain's A operand (token block tb, k-step w)
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) {
         f32x4 wt0 = zero4(), wt1 = zero4();
@@ -391,11 +434,6 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             for (int kb = 0; kb < 2; kb++) u = mfma_bf16(tf[tb][kb], vf[kb][cb], u);
             *reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(u);
         }
-    // (Q . Gamma)^T: tiles [channel][token] as A operand fragments (k-step w)
-#pragma unroll
-    for (int tb = 0; tb < 4; tb++)
-        *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tb * 4 + w) * 64 + lane) * 16) =
-            pack_frag(qinit[0][tb], qinit[1][tb]);
 }
 
 // ---------------------------------------------------------------------------
