@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the chain kernels scale and convert their
+    # state tiles with VALU ops every chunk, which AGPR accumulators would
+    # turn into register moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden",
 ]
 

@@ -106,9 +106,9 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const float* __restrict__ z,
                        const float* __restrict__ bl, const float* __restrict__ A,
                        const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
-                       uint8_t* __restrict__ recs, float* __restrict__ dbg)
+                       int cap, uint8_t* __restrict__ recs, float* __restrict__ dbg)
 {
-    const int cid = blockIdx.x, h = blockIdx.y;
+    const int cid = blockIdx.x / H, h = blockIdx.x % H;   // heads fastest: whole input rows
     if (cid >= hdr[0]) return;
     const int4 cd = chunks[cid];
     const int tok0 = cd.y, len = cd.z;
@@ -462,8 +462,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 constexpr int kOut = 0, kTrans = 1;
 
 template <int MODE> struct ChainCfg;
-template <> struct ChainCfg<kTrans> { static constexpr int NS = 8, DEPTH = 3; };
-template <> struct ChainCfg<kOut>   { static constexpr int NS = 8,  DEPTH = 3; };
+template <> struct ChainCfg<kTrans> { static constexpr int NS = 8, DEPTH = 3, SB = 4; };
+template <> struct ChainCfg<kOut>   { static constexpr int NS = 8, DEPTH = 3, SB = 4; };
 
 template <int MODE, bool HAS_U>
 struct ChainFrags {
@@ -522,18 +522,19 @@ __device__ __forceinline__ void chain_step(const ChainFrags<MODE, HAS_U>& f, int
                 }
     }
     f32x4 accO[MODE == kOut ? NS : 1];
-    // V~ (and the (Q . Gamma) S part of O), four slices at a time
+    // V~ (and the (Q . Gamma) S part of O), SB slices at a time
+    constexpr int SB = ChainCfg<MODE>::SB;
 #pragma unroll
-    for (int b4 = 0; b4 < NS / 4; b4++) {
-        bf16x8 sf[4][4];
+    for (int bb = 0; bb < NS / SB; bb++) {
+        bf16x8 sf[SB][4];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; s4++)
+        for (int s4 = 0; s4 < SB; s4++)
 #pragma unroll
             for (int ks = 0; ks < 4; ks++)
-                sf[s4][ks] = *reinterpret_cast<const bf16x8*>(sS + (((4 * b4 + s4) * 4 + ks) * 64 + lane) * 8);
+                sf[s4][ks] = *reinterpret_cast<const bf16x8*>(sS + (((SB * bb + s4) * 4 + ks) * 64 + lane) * 8);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; s4++) {
-            const int sl = 4 * b4 + s4;
+        for (int s4 = 0; s4 < SB; s4++) {
+            const int sl = SB * bb + s4;
             f32x4 accV = HAS_U ? unpack4(f.u[sl]) : zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
@@ -631,7 +632,7 @@ template <int MODE, bool DBG>
 __global__ __launch_bounds__(256, 1)
 void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
                       const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
-                      const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
+                      const int* __restrict__ hdr, int H, int cap, const float* __restrict__ sstart,
                       float* __restrict__ rm, bf16* __restrict__ o, float* __restrict__ hT,
                       float* __restrict__ dbgS)
 {
@@ -700,6 +701,135 @@ void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
                 else if (last && hT)
                     hT[(((size_t)n * H + h) * 128 + row) * 128 + col] = accS[sl][b][e];
             }
+}
+
+// Transition launch: one workgroup of 8 waves per (segment, head) carries the
+// whole augmented state [R | M], 256 columns = 16 slices (R in slices 0..7,
+// M in 8..15), so each chunk's fixed cost (two barriers, LDS round trips)
+// is paid once for all columns; two waves per SIMD hide each other's MFMA
+// and LDS latencies.
+//   V~ phase:    wave (tb = w & 3, q = w >> 2) forms V~ rows [16tb, 16tb + 16)
+//                of R slices [4q, 4q + 4) and M slices [8 + 4q, 12 + 4q)
+//   state phase: wave w owns state rows [16w, 16w + 16) of all 16 slices (one
+//                C tile per slice), the half k-step fragment (w >> 1, w & 1)
+//                of the bf16 copy of S
+constexpr int kTS = 16;     // slices of [R | M]
+
+struct TransFrags {
+    bf16x8 w[4];      // -W^T, token block w & 3, k-steps 0..3
+    bf16x8 k[2];      // Kbar^T rows [16w, 16w + 16), token k-steps 0..1
+    bf16x4 u[4];      // U tiles of R slices 4q .. 4q + 3, token block w & 3
+    float4 g;         // gamma_C of rows 16w + 4g .. 16w + 4g + 3
+};
+
+__device__ __forceinline__ void load_trans_frags(TransFrags& f, const uint8_t* __restrict__ rec,
+                                                 int w, int lane, int g4) {
+    const int tb = w & 3, q = w >> 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((tb * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+        f.k[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 2 + kb) * 64 + lane) * 16);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++)
+        f.u[s4] = *reinterpret_cast<const bf16x4*>(rec + REC_U + (((4 * q + s4) * 4 + tb) * 64 + lane) * 8);
+    f.g = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(rec + REC_G) + 16 * w + 4 * g4);
+}
+
+__device__ __forceinline__ void trans_step(const TransFrags& f, f32x4 (&acc)[kTS], bf16* sS,
+                                           bf16* sVt, int w, int lane) {
+    const int tb = w & 3, q = w >> 2;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int sl = j < 4 ? 4 * q + j : 8 + 4 * q + (j - 4);
+        bf16x8 sf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            sf[ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl * 4 + ks) * 64 + lane) * 8);
+        f32x4 v = j < 4 ? unpack4(f.u[j & 3]) : zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) v = mfma_bf16(f.w[ks], sf[ks], v);
+        *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + tb) * 64 + lane) * 4) = pack4(v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < kTS; sl++) {
+        bf16x8 vfr[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+            vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb) * 64 + lane) * 4),
+                               *reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb + 1) * 64 + lane) * 4));
+        f32x4& s = acc[sl];
+        s[0] *= f.g.x; s[1] *= f.g.y; s[2] *= f.g.z; s[3] *= f.g.w;
+        s = mfma_bf16(f.k[0], vfr[0], s);
+        s = mfma_bf16(f.k[1], vfr[1], s);
+        *reinterpret_cast<bf16x4*>(sS + ((sl * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) = pack4(s);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void run_trans(const uint8_t* __restrict__ recs, int c0, int nch, int H,
+                                          int h, f32x4 (&acc)[kTS], bf16* sS, bf16* sVt, int w,
+                                          int lane, int g4) {
+    constexpr int D = 3;
+    auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
+    TransFrags F[D];
+    if (nch > 0) {
+#pragma unroll
+        for (int u = 0; u < D - 1; u++) load_trans_frags(F[u], rec(min(u, nch - 1)), w, lane, g4);
+    }
+    __syncthreads();
+    const int nfull = nch / D * D;
+    for (int ci = 0; ci < nfull; ci += D) {
+#pragma unroll
+        for (int u = 0; u < D; u++) {
+            // unconditional prefetch (index clamped) keeps the wait counts exact
+            load_trans_frags(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
+            trans_step(F[u], acc, sS, sVt, w, lane);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; u++)
+        if (nfull + u < nch) trans_step(F[u], acc, sS, sVt, w, lane);
+}
+
+// grid: seg_cap * H blocks, block = (segment, head)
+__global__ __launch_bounds__(512, 1)
+void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
+                      const int2* __restrict__ seqsegs, const int* __restrict__ hdr, int H,
+                      float* __restrict__ rm)
+{
+    const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
+    if (seg_id >= hdr[1]) return;
+    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
+    const int2 ss = seqsegs[sg.x];
+    if (sg.w == ss.y - 1) return;          // the last segment's transition is never needed
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+
+    __shared__ __align__(16) bf16 sS[kTS * 4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[kTS * 4 * 64 * 4];
+
+    f32x4 acc[kTS];     // R from 0, M from the identity
+#pragma unroll
+    for (int sl = 0; sl < kTS; sl++) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 16 * w + 4 * g4 + e, col = 16 * sl + n16;
+            acc[sl][e] = (row == col - 128) ? 1.f : 0.f;
+        }
+        *reinterpret_cast<bf16x4*>(sS + ((sl * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) = pack4(acc[sl]);
+    }
+    run_trans(recs, sg.y, sg.z, H, h, acc, sS, sVt, w, lane, g4);
+#pragma unroll
+    for (int sl = 0; sl < kTS; sl++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = 16 * w + 4 * g4 + e, col = 16 * sl + n16;
+            rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = acc[sl][e];
+        }
 }
 
 // Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and
@@ -797,24 +927,23 @@ hipError_t launch_fast(const ChunkArgs& a) {
     uint8_t* recs = a.ws + a.L.off_recs;
     float* sstart = reinterpret_cast<float*>(a.ws + a.L.off_sstart);
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
-    const dim3 gi((unsigned)a.L.cap, (unsigned)a.H);
+    const dim3 gi((unsigned)((long long)a.L.cap * a.H));
     if (a.dbg_intra)
         hipLaunchKernelGGL(fast_intra_kernel<true>, gi, dim3(256), 0, a.stream,
                            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, recs, a.dbg_intra);
+                           hdr, chunks, a.H, a.L.cap, recs, a.dbg_intra);
     else
         hipLaunchKernelGGL(fast_intra_kernel<false>, gi, dim3(256), 0, a.stream,
                            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, recs, (float*)nullptr);
+                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
 
     const long long pairs = (long long)a.L.seg_cap * a.H;
-    const dim3 gc((unsigned)pairs), gt((unsigned)((pairs + 7) / 8 * 16));
-    hipLaunchKernelGGL((seg_chain_kernel<kTrans, false>), gt, dim3(256), 0, a.stream,
-                       (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
-                       rm, (bf16*)nullptr, (float*)nullptr, (float*)nullptr);
+    const dim3 gc((unsigned)pairs);
+    hipLaunchKernelGGL(seg_trans_kernel, gc, dim3(512), 0, a.stream, (const uint8_t*)recs, segs,
+                       seqsegs, hdr, a.H, rm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
     const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
@@ -824,11 +953,11 @@ hipError_t launch_fast(const ChunkArgs& a) {
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     if (a.dbg_state)
         hipLaunchKernelGGL((seg_chain_kernel<kOut, true>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, a.L.cap, (const float*)sstart,
                            rm, (bf16*)a.o, a.hT, a.dbg_state);
     else
         hipLaunchKernelGGL((seg_chain_kernel<kOut, false>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, a.L.cap, (const float*)sstart,
                            rm, (bf16*)a.o, a.hT, (float*)nullptr);
     return hipGetLastError();
 }
