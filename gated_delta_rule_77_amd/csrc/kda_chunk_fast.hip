@@ -443,76 +443,63 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // with R the state reached from zero and M the product of the per-chunk
 // transitions (the context-parallel composition of [LA-KDA §7.5], here
 // across the CUs of one GPU).  Three launches:
-//   mode kTrans  every segment but a sequence's last runs the chain on the
-//                augmented state [R | M] (R from 0 with the real U, M from I
-//                with U = 0): 256 columns;
-//   compose      per (sequence, head, 16 columns): S_start(j+1) = M_j S_start(j) + R_j
-//                in fp32, sequentially over the (few) segments;
-//   mode kOut    every segment re-runs from S_start with outputs; the
-//                sequence's last segment writes the final state.
+//   transition  every segment but a sequence's last runs the chain on the
+//               augmented state [R | M] (R from 0 with the real U, M from I
+//               with U = 0): 256 columns;
+//   compose     per (sequence, head, 16 columns): S_start(j+1) = M_j S_start(j) + R_j
+//               in fp32, sequentially over the (few) segments;
+//   output      every segment re-runs from S_start with outputs; the
+//               sequence's last segment writes the final state.
+// Per chunk, with S the state entering it:
+//   V~ = U - W S,  O = (Q . Gamma) S + A_qk V~,  S <- Diag(gamma_C) S + Kbar^T V~
+// (B operands: a bf16 copy of S and V~ gathered in LDS; A operands straight
+// from the chunk record).
 //
-// Workgroup = (segment, head[, half]), 4 waves, 128 columns: each record
-// byte is read once per workgroup.  Wave w computes V~ and O rows [16w, 16w + 16) and
-// owns state rows [32w, 32w + 32) as NS pairs of fp32 C tiles (one pair per
-// 16-column slice).  Per chunk:
-//   V~ = U - W S,  O = (Q . Gamma) S + A_qk V~   (B operands: bf16 copy of S
-//                                                  and V~ gathered in LDS)
-//   S <- Diag(gamma_C) S + Kbar^T V~
-// The bf16 copy of wave w's tiles is exactly the B fragment of k-step w.
-constexpr int kOut = 0, kTrans = 1;
+// Output launch: workgroup = (segment, head), 4 waves, all 128 columns, so
+// each record byte is read once.  Wave w computes V~ and O rows
+// [16w, 16w + 16) and owns state rows [32w, 32w + 32) as 8 pairs of fp32 C
+// tiles (one pair per 16-column slice).  The bf16 copy of wave w's tiles is
+// exactly the B fragment of k-step w.
+constexpr int kOutNS = 8;       // 16-column slices
+constexpr int kOutDepth = 3;    // record prefetch ring depth (chunks)
+constexpr int kLdO = 136;       // bf16 output staging rows [64][kLdO]
 
-template <int MODE> struct ChainCfg;
-template <> struct ChainCfg<kTrans> { static constexpr int NS = 8, DEPTH = 3, SB = 4; };
-template <> struct ChainCfg<kOut>   { static constexpr int NS = 8, DEPTH = 3, SB = 4; };
-
-template <int MODE, bool HAS_U>
-struct ChainFrags {
-    bf16x8 w[4], k[4];                      // -W^T (k-steps 0..3); Kbar^T [half][kstep]
-    bf16x8 q[MODE == kOut ? 4 : 1];         // (Q . Gamma)^T (k-steps 0..3)
-    bf16x8 a[MODE == kOut ? 2 : 1];         // A_qk rows (k-steps 0..1)
-    bf16x4 u[HAS_U ? 8 : 1];                // U tiles of the 8 slices
-    float4 g0, g1;                          // gamma_C for the wave's two row tiles
+struct OutFrags {
+    bf16x8 w[4], q[4];          // -W^T, (Q . Gamma)^T of token block w, k-steps 0..3
+    bf16x8 k[4];                // Kbar^T rows [32w, 32w + 32): [16-row half][token kstep]
+    bf16x8 a[2];                // A_qk rows of token block w, token k-steps 0..1
+    bf16x4 u[kOutNS];           // U tiles of token block w
+    float4 g0, g1;              // gamma_C for the wave's two row tiles
 };
 
-template <int MODE, bool HAS_U>
-__device__ __forceinline__ void load_chain_frags(ChainFrags<MODE, HAS_U>& f,
-                                                 const uint8_t* __restrict__ rec, int w, int lane,
-                                                 int g4) {
+__device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __restrict__ rec, int w,
+                                               int lane, int g4) {
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
         f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
         f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 4 + ks) * 64 + lane) * 16);
-        if constexpr (MODE == kOut)
-            f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
+        f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
     }
-    if constexpr (MODE == kOut) {
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-            f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16);
-    }
-    if constexpr (HAS_U) {
+    for (int kb = 0; kb < 2; kb++)
+        f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16);
 #pragma unroll
-        for (int sl = 0; sl < 8; sl++)
-            f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sl * 4 + w) * 64 + lane) * 8);
-    }
+    for (int sl = 0; sl < kOutNS; sl++)
+        f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sl * 4 + w) * 64 + lane) * 8);
     const float* gC = reinterpret_cast<const float*>(rec + REC_G);
     f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
 }
 
-constexpr int kLdO = 136;   // bf16 output staging rows [64][kLdO]
-
-// One chunk for one wave over all NS slices.
-template <int MODE, bool HAS_U, bool DBG>
-__device__ __forceinline__ void chain_step(const ChainFrags<MODE, HAS_U>& f, int cid, int tok0, int len,
-                                           f32x4 (&accS)[ChainCfg<MODE>::NS][2], bf16* sS,
-                                           bf16* sVt, bf16* sO, bf16* __restrict__ o,
-                                           float* __restrict__ dbgS, int H, int h, int w,
-                                           int lane, int n16, int g4, int tid) {
-    constexpr int NS = ChainCfg<MODE>::NS;
+// One chunk for one wave over all slices.
+template <bool DBG>
+__device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, int len,
+                                         f32x4 (&accS)[kOutNS][2], bf16* sS, bf16* sVt, bf16* sO,
+                                         bf16* __restrict__ o, float* __restrict__ dbgS, int H,
+                                         int h, int w, int lane, int n16, int g4, int tid) {
     if (DBG) {
 #pragma unroll
-        for (int sl = 0; sl < NS; sl++)
+        for (int sl = 0; sl < kOutNS; sl++)
 #pragma unroll
             for (int b = 0; b < 2; b++)
 #pragma unroll
@@ -521,35 +508,33 @@ __device__ __forceinline__ void chain_step(const ChainFrags<MODE, HAS_U>& f, int
                     dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * sl + n16] = accS[sl][b][e];
                 }
     }
-    f32x4 accO[MODE == kOut ? NS : 1];
-    // V~ (and the (Q . Gamma) S part of O), SB slices at a time
-    constexpr int SB = ChainCfg<MODE>::SB;
+    f32x4 accO[kOutNS];
+    // V~ and the (Q . Gamma) S part of O, four slices at a time
 #pragma unroll
-    for (int bb = 0; bb < NS / SB; bb++) {
-        bf16x8 sf[SB][4];
+    for (int bb = 0; bb < kOutNS / 4; bb++) {
+        bf16x8 sf[4][4];
 #pragma unroll
-        for (int s4 = 0; s4 < SB; s4++)
+        for (int s4 = 0; s4 < 4; s4++)
 #pragma unroll
             for (int ks = 0; ks < 4; ks++)
-                sf[s4][ks] = *reinterpret_cast<const bf16x8*>(sS + (((SB * bb + s4) * 4 + ks) * 64 + lane) * 8);
+                sf[s4][ks] = *reinterpret_cast<const bf16x8*>(sS + (((4 * bb + s4) * 4 + ks) * 64 + lane) * 8);
 #pragma unroll
-        for (int s4 = 0; s4 < SB; s4++) {
-            const int sl = SB * bb + s4;
-            f32x4 accV = HAS_U ? unpack4(f.u[sl]) : zero4();
+        for (int s4 = 0; s4 < 4; s4++) {
+            const int sl = 4 * bb + s4;
+            f32x4 accV = unpack4(f.u[sl]);
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
-            *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
-            if constexpr (MODE == kOut) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) acc = mfma_bf16(f.q[ks], sf[s4][ks], acc);
-                accO[sl] = acc;
+            for (int ks = 0; ks < 4; ks++) {
+                accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
+                acc = mfma_bf16(f.q[ks], sf[s4][ks], acc);
             }
+            *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
+            accO[sl] = acc;
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int sl = 0; sl < NS; sl++) {
+    for (int sl = 0; sl < kOutNS; sl++) {
         bf16x8 vfr[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -559,46 +544,74 @@ __device__ __forceinline__ void chain_step(const ChainFrags<MODE, HAS_U>& f, int
         f32x4& s1 = accS[sl][1];
         s0[0] *= f.g0.x; s0[1] *= f.g0.y; s0[2] *= f.g0.z; s0[3] *= f.g0.w;
         s1[0] *= f.g1.x; s1[1] *= f.g1.y; s1[2] *= f.g1.z; s1[3] *= f.g1.w;
+        f32x4 acc = accO[sl];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             s0 = mfma_bf16(f.k[kb], vfr[kb], s0);
             s1 = mfma_bf16(f.k[2 + kb], vfr[kb], s1);
+            acc = mfma_bf16(f.a[kb], vfr[kb], acc);
         }
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(s0, s1);
-        if constexpr (MODE == kOut) {
-            f32x4 acc = accO[sl];
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) acc = mfma_bf16(f.a[kb], vfr[kb], acc);
-#pragma unroll
-            for (int e = 0; e < 4; e++) sO[(16 * w + 4 * g4 + e) * kLdO + 16 * sl + n16] = (bf16)acc[e];
-        }
+        for (int e = 0; e < 4; e++) sO[(16 * w + 4 * g4 + e) * kLdO + 16 * sl + n16] = (bf16)acc[e];
     }
     __syncthreads();
-    if constexpr (MODE == kOut) {
-        // 64 rows x 256 bytes of O, 16 bytes per lane
+    // 64 rows x 256 bytes of O, 16 bytes per lane
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-            if (row < len)
-                *reinterpret_cast<uint4*>(o + ((size_t)(tok0 + row) * H + h) * 128 + c8) =
-                    *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
-        }
+    for (int i = 0; i < 4; i++) {
+        const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
+        if (row < len)
+            *reinterpret_cast<uint4*>(o + ((size_t)(tok0 + row) * H + h) * 128 + c8) =
+                *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
     }
 }
 
-template <int MODE, bool HAS_U, bool DBG>
-__device__ __forceinline__ void run_segment(const uint8_t* __restrict__ recs, int c0, int nch,
-                                            int seg_tok0, int seg_len,
-                                            f32x4 (&accS)[ChainCfg<MODE>::NS][2], bf16* sS,
-                                            bf16* sVt, bf16* sO, bf16* __restrict__ o,
-                                            float* __restrict__ dbgS, int H, int h, int w,
-                                            int lane, int n16, int g4, int tid) {
-    constexpr int D = ChainCfg<MODE>::DEPTH;
+// grid: seg_cap * H blocks, block = (segment, head)
+template <bool DBG>
+__global__ __launch_bounds__(256, 1)
+void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
+                    const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
+                    const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
+                    bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS)
+{
+    const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
+    if (seg_id >= hdr[1]) return;
+    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
+    const int n = sg.x, c0 = sg.y, nch = sg.z;
+    const bool last = sg.w == seqsegs[n].y - 1;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+
+    __shared__ __align__(16) bf16 sS[kOutNS * 4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[kOutNS * 4 * 64 * 4];
+    __shared__ __align__(16) bf16 sO[64 * kLdO];
+
+    f32x4 accS[kOutNS][2];
+    const float* st = sstart + ((size_t)seg_id * H + h) * 128 * 128;
+#pragma unroll
+    for (int sl = 0; sl < kOutNS; sl++) {
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                accS[sl][b][e] = st[(32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * sl + n16];
+        *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(accS[sl][0], accS[sl][1]);
+    }
+    int seg_tok0 = 0, seg_len = 0;
+    if (nch > 0) {
+        const int4 first = chunks[c0], lastc = chunks[c0 + nch - 1];
+        seg_tok0 = first.y;
+        seg_len = lastc.y + lastc.z - first.y;
+    }
+
+    constexpr int D = kOutDepth;
     auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
-    ChainFrags<MODE, HAS_U> F[D];
+    OutFrags F[D];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < D - 1; u++) load_chain_frags<MODE, HAS_U>(F[u], rec(min(u, nch - 1)), w, lane, g4);
+        for (int u = 0; u < D - 1; u++) load_out_frags(F[u], rec(min(u, nch - 1)), w, lane, g4);
     }
     __syncthreads();
     const int nfull = nch / D * D;
@@ -606,101 +619,30 @@ __device__ __forceinline__ void run_segment(const uint8_t* __restrict__ recs, in
 #pragma unroll
         for (int u = 0; u < D; u++) {
             // unconditional prefetch (index clamped) keeps the wait counts exact
-            const int pf = min(ci + u + D - 1, nch - 1);
-            load_chain_frags<MODE, HAS_U>(F[(u + D - 1) % D], rec(pf), w, lane, g4);
+            load_out_frags(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
             const int t0 = (ci + u) * C;
-            chain_step<MODE, HAS_U, DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
-                                  o, dbgS, H, h, w, lane, n16, g4, tid);
+            out_step<DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o, dbgS,
+                          H, h, w, lane, n16, g4, tid);
         }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            chain_step<MODE, HAS_U, DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt,
-                                  sO, o, dbgS, H, h, w, lane, n16, g4, tid);
+            out_step<DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
+                          dbgS, H, h, w, lane, n16, g4, tid);
         }
-}
 
-// kOut grid: seg_cap * H blocks, block = (segment, head), 128 columns.
-// kTrans grid: ceil(seg_cap * H / 8) * 16 blocks, block = (segment, head,
-// half): half 0 carries R (columns 0..127 of [R | M], with U), half 1 carries
-// M (columns 128..255, identity start, U = 0).  The two halves of a
-// (segment, head) are 8 blocks apart, on one XCD, and read the same W and
-// Kbar fragments through its L2.
-template <int MODE, bool DBG>
-__global__ __launch_bounds__(256, 1)
-void seg_chain_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
-                      const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
-                      const int* __restrict__ hdr, int H, int cap, const float* __restrict__ sstart,
-                      float* __restrict__ rm, bf16* __restrict__ o, float* __restrict__ hT,
-                      float* __restrict__ dbgS)
-{
-    constexpr int NS = ChainCfg<MODE>::NS;
-    const int id = blockIdx.x;
-    const int p = MODE == kOut ? id : (id >> 4) * 8 + (id & 7);
-    const int half = MODE == kOut ? 0 : (id >> 3) & 1;
-    const int seg_id = p / H, h = p % H;
-    if (seg_id >= hdr[1]) return;
-    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
-    const int n = sg.x, c0 = sg.y, nch = sg.z, jseg = sg.w;
-    const int2 ss = seqsegs[n];
-    const bool last = jseg == ss.y - 1;
-    if (MODE == kTrans && last) return;    // the last segment's transition is never needed
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n16 = lane & 15, g4 = lane >> 4;
-
-    __shared__ __align__(16) bf16 sS[NS * 4 * 64 * 8];
-    __shared__ __align__(16) bf16 sVt[NS * 4 * 64 * 4];
-    __shared__ __align__(16) bf16 sO[MODE == kOut ? 64 * kLdO : 8];
-
-    f32x4 accS[NS][2];
-    const float* st = sstart + ((size_t)seg_id * H + h) * 128 * 128;
+    if (last && hT) {
 #pragma unroll
-    for (int sl = 0; sl < NS; sl++)
+        for (int sl = 0; sl < kOutNS; sl++)
 #pragma unroll
-        for (int b = 0; b < 2; b++)
+            for (int b = 0; b < 2; b++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = 32 * w + 16 * b + 4 * g4 + e;
-                const int col = 16 * sl + n16;
-                float x;
-                if (MODE == kOut) x = st[row * 128 + col];
-                else x = (half == 1 && row == col) ? 1.f : 0.f;
-                accS[sl][b][e] = x;
-            }
-#pragma unroll
-    for (int sl = 0; sl < NS; sl++)
-        *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(accS[sl][0], accS[sl][1]);
-
-    int seg_tok0 = 0, seg_len = 0;
-    if (nch > 0) {
-        const int4 first = chunks[c0], lastc = chunks[c0 + nch - 1];
-        seg_tok0 = first.y;
-        seg_len = lastc.y + lastc.z - first.y;
+                for (int e = 0; e < 4; e++)
+                    hT[(((size_t)n * H + h) * 128 + 32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * sl + n16] =
+                        accS[sl][b][e];
     }
-    if (MODE == kOut || half == 0)
-        run_segment<MODE, true, DBG>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, sO, o, dbgS,
-                                     H, h, w, lane, n16, g4, tid);
-    else if constexpr (MODE == kTrans)
-        run_segment<MODE, false, false>(recs, c0, nch, seg_tok0, seg_len, accS, sS, sVt, sO, o,
-                                        dbgS, H, h, w, lane, n16, g4, tid);
-
-#pragma unroll
-    for (int sl = 0; sl < NS; sl++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = 32 * w + 16 * b + 4 * g4 + e;
-                const int col = 16 * sl + n16;
-                if (MODE == kTrans)
-                    rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + 128 * half + col] = accS[sl][b][e];
-                else if (last && hT)
-                    hT[(((size_t)n * H + h) * 128 + row) * 128 + col] = accS[sl][b][e];
-            }
 }
 
 // Transition launch: one workgroup of 8 waves per (segment, head) carries the
@@ -952,13 +894,13 @@ hipError_t launch_fast(const ChunkArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     if (a.dbg_state)
-        hipLaunchKernelGGL((seg_chain_kernel<kOut, true>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, a.L.cap, (const float*)sstart,
-                           rm, (bf16*)a.o, a.hT, a.dbg_state);
+        hipLaunchKernelGGL(seg_out_kernel<true>, gc, dim3(256), 0, a.stream, (const uint8_t*)recs,
+                           chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, (bf16*)a.o, a.hT,
+                           a.dbg_state);
     else
-        hipLaunchKernelGGL((seg_chain_kernel<kOut, false>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, a.L.cap, (const float*)sstart,
-                           rm, (bf16*)a.o, a.hT, (float*)nullptr);
+        hipLaunchKernelGGL(seg_out_kernel<false>, gc, dim3(256), 0, a.stream, (const uint8_t*)recs,
+                           chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, (bf16*)a.o, a.hT,
+                           (float*)nullptr);
     return hipGetLastError();
 }
 
