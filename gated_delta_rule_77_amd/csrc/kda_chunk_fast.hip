@@ -682,31 +682,53 @@ __device__ __forceinline__ void load_trans_frags(TransFrags& f, const uint8_t* _
 __device__ __forceinline__ void trans_step(const TransFrags& f, f32x4 (&acc)[kTS], bf16* sS,
                                            bf16* sVt, int w, int lane) {
     const int tb = w & 3, q = w >> 2;
+    // two slices at a time, so that two independent MFMA chains interleave
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int sl = j < 4 ? 4 * q + j : 8 + 4 * q + (j - 4);
-        bf16x8 sf[4];
+    for (int jj = 0; jj < 8; jj += 2) {
+        int sl[2];
+        bf16x8 sf[2][4];
+        f32x4 v[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int j = jj + t;
+            sl[t] = j < 4 ? 4 * q + j : 8 + 4 * q + (j - 4);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+                sf[t][ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl[t] * 4 + ks) * 64 + lane) * 8);
+            v[t] = j < 4 ? unpack4(f.u[j & 3]) : zero4();
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
-            sf[ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl * 4 + ks) * 64 + lane) * 8);
-        f32x4 v = j < 4 ? unpack4(f.u[j & 3]) : zero4();
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) v = mfma_bf16(f.w[ks], sf[ks], v);
-        *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + tb) * 64 + lane) * 4) = pack4(v);
+            for (int t = 0; t < 2; t++) v[t] = mfma_bf16(f.w[ks], sf[t][ks], v[t]);
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+            *reinterpret_cast<bf16x4*>(sVt + ((sl[t] * 4 + tb) * 64 + lane) * 4) = pack4(v[t]);
     }
     __syncthreads();
 #pragma unroll
-    for (int sl = 0; sl < kTS; sl++) {
-        bf16x8 vfr[2];
+    for (int s0 = 0; s0 < kTS; s0 += 2) {
+        bf16x8 vfr[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+                vfr[t][kb] = concat44(
+                    *reinterpret_cast<const bf16x4*>(sVt + (((s0 + t) * 4 + 2 * kb) * 64 + lane) * 4),
+                    *reinterpret_cast<const bf16x4*>(sVt + (((s0 + t) * 4 + 2 * kb + 1) * 64 + lane) * 4));
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            f32x4& s = acc[s0 + t];
+            s[0] *= f.g.x; s[1] *= f.g.y; s[2] *= f.g.z; s[3] *= f.g.w;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
-            vfr[kb] = concat44(*reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb) * 64 + lane) * 4),
-                               *reinterpret_cast<const bf16x4*>(sVt + ((sl * 4 + 2 * kb + 1) * 64 + lane) * 4));
-        f32x4& s = acc[sl];
-        s[0] *= f.g.x; s[1] *= f.g.y; s[2] *= f.g.z; s[3] *= f.g.w;
-        s = mfma_bf16(f.k[0], vfr[0], s);
-        s = mfma_bf16(f.k[1], vfr[1], s);
-        *reinterpret_cast<bf16x4*>(sS + ((sl * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) = pack4(s);
+#pragma unroll
+            for (int t = 0; t < 2; t++) acc[s0 + t] = mfma_bf16(f.k[kb], vfr[t][kb], acc[s0 + t]);
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+            *reinterpret_cast<bf16x4*>(sS + (((s0 + t) * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) =
+                pack4(acc[s0 + t]);
     }
     __syncthreads();
 }
