@@ -142,7 +142,7 @@ def bench_prefill(args, kda, torch, KI):
     units = tokens * H
     kernels = {
         "fast_intra_kernel": {"ms": avg["intra"], "alg_bytes": INTRA_BYTES * units},
-        "seg_chain_kernel<out>": {"ms": avg["output"],
+        "seg_out_kernel": {"ms": avg["output"],
                                   "alg_bytes": CHAIN_BYTES * units + 2 * N * H * dk * dv * 4},
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
