@@ -68,18 +68,28 @@ def _elapsed(h, a, b) -> float:
     return float(ms.value)
 
 
+def code_sha1(path: str) -> str:
+    """sha1 of a C++/HIP source with comments and whitespace removed, so that
+    a change to comments alone keeps a counter record valid."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha1(" ".join(text.split()).encode()).hexdigest()
+
+
 def _traffic_for(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/traffic_long_1m.json), or None when the kernel source changed
+    (profiles/traffic_long_1m.json), or None when the kernel code changed
     since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic_long_1m.json")
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        sha = code_sha1(os.path.join(ROOT, rec["source"]))
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha1(src).hexdigest() != rec.get("source_sha1"):
+    if sha != rec.get("source_code_sha1"):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else int(k["hbm_bytes"])

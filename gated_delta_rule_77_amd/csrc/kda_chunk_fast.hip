@@ -12,22 +12,22 @@
 //   T  = (I + A_kk)^{-1} Diag(beta)          (the UT transform)
 //   W  = T (K . Gamma),  U = T V             (the WY pair; no S dependence)
 //   V~ = U - W S
-//   O  = (Q . Gamma) S + A_qk V~  =  Q' S + Y,   Q' = Q . Gamma - A_qk W,  Y = A_qk U
+//   O  = (Q . Gamma) S + A_qk V~
 //   S <- Diag(Gamma_C) S + Kbar^T V~,   Kbar = K . e^{G_C - G}
 // Only the two C x C matrices A_kk and A_qk are formed: the diagonal and the
 // low-rank terms share the same k ([K3-ATTN §2.2]).
 //
-// Two kernels:
-//   intra  one workgroup per (chunk, head), all chunks in parallel: gate,
-//          cumulative decay, A_kk and A_qk on MFMA, the fp32 triangular
-//          inverse, W, U, Q', Y and Kbar on MFMA.  It writes them as bf16
-//          operand fragments already in the order the chain kernel's lanes
-//          load them (one 16-byte load per lane per fragment).
-//   chain  one workgroup per (sequence, head, 16-column slice of the state):
-//          walks the sequence's chunks in order carrying its fp32 state
-//          slice; per chunk it forms V~, the output rows and the new state.
-//          Columns of the state evolve independently (the correction u_j
-//          depends only on column j), so 8 slices run as 8 chains.
+// Launches:
+//   intra       one workgroup per (chunk, head), all chunks in parallel: gate,
+//               cumulative decay, A_kk and A_qk on MFMA, the fp32 triangular
+//               inverse, W, U, Q . Gamma and Kbar on MFMA.  It writes them as
+//               bf16 operand fragments already in the order the chain
+//               kernels' lanes load them.
+//   transition  per (segment, head): the chain over the segment's chunks on
+//               the augmented state [R | M] (see the chain section below);
+//   compose     per (sequence, head): segment start states in fp32;
+//   output      per (segment, head): the chain from the segment's start
+//               state, forming V~, the output rows and the next state.
 //
 // Exponent range: the lower bound g > -5 ([LA-KDA §5.4]) keeps every
 // reciprocal decay factor inside a 16-token sub-tile ([LA-KDA §8]) below
