@@ -203,6 +203,7 @@ def bench_decode(args, kda, torch, KI):
     mean = sum(ms) / len(ms)
     units = run["N"] * run["H"]
     gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
+    fold = bench_fold(args, kda, torch, run, mean)
     return {
         "workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v",
         "steps_timed": len(ms),
@@ -213,6 +214,48 @@ def bench_decode(args, kda, torch, KI):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
                 "algorithmic bytes and may exceed the HBM rate",
+        "fold": fold,
+    }
+
+
+# Replay fold: a window of 7 draft tokens (the pages' num_speculative_tokens),
+# all accepted; per (sequence, head) the fold moves the state once in and out
+# plus each token's k, v (bf16), gate logits (fp32) and beta logit.
+FOLD_WINDOW = 7
+FOLD_TOKEN_BYTES = 2 * 128 + 2 * 128 + 4 * 128 + 4
+
+
+def bench_fold(args, kda, torch, run, step_ms):
+    W = FOLD_WINDOW
+    steps = run["steps"][:W]
+    win = {key: torch.stack([s[key] for s in steps], dim=1).contiguous() for key in ("k", "v", "z", "b")}
+    N, H = run["N"], run["H"]
+    n_acc = torch.full((N,), W, dtype=torch.int32, device=win["k"].device)
+    st = run["state"].clone()
+    A = run["A"]
+    for _ in range(2):
+        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, st)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(4, args.decode_reps * 4)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, st)
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    mean = sum(ms) / len(ms)
+    per_unit = 2 * 128 * 128 * 4 + W * FOLD_TOKEN_BYTES
+    gbs = per_unit * N * H / (mean * 1e-3) / 1e9
+    return {
+        "workload": f"decode_256 states, window of {W} draft tokens per sequence, all accepted",
+        "calls_timed": len(ms),
+        "ms_per_call_mean": round(mean, 4),
+        "tokens_per_s": round(N * W / (mean * 1e-3), 1),
+        "alg_GBps": round(gbs, 1),
+        "vs_token_steps": round(W * step_ms / mean, 2),
     }
 
 
@@ -234,7 +277,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-reps", type=int, default=4, help="passes over the 16 decode steps")
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -242,8 +285,8 @@ def main():
                          "kernel for calibrating the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard across GPUs with no communication; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads shard across GPUs with no communication, one call per GPU). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

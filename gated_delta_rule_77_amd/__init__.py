@@ -9,6 +9,7 @@ Names follow the C ABI in include/kda.h:
     kda_chunk_fwd(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
                   chunk_size=64, output_final_state=True, workspace=None) -> (o, hT)
     kda_recurrent_step(q, k, v, g, beta, A, state) -> o     (state updated in place)
+    kda_recurrent_fold(k, v, g, beta, A, n_accept, state)    (state updated in place)
     kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
 `g` are the raw per-channel gate logits and `beta` the raw write-strength
 logits; both activations run inside the kernels.
@@ -20,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step",
+    "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_fold",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
     "kda_recurrent_step_supported", "EXPORTED_SYMBOLS",
 ]
@@ -32,7 +33,7 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "kda_status_string", "kda_chunk_fwd_supported", "kda_recurrent_step_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_debug_floats",
-    "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step",
+    "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
 )
 
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd_timed.argtypes = chunk_args + [ctypes.POINTER(vp), i, vp]
     L.kda_recurrent_step.restype = i
     L.kda_recurrent_step.argtypes = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, vp]
+    L.kda_recurrent_fold.restype = i
+    L.kda_recurrent_fold.argtypes = [vp, vp, f, f, f, vp, f, i, i, i, i, i, i, vp]
     _lib = L
     return L
 
@@ -254,3 +257,32 @@ def kda_recurrent_step(q, k, v, g, beta, A, state):
                                   _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(dev))
     _check(rc, "kda_recurrent_step")
     return o
+
+
+def kda_recurrent_fold(k, v, g, beta, A, n_accept, state) -> None:
+    """Replay the first n_accept[s] tokens of each sequence's stored window
+    into its state: k [N, W, H, dk], v [N, W, H, dv] (bf16 or fp32), g
+    [N, W, H, dk] fp32, beta [N, W, H] fp32, A [H] fp32, n_accept [N] int32
+    (device), state [N, H, dk, dv] fp32 (updated in place).  Bit-identical to
+    that many kda_recurrent_step calls."""
+    torch = _torch()
+    _req(k, "k")
+    dev, dt = k.device, k.dtype
+    code = _dtype_code(k)
+    _req(v, "v", dt, dev)
+    _req(g, "g", torch.float32, dev)
+    _req(beta, "beta", torch.float32, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(n_accept, "n_accept", torch.int32, dev)
+    _req(state, "state", torch.float32, dev)
+    if k.dim() != 4:
+        raise ValueError("k must be [N, W, H, dk]")
+    N, W, H, dk = k.shape
+    dv = v.shape[-1]
+    if g.shape != k.shape or v.shape != (N, W, H, dv) or beta.shape != (N, W, H):
+        raise ValueError("g must match k [N, W, H, dk], v must be [N, W, H, dv], beta [N, W, H]")
+    if A.shape != (H,) or n_accept.shape != (N,) or state.shape != (N, H, dk, dv):
+        raise ValueError("A [H], n_accept [N] and state [N, H, dk, dv] expected")
+    rc = lib().kda_recurrent_fold(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(n_accept),
+                                  _ptr(state), N, W, H, dk, dv, code, _stream(dev))
+    _check(rc, "kda_recurrent_fold")

@@ -19,6 +19,106 @@
 
 namespace kda {
 
+// One token for one (sequence, head): S (this thread's 16 x 4 block, in
+// registers) advances by one step; with WITH_Q the output o = S^T q is also
+// formed.  Every product that feeds an addition is an explicit fma and no
+// other contraction is allowed, so the arithmetic of a step is fixed by this
+// source: the decode kernel and the replay fold below run the same step and
+// produce the same bits.
+template <int DK, int DV, typename Tin, bool WITH_Q>
+__device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __restrict__ kt,
+                                               const Tin* __restrict__ vt, const float* __restrict__ zt,
+                                               float b_logit, float ea, const Tin* __restrict__ qt,
+                                               Tin* __restrict__ ot, float* s_al, float* s_k,
+                                               float* s_q, float (*s_red)[DK / 16][DV]) {
+#pragma clang fp contract(off)
+    constexpr int CG = DV / 4, RG = DK / 16, NT = CG * RG;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    for (int i = t; i < DK; i += NT) {
+        s_al[i] = expf(log_decay<true>(ea, zt[i]));
+        s_k[i] = to_f32(kt[i]);
+        if (WITH_Q) s_q[i] = to_f32(qt[i]);
+    }
+    const float beta = sigmoid_f<true>(b_logit);
+    float vj[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) vj[c] = to_f32(vt[cg * 4 + c]);
+    __syncthreads();
+
+    // partial S'^T k (and S'^T q) over this thread's 16 rows
+    float p[4] = {0.f, 0.f, 0.f, 0.f}, r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int i = rg * 16 + r;
+        const float ka = s_al[i] * s_k[i];
+        p[0] = __builtin_fmaf(ka, Sv[r].x, p[0]);
+        p[1] = __builtin_fmaf(ka, Sv[r].y, p[1]);
+        p[2] = __builtin_fmaf(ka, Sv[r].z, p[2]);
+        p[3] = __builtin_fmaf(ka, Sv[r].w, p[3]);
+        if (WITH_Q) {
+            const float qa = s_al[i] * s_q[i];
+            r4[0] = __builtin_fmaf(qa, Sv[r].x, r4[0]);
+            r4[1] = __builtin_fmaf(qa, Sv[r].y, r4[1]);
+            r4[2] = __builtin_fmaf(qa, Sv[r].z, r4[2]);
+            r4[3] = __builtin_fmaf(qa, Sv[r].w, r4[3]);
+        }
+    }
+    *reinterpret_cast<float4*>(&s_red[0][rg][cg * 4]) = make_float4(p[0], p[1], p[2], p[3]);
+    if (WITH_Q) *reinterpret_cast<float4*>(&s_red[1][rg][cg * 4]) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+    __syncthreads();
+
+    float P[4] = {0.f, 0.f, 0.f, 0.f}, R[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gidx = 0; gidx < RG; gidx++) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_red[0][gidx][cg * 4]);
+        P[0] += a.x; P[1] += a.y; P[2] += a.z; P[3] += a.w;
+        if (WITH_Q) {
+            const float4 c = *reinterpret_cast<const float4*>(&s_red[1][gidx][cg * 4]);
+            R[0] += c.x; R[1] += c.y; R[2] += c.z; R[3] += c.w;
+        }
+    }
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) u[c] = beta * (vj[c] - P[c]);
+    if (WITH_Q) {
+        float qk = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < DK; i++) qk = __builtin_fmaf(s_q[i], s_k[i], qk);
+        if (rg == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; c++) ot[cg * 4 + c] = from_f32<Tin>(__builtin_fmaf(qk, u[c], R[c]));
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int i = rg * 16 + r;
+        const float al = s_al[i], ki = s_k[i];
+        Sv[r].x = __builtin_fmaf(ki, u[0], al * Sv[r].x);
+        Sv[r].y = __builtin_fmaf(ki, u[1], al * Sv[r].y);
+        Sv[r].z = __builtin_fmaf(ki, u[2], al * Sv[r].z);
+        Sv[r].w = __builtin_fmaf(ki, u[3], al * Sv[r].w);
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void load_state(float4 (&Sv)[16], const float* __restrict__ S) {
+    constexpr int CG = DV / 4;
+    const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        Sv[r] = *reinterpret_cast<const float4*>(S + (size_t)(rg * 16 + r) * DV + cg * 4);
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void store_state(const float4 (&Sv)[16], float* __restrict__ S) {
+    constexpr int CG = DV / 4;
+    const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        *reinterpret_cast<float4*>(S + (size_t)(rg * 16 + r) * DV + cg * 4) = Sv[r];
+}
+
 template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__((DV / 4) * (DK / 16))
 void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
@@ -26,79 +126,49 @@ void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                    const float* __restrict__ bl, const float* __restrict__ A,
                    float* __restrict__ state, Tin* __restrict__ o, int H)
 {
-    constexpr int CG = DV / 4, RG = DK / 16, NT = CG * RG;
     const int nh = blockIdx.x;          // sequence * H + head
-    const int h = nh % H;
-    const int t = threadIdx.x;
-    const int cg = t % CG, rg = t / CG;
     float* S = state + (size_t)nh * DK * DV;
-
     __shared__ float s_al[DK], s_k[DK], s_q[DK];
-    __shared__ __align__(16) float s_red[2][RG][DV];
-
+    __shared__ __align__(16) float s_red[2][DK / 16][DV];
     // the state stream is the cost of this kernel: issue its loads first
     float4 Sv[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-        Sv[r] = *reinterpret_cast<const float4*>(S + (size_t)(rg * 16 + r) * DV + cg * 4);
+    load_state<DK, DV>(Sv, S);
+    const float ea = expf(A[nh % H]);
+    kda_token_step<DK, DV, Tin, true>(Sv, k + (size_t)nh * DK, v + (size_t)nh * DV,
+                                      z + (size_t)nh * DK, bl[nh], ea, q + (size_t)nh * DK,
+                                      o + (size_t)nh * DV, s_al, s_k, s_q, s_red);
+    store_state<DK, DV>(Sv, S);
+}
 
+// Replay fold ([K3-ATTN §6.2], ReplaySSM): advance each (sequence, head)
+// state over the first n_accept[s] tokens of its stored window with exactly
+// the decode step above, keeping the state in registers between tokens: one
+// state read and one write for the whole window instead of one per token.
+// Window layout: k, z [N, W, H, DK]; v [N, W, H, DV]; b [N, W, H].
+template <int DK, int DV, typename Tin>
+__global__ __launch_bounds__((DV / 4) * (DK / 16))
+void fold_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v, const float* __restrict__ z,
+                 const float* __restrict__ bl, const float* __restrict__ A,
+                 const int* __restrict__ n_accept, float* __restrict__ state, int W, int H)
+{
+    const int nh = blockIdx.x;          // sequence * H + head
+    const int n = nh / H, h = nh % H;
+    const int cnt = min(max(n_accept[n], 0), W);
+    if (cnt == 0) return;
+    float* S = state + (size_t)nh * DK * DV;
+    __shared__ float s_al[DK], s_k[DK];
+    __shared__ __align__(16) float s_red[2][DK / 16][DV];
+    float4 Sv[16];
+    load_state<DK, DV>(Sv, S);
     const float ea = expf(A[h]);
-    for (int i = t; i < DK; i += NT) {
-        const size_t off = (size_t)nh * DK + i;
-        s_al[i] = expf(log_decay<true>(ea, z[off]));
-        s_k[i] = to_f32(k[off]);
-        s_q[i] = to_f32(q[off]);
+    for (int t = 0; t < cnt; t++) {
+        const size_t tok = ((size_t)n * W + t) * H + h;
+        if (t > 0) __syncthreads();     // the previous step's readers of s_al, s_k, s_red are done
+        kda_token_step<DK, DV, Tin, false>(Sv, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
+                                           ea, (const Tin*)nullptr, (Tin*)nullptr, s_al, s_k,
+                                           (float*)nullptr, s_red);
     }
-    const float beta = sigmoid_f<true>(bl[nh]);
-    float vj[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) vj[c] = to_f32(v[(size_t)nh * DV + cg * 4 + c]);
-    __syncthreads();
-
-    // partial S'^T k and S'^T q over this thread's 16 rows
-    float p[4] = {0.f, 0.f, 0.f, 0.f}, r4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int i = rg * 16 + r;
-        const float ka = s_al[i] * s_k[i], qa = s_al[i] * s_q[i];
-        p[0] += ka * Sv[r].x; p[1] += ka * Sv[r].y; p[2] += ka * Sv[r].z; p[3] += ka * Sv[r].w;
-        r4[0] += qa * Sv[r].x; r4[1] += qa * Sv[r].y; r4[2] += qa * Sv[r].z; r4[3] += qa * Sv[r].w;
-    }
-    *reinterpret_cast<float4*>(&s_red[0][rg][cg * 4]) = make_float4(p[0], p[1], p[2], p[3]);
-    *reinterpret_cast<float4*>(&s_red[1][rg][cg * 4]) = make_float4(r4[0], r4[1], r4[2], r4[3]);
-    __syncthreads();
-
-    float P[4] = {0.f, 0.f, 0.f, 0.f}, R[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int gidx = 0; gidx < RG; gidx++) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_red[0][gidx][cg * 4]);
-        const float4 c = *reinterpret_cast<const float4*>(&s_red[1][gidx][cg * 4]);
-        P[0] += a.x; P[1] += a.y; P[2] += a.z; P[3] += a.w;
-        R[0] += c.x; R[1] += c.y; R[2] += c.z; R[3] += c.w;
-    }
-    float qk = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < DK; i++) qk += s_q[i] * s_k[i];
-
-    float u[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) u[c] = beta * (vj[c] - P[c]);
-    if (rg == 0) {
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-            o[(size_t)nh * DV + cg * 4 + c] = from_f32<Tin>(R[c] + qk * u[c]);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int i = rg * 16 + r;
-        const float al = s_al[i], ki = s_k[i];
-        float4 n;
-        n.x = al * Sv[r].x + ki * u[0];
-        n.y = al * Sv[r].y + ki * u[1];
-        n.z = al * Sv[r].z + ki * u[2];
-        n.w = al * Sv[r].w + ki * u[3];
-        *reinterpret_cast<float4*>(S + (size_t)i * DV + cg * 4) = n;
-    }
+    store_state<DK, DV>(Sv, S);
 }
 
 bool decode_supported(int dk, int dv) {
@@ -125,6 +195,29 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
         : launch_decode_t<D, float>(q, k, v, z, b, A, state, o, N, H, s);
     KDA_DEC(16) KDA_DEC(32) KDA_DEC(64) KDA_DEC(128)
 #undef KDA_DEC
+    return hipErrorInvalidValue;
+}
+
+template <int D, typename Tin>
+static hipError_t launch_fold_t(const void* k, const void* v, const float* z, const float* b,
+                                const float* A, const int* n_accept, float* state, int N, int W,
+                                int H, hipStream_t s) {
+    constexpr int NT = (D / 4) * (D / 16);
+    hipLaunchKernelGGL((fold_kernel<D, D, Tin>), dim3((unsigned)N * H), dim3(NT), 0, s,
+                       (const Tin*)k, (const Tin*)v, z, b, A, n_accept, state, W, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold(const void* k, const void* v, const float* z, const float* b,
+                       const float* A, const int* n_accept, float* state, int N, int W, int H,
+                       int dk, int dv, int dtype_bf16, hipStream_t s) {
+    (void)dv;
+#define KDA_FOLD(D)                                                                         \
+    if (dk == D) return dtype_bf16                                                          \
+        ? launch_fold_t<D, bf16>(k, v, z, b, A, n_accept, state, N, W, H, s)               \
+        : launch_fold_t<D, float>(k, v, z, b, A, n_accept, state, N, W, H, s);
+    KDA_FOLD(16) KDA_FOLD(32) KDA_FOLD(64) KDA_FOLD(128)
+#undef KDA_FOLD
     return hipErrorInvalidValue;
 }
 

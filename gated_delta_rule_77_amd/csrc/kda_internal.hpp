@@ -119,5 +119,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          const float* b, const float* A, float* state, void* o,
                          int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s);
 bool decode_supported(int dk, int dv);
+hipError_t launch_fold(const void* k, const void* v, const float* z, const float* b,
+                       const float* A, const int* n_accept, float* state, int N, int W, int H,
+                       int dk, int dv, int dtype_bf16, hipStream_t s);
 
 }  // namespace kda

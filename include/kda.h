@@ -197,6 +197,35 @@ KDA_API kda_status_t kda_recurrent_step(const void* q, const void* k, const void
                                 int N, int H, int dk, int dv, kda_dtype_t dtype,
                                 void* stream);
 
+/*
+ * Replay fold for speculative decoding ([K3-ATTN §6.2], ReplaySSM): instead
+ * of a state snapshot per draft token, the caller keeps each window token's
+ * inputs; once the number of accepted tokens is known, this call advances
+ * every (sequence, head) state over the first n_accept[s] tokens of its
+ * window.  Each token is processed by the same step as kda_recurrent_step, so
+ * the result is bit-identical to n_accept[s] kda_recurrent_step calls on the
+ * same state with the same k, v, g_logits, beta_logits and A (q only shapes
+ * the output of those calls, never the state).  The state is read and written
+ * once for the whole window.
+ *
+ *   k            [N, W, H, dk]    dtype  window keys
+ *   v            [N, W, H, dv]    dtype  window values
+ *   g_logits     [N, W, H, dk]    fp32   window gate logits
+ *   beta_logits  [N, W, H]        fp32   window write-strength logits
+ *   A            [H]              fp32
+ *   n_accept     [N]              int32, on the device: tokens to replay per
+ *                                 sequence; values outside [0, W] are clamped
+ *   state        [N, H, dk, dv]   fp32, read and overwritten (untouched where
+ *                                 n_accept[s] <= 0)
+ *
+ * Same supported set as kda_recurrent_step.  N = 0 or W = 0 is a no-op.  No
+ * workspace.
+ */
+KDA_API kda_status_t kda_recurrent_fold(const void* k, const void* v, const float* g_logits,
+                                const float* beta_logits, const float* A,
+                                const int* n_accept, float* state, int N, int W, int H,
+                                int dk, int dv, kda_dtype_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -271,3 +271,23 @@ def decode_step(q, k, v, z, b, A, state):
                       v.reshape(1, N * H, dv), z.reshape(1, N * H, dk),
                       b.reshape(1, N * H), np.tile(A, N), state.reshape(N * H, dk, dv))
     return o.reshape(N, H, dv), S.reshape(N, H, dk, dv)
+
+
+def replay_fold(k, v, z, b, A, state, n_accept):
+    """The replay of [K3-ATTN §6.2] (ReplaySSM): from a checkpoint state,
+    advance sequence s by the first n_accept[s] tokens of its stored window
+    (k, z [N, W, H, d_k]; v [N, W, H, d_v]; b [N, W, H]); counts outside
+    [0, W] are clamped.  The state after a token does not depend on q, so the
+    window carries none.  Returns the new state [N, H, d_k, d_v]; the input is
+    not modified."""
+    k, v, z, b, A, state = map(_f64, (k, v, z, b, A, state))
+    N, W, H, dk = k.shape
+    out = state.copy()
+    for s in range(N):
+        n = min(max(int(n_accept[s]), 0), W)
+        if n == 0:
+            continue
+        # the accepted prefix is a short sequence of its own, started from the checkpoint
+        _, out[s] = recurrence(np.zeros_like(k[s, :n]), k[s, :n], v[s, :n], z[s, :n], b[s, :n], A,
+                               state[s])
+    return out

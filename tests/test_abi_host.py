@@ -125,3 +125,20 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         kda.kda_recurrent_step(x[0], x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(1),
                                torch.zeros(4, 1, 16, 16))
+
+
+def test_recurrent_fold_rejects_bad_arguments(L):
+    fn = L.kda_recurrent_fold
+    fn.restype = ctypes.c_int
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    ok = [FAKE] * 7
+    assert fn(*ok, 4, 7, 2, 96, 96, 1, None) == 2
+    assert fn(*ok, 4, 7, 2, 128, 64, 1, None) == 2
+    assert fn(*ok, -1, 7, 2, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, -1, 2, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, 7, 0, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, 7, 2, 128, 128, 3, None) == 1
+    assert fn(*([FAKE] * 5 + [None, FAKE]), 4, 7, 2, 128, 128, 1, None) == 1   # n_accept missing
+    assert fn(*([None] * 7), 0, 7, 2, 128, 128, 1, None) == 0    # N = 0 is a no-op
+    assert fn(*([None] * 7), 4, 0, 2, 128, 128, 1, None) == 0    # an empty window is a no-op

@@ -425,3 +425,94 @@ def test_in_place_final_state(kda):
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(o1, o2) and torch.equal(h1, st)
+
+
+# ---------------------------------------------------------------- replay fold
+
+def _fold_window(dtype, dk, N, H, W, seed):
+    """A speculative window of W draft tokens per sequence from the seeded
+    decode generator, stacked to [N, W, H, .], plus the checkpoint state."""
+    case = KI.DecodeCase("fold", N=N, H=H, dk=dk, dv=dk, steps=W, dtype=dtype)
+    run = KI.make_decode(case, seed=seed)
+    st = run["steps"]
+    win = {key: torch.stack([s[key] for s in st], dim=1) for key in ("q", "k", "v", "z", "b")}
+    return run, st, win
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("fp32", 16), ("bf16", 64)])
+def test_fold_bit_identical_to_recurrent_steps(kda, dtype, dk):
+    """[K3-ATTN §6.2]: the fold replays the accepted prefix with results
+    bit-identical to the token-by-token recurrent calls.  Counts cover none,
+    part, all, and out-of-range values (clamped)."""
+    N, H, W = 7, 3, 7
+    run, steps, win = _fold_window(dtype, dk, N, H, W, seed=21)
+    n_acc = torch.tensor([0, 1, 3, 7, 5, 9, -2], dtype=torch.int32)
+    A = run["A"].cuda()
+    st0 = run["state"].cuda().contiguous()
+    folded = st0.clone()
+    kda.kda_recurrent_fold(win["k"].cuda().contiguous(), win["v"].cuda().contiguous(),
+                           win["z"].cuda().contiguous(), win["b"].cuda().contiguous(), A,
+                           n_acc.cuda(), folded)
+    # reference: the recurrent call token by token, state snapshotted at each
+    # sequence's count
+    ref = st0.clone()
+    cur = st0.clone()
+    cnt = n_acc.clamp(0, W)
+    for t, s in enumerate(steps):
+        sd = to_dev(s)
+        kda.kda_recurrent_step(sd["q"], sd["k"], sd["v"], sd["z"], sd["b"], A, cur)
+        for n in range(N):
+            if int(cnt[n]) == t + 1:
+                ref[n] = cur[n]
+    torch.cuda.synchronize()
+    print(f"[parity] fold {dtype} d={dk}: max|fold - steps| = "
+          f"{float((folded - ref).abs().max()):.3e}", flush=True)
+    assert torch.equal(folded, ref)
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("fp32", 16)])
+def test_fold_vs_oracle(kda, dtype, dk):
+    """The folded states against the oracle's replay on the same (rounded)
+    inputs; the arithmetic is fp32 in both dtypes."""
+    N, H, W = 6, 4, 7
+    run, _, win = _fold_window(dtype, dk, N, H, W, seed=22)
+    n_acc = [7, 2, 0, 4, 7, 1]
+    st = run["state"].cuda().contiguous()
+    kda.kda_recurrent_fold(win["k"].cuda().contiguous(), win["v"].cuda().contiguous(),
+                           win["z"].cuda().contiguous(), win["b"].cuda().contiguous(),
+                           run["A"].cuda(), torch.tensor(n_acc, dtype=torch.int32).cuda(), st)
+    ref = oracle.replay_fold(win["k"], win["v"], win["z"], win["b"], run["A"], run["state"], n_acc)
+    torch.cuda.synchronize()
+    err = rel_err(st, ref)
+    _report(f"fold vs oracle {dtype} d={dk}", state=err)
+    assert err <= TOL_F32
+
+
+def test_fold_decode_workload_window(kda):
+    """The decode workload's shape (256 sequences, 12 heads, d = 128, bf16)
+    with a window of 7 draft tokens (the page's num_speculative_tokens) and
+    mixed acceptance: equal bits to the recurrent steps, and the oracle on
+    sampled sequences."""
+    N, H, W = 256, 12, 7
+    run, steps, win = _fold_window("bf16", 128, N, H, W, seed=23)
+    g = torch.Generator().manual_seed(5)
+    n_acc = torch.randint(0, W + 1, (N,), generator=g, dtype=torch.int32)
+    A = run["A"].cuda()
+    st0 = run["state"].cuda().contiguous()
+    folded = st0.clone()
+    kda.kda_recurrent_fold(win["k"].cuda().contiguous(), win["v"].cuda().contiguous(),
+                           win["z"].cuda().contiguous(), win["b"].cuda().contiguous(), A,
+                           n_acc.cuda(), folded)
+    cur = st0.clone()
+    ref = st0.clone()
+    for t, s in enumerate(steps):
+        sd = to_dev(s)
+        kda.kda_recurrent_step(sd["q"], sd["k"], sd["v"], sd["z"], sd["b"], A, cur)
+        sel = (n_acc == t + 1).nonzero().flatten().cuda()
+        ref[sel] = cur[sel]
+    torch.cuda.synchronize()
+    assert torch.equal(folded, ref)
+    for n in (0, 97, 255):
+        r = oracle.replay_fold(win["k"][n:n + 1], win["v"][n:n + 1], win["z"][n:n + 1],
+                               win["b"][n:n + 1], run["A"], run["state"][n:n + 1], [int(n_acc[n])])
+        assert rel_err(folded[n], r[0]) <= TOL_F32

@@ -302,3 +302,87 @@ def test_chunkwise_records_the_incoming_state():
     assert np.array_equal(inter[0][0]["S0"], h0[0])
     _, S16 = oracle.recurrence(q[:16], k[:16], v[:16], z[:16], b[:16], A, h0)
     assert np.allclose(inter[1][0]["S0"], S16[0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- replay fold
+
+def _window(rng, N, W, H, dk, dv):
+    k = rng.standard_normal((N, W, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, W, H, dv))
+    z = rng.standard_normal((N, W, H, dk))
+    b = rng.standard_normal((N, W, H))
+    A = rng.uniform(-1, 1, H)
+    state = 0.3 * rng.standard_normal((N, H, dk, dv))
+    return k, v, z, b, A, state
+
+
+def test_replay_fold_counts_zero_and_clamped():
+    """[K3-ATTN §6.2]: only the accepted prefix is replayed.  A count of zero
+    (or below) leaves the checkpoint as it is; a count above the window length
+    replays the whole window."""
+    rng = np.random.default_rng(11)
+    k, v, z, b, A, state = _window(rng, 4, 5, 2, 6, 5)
+    out = oracle.replay_fold(k, v, z, b, A, state, [0, -3, 5, 9])
+    assert np.array_equal(out[0], state[0]) and np.array_equal(out[1], state[1])
+    full = oracle.replay_fold(k, v, z, b, A, state, [5, 5, 5, 5])
+    assert np.array_equal(out[3], full[3]) and np.array_equal(out[2], full[2])
+
+
+def test_replay_fold_pure_decay_closed_form():
+    """[K3-ATTN §6.2] with beta = 0 (b = -1e4): no write happens, so replaying
+    n tokens multiplies each state row by the product of the n decays
+    alpha = exp(-5 sigma(e^{A_h} z)) of [LA-KDA §5.4]."""
+    rng = np.random.default_rng(12)
+    N, W, H, dk, dv = 3, 6, 2, 5, 4
+    k, v, z, b, A, state = _window(rng, N, W, H, dk, dv)
+    b = np.full_like(b, -BIG)
+    n_acc = [2, 6, 4]
+    out = oracle.replay_fold(k, v, z, b, A, state, n_acc)
+    for s, n in enumerate(n_acc):
+        for h in range(H):
+            logit = np.exp(A[h]) * z[s, :n, h]                     # [n, dk]
+            alpha = np.exp(-5.0 / (1.0 + np.exp(-logit)))
+            expect = np.prod(alpha, axis=0)[:, None] * state[s, h]
+            assert np.allclose(out[s, h], expect, rtol=1e-12, atol=0)
+
+
+def test_replay_fold_exact_recall_of_last_token():
+    """With beta = 1 and a unit key, the state after a token recalls that
+    token's value exactly at its key, S^T k = v ([K3-ATTN §2.2]); this holds
+    for the state the fold leaves after the last accepted token."""
+    rng = np.random.default_rng(13)
+    N, W, H, dk, dv = 3, 4, 2, 6, 3
+    k, v, z, b, A, state = _window(rng, N, W, H, dk, dv)
+    b = np.full_like(b, BIG)
+    n_acc = [1, 3, 4]
+    out = oracle.replay_fold(k, v, z, b, A, state, n_acc)
+    for s, n in enumerate(n_acc):
+        for h in range(H):
+            kk = k[s, n - 1, h]
+            assert np.allclose(out[s, h].T @ kk, v[s, n - 1, h], rtol=0, atol=1e-12)
+
+
+def test_replay_fold_equals_chunked_final_state():
+    """The fold's state equals the final state of the chunked formulation
+    ([LA-KDA §7.3] with the decay) run over the accepted tokens from the same
+    checkpoint: two independent routes to the same state."""
+    rng = np.random.default_rng(14)
+    N, W, H, dk, dv = 3, 7, 2, 8, 6
+    k, v, z, b, A, state = _window(rng, N, W, H, dk, dv)
+    n_acc = [7, 5, 3]
+    out = oracle.replay_fold(k, v, z, b, A, state, n_acc)
+    for s, n in enumerate(n_acc):
+        q = rng.standard_normal((n, H, dk))
+        _, S = oracle.chunkwise(q, k[s, :n], v[s, :n], z[s, :n], b[s, :n], A, state[s], chunk=4)
+        assert np.allclose(out[s], S, rtol=1e-12, atol=1e-13)
+
+
+def test_replay_window_token_is_about_one_kilobyte():
+    """[K3-ATTN §6.2] keeps about 1 KB of inputs per draft token instead of a
+    64 KB state snapshot: at d_k = d_v = 128 the fold's per-token inputs are
+    k and v in bf16 plus the fp32 gate logits and beta logit."""
+    dk = dv = 128
+    per_token = 2 * dk + 2 * dv + 4 * dk + 4
+    assert 1000 <= per_token <= 1100
+    assert dk * dv * 4 == 64 * 1024
