@@ -291,3 +291,72 @@ def replay_fold(k, v, z, b, A, state, n_accept):
         _, out[s] = recurrence(np.zeros_like(k[s, :n]), k[s, :n], v[s, :n], z[s, :n], b[s, :n], A,
                                state[s])
     return out
+
+
+# ------------------------------------------------------------ around the core
+# The steps either side of the recurrence that act on one token-head row:
+# [LA-KDA §5.3] q, k = L2Norm(Swish(ShortConv(W x))), v = Swish(ShortConv(W x));
+# [LA-KDA §5.5] y = W_o [Sigmoid(W_g x) * RMSNorm(o)], the RMSNorm per head
+# ([K3-ATTN §2.3]).  The projections W are outside: these functions take their
+# outputs.  Readings where the pages are silent: the convolution has no bias,
+# its four taps are ordered oldest first; Swish has unit slope; L2Norm and
+# RMSNorm take an additive epsilon under the square root; RMSNorm has one
+# weight per channel shared by the heads.
+
+CONV_TAPS = 4   # depthwise causal convolution, kernel size 4 [K3-ATTN §2.3]
+
+
+def short_conv(x, w, state=None):
+    """Depthwise causal convolution over time: y_t = sum_j w[..., j] x_{t-3+j}
+    (j = 0..3, taps oldest first, no bias).  x [T, H, d]; w [H, d, 4]; state
+    [3, H, d] holds the three inputs before x[0] (None: zeros, a sequence
+    start).  Returns (y [T, H, d], the state after x: its last three inputs)."""
+    x, w = _f64(x), _f64(w)
+    T, H, d = x.shape
+    hist = np.zeros((CONV_TAPS - 1, H, d)) if state is None else _f64(state)
+    xs = np.concatenate([hist, x], axis=0)
+    y = np.zeros((T, H, d))
+    for t in range(T):
+        for j in range(CONV_TAPS):
+            y[t] += w[..., j] * xs[t + j]
+    return y, xs[len(xs) - (CONV_TAPS - 1):].copy()
+
+
+def silu(x):
+    """Swish with unit slope: x * sigma(x)."""
+    x = _f64(x)
+    return x * logistic(x)
+
+
+def l2norm(x, eps):
+    """x / sqrt(sum_c x_c^2 + eps) over the last axis."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rmsnorm_gated(o, g, w, eps):
+    """sigma(g) * RMSNorm(o): RMSNorm over one head's d_v channels,
+    o / sqrt(mean_c o_c^2 + eps) * w, then the output gate sigma(g)."""
+    o, g, w = _f64(o), _f64(g), _f64(w)
+    r = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return logistic(g) * r * w
+
+
+def fused_forward(q_in, k_in, v_in, conv_w, z, b, A, gate, norm_w, h0=None, conv_state=None,
+                  l2_eps=1e-6, rms_eps=1e-5):
+    """One sequence through the whole KDA layer between its projections:
+    q, k = L2Norm(Swish(ShortConv(.))), v = Swish(ShortConv(.)), the
+    recurrence, then Sigmoid(gate) * RMSNorm(o).
+    q_in, k_in, v_in, gate [T, H, d]; conv_w [3, H, d, 4] (q, k, v taps);
+    conv_state [3, 3, H, d] or None (q, k, v histories); norm_w [d].
+    Returns (y [T, H, d], S [H, d, d], conv_state_out [3, 3, H, d])."""
+    conv_w = _f64(conv_w)
+    cs = [None] * 3 if conv_state is None else [_f64(conv_state)[i] for i in range(3)]
+    qc, sq = short_conv(q_in, conv_w[0], cs[0])
+    kc, sk = short_conv(k_in, conv_w[1], cs[1])
+    vc, sv = short_conv(v_in, conv_w[2], cs[2])
+    q = l2norm(silu(qc), l2_eps)
+    k = l2norm(silu(kc), l2_eps)
+    v = silu(vc)
+    o, S = recurrence(q, k, v, z, b, A, h0)
+    return rmsnorm_gated(o, gate, norm_w, rms_eps), S, np.stack([sq, sk, sv])

@@ -386,3 +386,105 @@ def test_replay_window_token_is_about_one_kilobyte():
     per_token = 2 * dk + 2 * dv + 4 * dk + 4
     assert 1000 <= per_token <= 1100
     assert dk * dv * 4 == 64 * 1024
+
+
+# ---------------------------------------------------------------- around the core
+
+def test_short_conv_worked_example():
+    """[K3-ATTN §2.3] kernel-size-4 causal convolution on one channel: with taps
+    (1, 10, 100, 1000) oldest first each output spells its last four inputs as
+    decimal digits, x = 1..5 -> 1000, 2100, 3210, 4321, 5432; a carried history
+    (7, 8, 9) gives 9 * 100 + 8 * 10 + 7 + 1000 = 1987 first."""
+    x = np.arange(1.0, 6.0).reshape(5, 1, 1)
+    w = np.array([1.0, 10.0, 100.0, 1000.0]).reshape(1, 1, 4)
+    y, st = oracle.short_conv(x, w)
+    assert y[:, 0, 0].tolist() == [1000.0, 2100.0, 3210.0, 4321.0, 5432.0]
+    assert st[:, 0, 0].tolist() == [3.0, 4.0, 5.0]
+    y2, _ = oracle.short_conv(x[:1], w, np.array([7.0, 8.0, 9.0]).reshape(3, 1, 1))
+    assert y2[0, 0, 0] == 1987.0
+
+
+def test_short_conv_is_causal_and_resumable():
+    """Depthwise and causal ([K3-ATTN §2.3]): an output never sees later inputs
+    or other channels, and running a sequence in two pieces with the carried
+    state equals one pass."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((11, 2, 5))
+    w = rng.standard_normal((2, 5, 4))
+    y, st = oracle.short_conv(x, w)
+    x2 = x.copy()
+    x2[7:] += 3.0                       # change the future
+    x2[:, 1, 2] += 1.0                  # and one other channel
+    y2, _ = oracle.short_conv(x2, w)
+    assert np.array_equal(y[:7, 0], y2[:7, 0]) and np.array_equal(y[:7, 1, :2], y2[:7, 1, :2])
+    ya, sa = oracle.short_conv(x[:4], w)
+    yb, sb = oracle.short_conv(x[4:], w, sa)
+    assert np.allclose(np.concatenate([ya, yb]), y, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(sb, st)
+
+
+def test_swish_l2norm_rmsnorm_closed_forms():
+    """Swish(0) = 0 and Swish(ln 3) = 3/4 ln 3 (sigma(ln 3) = 3/4); L2Norm
+    returns unit rows whatever the scale; Sigmoid(g) RMSNorm(c 1) =
+    sigma(g) c / sqrt(c^2 + eps) per channel ([LA-KDA §5.5])."""
+    assert oracle.silu(0.0) == 0.0
+    assert math.isclose(float(oracle.silu(math.log(3.0))), 0.75 * math.log(3.0), rel_tol=1e-15)
+    assert math.isclose(float(oracle.silu(40.0)), 40.0, rel_tol=1e-15)
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((4, 3, 16))
+    n = oracle.l2norm(x, 0.0)
+    assert np.allclose(np.linalg.norm(n, axis=-1), 1.0, rtol=1e-14)
+    assert np.allclose(oracle.l2norm(1e3 * x, 0.0), n, rtol=1e-13)
+    assert np.array_equal(oracle.l2norm(np.zeros(8), 1e-6), np.zeros(8))
+    c, eps = -2.5, 1e-5
+    o = np.full((1, 1, 8), c)
+    y0 = oracle.rmsnorm_gated(o, np.zeros((1, 1, 8)), np.ones(8), eps)
+    assert np.allclose(y0, 0.5 * c / math.sqrt(c * c + eps), rtol=1e-15)
+    y1 = oracle.rmsnorm_gated(o, np.full((1, 1, 8), BIG), 2 * np.ones(8), eps)
+    assert np.allclose(y1, 2 * c / math.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_fused_layer_resumes_with_both_states():
+    """[K3-NOTES]: KDA carries a short-convolution state for q, k, v beside the
+    recurrent state; a sequence cut in two and resumed from both states gives
+    the same outputs and final states as one pass."""
+    rng = np.random.default_rng(33)
+    T, H, d = 13, 2, 8
+    q_in, k_in, v_in, gate = (rng.standard_normal((T, H, d)) for _ in range(4))
+    z = rng.standard_normal((T, H, d))
+    b = rng.standard_normal((T, H))
+    A = rng.uniform(-1, 1, H)
+    cw = rng.standard_normal((3, H, d, 4))
+    nw = rng.uniform(0.5, 1.5, d)
+    y, S, cs = oracle.fused_forward(q_in, k_in, v_in, cw, z, b, A, gate, nw)
+    a = 5
+    y1, S1, cs1 = oracle.fused_forward(q_in[:a], k_in[:a], v_in[:a], cw, z[:a], b[:a], A, gate[:a], nw)
+    y2, S2, cs2 = oracle.fused_forward(q_in[a:], k_in[a:], v_in[a:], cw, z[a:], b[a:], A, gate[a:], nw,
+                                       h0=S1, conv_state=cs1)
+    assert np.allclose(np.concatenate([y1, y2]), y, rtol=1e-12, atol=1e-12)
+    assert np.allclose(S2, S, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(cs2, cs)
+
+
+def test_fused_layer_identity_taps_reduce_to_the_core():
+    """With the taps (0, 0, 0, 1) the convolution passes its input through, so
+    the layer is the recurrence on L2Norm(Swish(.)) inputs followed by the
+    output gate; with Swish inputs already unit rows the L2Norm is exact."""
+    rng = np.random.default_rng(34)
+    T, H, d = 9, 2, 6
+    q_in, k_in, v_in, gate = (rng.standard_normal((T, H, d)) for _ in range(4))
+    z = rng.standard_normal((T, H, d))
+    b = rng.standard_normal((T, H))
+    A = rng.uniform(-1, 1, H)
+    cw = np.zeros((3, H, d, 4))
+    cw[..., 3] = 1.0
+    nw = np.ones(d)
+    y, S, _ = oracle.fused_forward(q_in, k_in, v_in, cw, z, b, A, gate, nw, l2_eps=0.0, rms_eps=0.0)
+    sq = q_in / (1 + np.exp(-q_in)) * 1.0
+    sk = k_in / (1 + np.exp(-k_in))
+    q = sq / np.linalg.norm(sq, axis=-1, keepdims=True)
+    k = sk / np.linalg.norm(sk, axis=-1, keepdims=True)
+    o, S_ref = oracle.recurrence(q, k, v_in / (1 + np.exp(-v_in)), z, b, A)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    assert np.allclose(S, S_ref, rtol=1e-13, atol=1e-14)
+    assert np.allclose(y, o / rms / (1 + np.exp(-gate)), rtol=1e-12, atol=1e-13)
