@@ -10,6 +10,8 @@ Names follow the C ABI in include/kda.h:
                   chunk_size=64, output_final_state=True, workspace=None) -> (o, hT)
     kda_recurrent_step(q, k, v, g, beta, A, state) -> o     (state updated in place)
     kda_recurrent_fold(k, v, g, beta, A, n_accept, state)    (state updated in place)
+    kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, ...) -> (y, hT, conv_state)
+    kda_layer_step(q_in, k_in, v_in, conv_w, conv_state, g, beta, A, state, gate, norm_w) -> y
     kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
 `g` are the raw per-channel gate logits and `beta` the raw write-strength
 logits; both activations run inside the kernels.
@@ -22,6 +24,7 @@ from typing import Optional
 
 __all__ = [
     "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_fold",
+    "kda_layer_fwd", "kda_layer_step", "kda_layer_fwd_workspace_bytes",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
     "kda_recurrent_step_supported", "EXPORTED_SYMBOLS",
 ]
@@ -34,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "kda_status_string", "kda_chunk_fwd_supported", "kda_recurrent_step_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_debug_floats",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
+    "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step",
 )
 
 
@@ -75,6 +79,14 @@ def lib() -> ctypes.CDLL:
     L.kda_recurrent_step.argtypes = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, vp]
     L.kda_recurrent_fold.restype = i
     L.kda_recurrent_fold.argtypes = [vp, vp, f, f, f, vp, f, i, i, i, i, i, i, vp]
+    fl = ctypes.c_float
+    L.kda_layer_fwd_workspace_bytes.restype = sz
+    L.kda_layer_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.kda_layer_fwd.restype = i
+    L.kda_layer_fwd.argtypes = ([vp, vp, vp, f, vp, vp, f, f, f, f, vp, vp, f, fl, fl]
+                                + [i] * 7 + [vp, f, vp, sz, vp])
+    L.kda_layer_step.restype = i
+    L.kda_layer_step.argtypes = [vp, vp, vp, f, vp, f, f, f, f, vp, f, fl, fl, vp, i, i, i, i, vp]
     _lib = L
     return L
 
@@ -286,3 +298,85 @@ def kda_recurrent_fold(k, v, g, beta, A, n_accept, state) -> None:
     rc = lib().kda_recurrent_fold(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(n_accept),
                                   _ptr(state), N, W, H, dk, dv, code, _stream(dev))
     _check(rc, "kda_recurrent_fold")
+
+
+def kda_layer_fwd_workspace_bytes(B, T, H, d, N, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(lib().kda_layer_fwd_workspace_bytes(B, T, H, d, N, chunk, code))
+
+
+def kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, initial_state=None,
+                  conv_state=None, cu_seqlens=None, chunk_size: int = 64, l2_eps: float = 1e-6,
+                  rms_eps: float = 1e-5, output_final_state: bool = True, workspace=None):
+    """The KDA layer between its projections: q, k = L2Norm(Swish(ShortConv)),
+    v = Swish(ShortConv), the chunked core, y = Sigmoid(gate) * RMSNorm(o).
+    q_in, k_in, v_in, gate [B, T, H, d] (bf16 or fp32); conv_w [3, H, d, 4]
+    fp32; g, beta, A, initial_state, cu_seqlens as for kda_chunk_fwd; norm_w
+    [d] fp32; conv_state [N, 3, 3, H, d] (input dtype) or None.  Returns
+    (y, final_state or None, final conv_state or None)."""
+    torch = _torch()
+    B, T, H, dk, dv, N, dev, dt = _prefill_args(q_in, k_in, v_in, g, beta, A, initial_state,
+                                                cu_seqlens)
+    if dk != dv:
+        raise ValueError("the layer entry point needs d_k == d_v")
+    d = dk
+    _req(conv_w, "conv_w", torch.float32, dev)
+    _req(gate, "gate", dt, dev)
+    _req(norm_w, "norm_w", torch.float32, dev)
+    if conv_w.shape != (3, H, d, 4) or gate.shape != q_in.shape or norm_w.shape != (d,):
+        raise ValueError("conv_w [3, H, d, 4], gate [B, T, H, d] and norm_w [d] expected")
+    if conv_state is not None:
+        _req(conv_state, "conv_state", dt, dev)
+        if conv_state.shape != (N, 3, 3, H, d):
+            raise ValueError(f"conv_state must be [{N}, 3, 3, {H}, {d}]")
+    code = _dtype_code(q_in)
+    L = lib()
+    need = int(L.kda_layer_fwd_workspace_bytes(B, T, H, d, N, chunk_size, code))
+    if need == 0:
+        _check(2 if not L.kda_chunk_fwd_supported(d, d, chunk_size, code) else 1,
+               "kda_layer_fwd_workspace_bytes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty((B, T, H, d), dtype=dt, device=dev)
+    hT = torch.empty((N, H, d, d), dtype=torch.float32, device=dev) if output_final_state else None
+    csT = torch.empty((N, 3, 3, H, d), dtype=dt, device=dev) if output_final_state else None
+    rc = L.kda_layer_fwd(_ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(conv_w), _ptr(conv_state),
+                         _ptr(csT), _ptr(g), _ptr(beta), _ptr(A), _ptr(initial_state),
+                         _ptr(cu_seqlens), _ptr(gate), _ptr(norm_w), float(l2_eps), float(rms_eps),
+                         B, T, H, d, N, chunk_size, code, _ptr(y), _ptr(hT), _ptr(workspace),
+                         workspace.numel(), _stream(dev))
+    _check(rc, "kda_layer_fwd")
+    return y, hT, csT
+
+
+def kda_layer_step(q_in, k_in, v_in, conv_w, conv_state, g, beta, A, state, gate, norm_w,
+                   l2_eps: float = 1e-6, rms_eps: float = 1e-5):
+    """One decode token of the layer in one launch: q_in, k_in, v_in, gate
+    [N, H, d]; conv_w [3, H, d, 4] fp32; conv_state [N, 3, 3, H, d] (input
+    dtype, shifted in place); g [N, H, d], beta [N, H], A [H] fp32; state
+    [N, H, d, d] fp32 (in place); norm_w [d] fp32.  Returns y [N, H, d]."""
+    torch = _torch()
+    _req(q_in, "q_in")
+    dev, dt = q_in.device, q_in.dtype
+    code = _dtype_code(q_in)
+    for t, name in ((k_in, "k_in"), (v_in, "v_in"), (gate, "gate"), (conv_state, "conv_state")):
+        _req(t, name, dt, dev)
+    for t, name in ((conv_w, "conv_w"), (g, "g"), (beta, "beta"), (A, "A"), (state, "state"),
+                    (norm_w, "norm_w")):
+        _req(t, name, torch.float32, dev)
+    if q_in.dim() != 3:
+        raise ValueError("q_in must be [N, H, d]")
+    N, H, d = q_in.shape
+    if (k_in.shape != q_in.shape or v_in.shape != q_in.shape or gate.shape != q_in.shape
+            or g.shape != q_in.shape):
+        raise ValueError("k_in, v_in, gate and g must match q_in [N, H, d]")
+    if (conv_w.shape != (3, H, d, 4) or conv_state.shape != (N, 3, 3, H, d) or beta.shape != (N, H)
+            or A.shape != (H,) or state.shape != (N, H, d, d) or norm_w.shape != (d,)):
+        raise ValueError("conv_w [3, H, d, 4], conv_state [N, 3, 3, H, d], beta [N, H], A [H], "
+                         "state [N, H, d, d] and norm_w [d] expected")
+    y = torch.empty((N, H, d), dtype=dt, device=dev)
+    rc = lib().kda_layer_step(_ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(conv_w), _ptr(conv_state),
+                              _ptr(g), _ptr(beta), _ptr(A), _ptr(state), _ptr(gate), _ptr(norm_w),
+                              float(l2_eps), float(rms_eps), _ptr(y), N, H, d, code, _stream(dev))
+    _check(rc, "kda_layer_step")
+    return y

@@ -58,6 +58,29 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// workspace of the layer entry point: the core's, then q, k, v after the
+// convolution and o before the output gate (dtype, [B*T, H, d] each)
+struct LayerWs {
+    size_t core, row_bytes, total;
+};
+
+LayerWs layer_ws(int B, int T, int H, int d, int N, int chunk, kda_dtype_t dtype) {
+    LayerWs w{0, 0, 0};
+    if (!dtype_ok(dtype) || !prefill_sizes_ok(B, T, H, d, d, N, chunk)) return w;
+    if (!chunk_shape_supported(d, d, chunk)) return w;
+    const bool fast = use_fast_path(d, d, chunk, dtype == KDA_BF16);
+    const WsLayout L = ws_layout(B, T, H, d, d, N, chunk, fast);
+    if (L.total == 0) return w;
+    w.core = align256(L.total);
+    w.row_bytes = align256((size_t)B * T * H * d * (dtype == KDA_BF16 ? 2 : 4));
+    w.total = w.core + 4 * w.row_bytes;
+    return w;
+}
+
+bool eps_ok(float e) { return e >= 0.f && e < 1e30f; }
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +171,74 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, con
     if (!q || !k || !v || !g_logits || !beta_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_decode(q, k, v, g_logits, beta_logits, A, state, o, N, H, dk, dv,
                                  dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_layer_fwd_workspace_bytes(int B, int T, int H, int d, int N, int chunk,
+                                     kda_dtype_t dtype) {
+    return layer_ws(B, T, H, d, N, chunk, dtype).total;
+}
+
+kda_status_t kda_layer_fwd(const void* q_in, const void* k_in, const void* v_in,
+                           const float* conv_w, const void* conv_state0, void* conv_stateT,
+                           const float* g_logits, const float* beta_logits, const float* A,
+                           const float* h0, const int* cu_seqlens, const void* gate,
+                           const float* norm_w, float l2_eps, float rms_eps, int B, int T, int H,
+                           int d, int N, int chunk, kda_dtype_t dtype, void* y, float* hT,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (!prefill_sizes_ok(B, T, H, d, d, N, chunk)) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
+    if (!eps_ok(l2_eps) || !eps_ok(rms_eps)) return KDA_ERR_INVALID_ARG;
+    if (!chunk_shape_supported(d, d, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    const long long tokens = (long long)B * T;
+    if (tokens > 0 && (!q_in || !k_in || !v_in || !g_logits || !beta_logits || !gate || !y))
+        return KDA_ERR_INVALID_ARG;
+    if (!A || !conv_w || !norm_w) return KDA_ERR_INVALID_ARG;
+    const LayerWs W = layer_ws(B, T, H, d, N, chunk, dtype);
+    if (W.total == 0) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < W.total) return KDA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* qw = ws + W.core;
+    void* kw = ws + W.core + W.row_bytes;
+    void* vw = ws + W.core + 2 * W.row_bytes;
+    void* ow = ws + W.core + 3 * W.row_bytes;
+    const int bf = dtype == KDA_BF16;
+    const int Ttot = (int)tokens;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_layer_pre(q_in, k_in, v_in, conv_w, conv_state0, cu_seqlens, N, T, Ttot, H,
+                                    d, l2_eps, qw, kw, vw, bf, s);
+    if (e == hipSuccess && conv_stateT)
+        e = launch_layer_convstate(q_in, k_in, v_in, conv_state0, cu_seqlens, N, T, Ttot, H, d,
+                                   conv_stateT, bf, s);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    const kda_status_t st = run_prefill(qw, kw, vw, g_logits, beta_logits, A, h0, cu_seqlens, B, T,
+                                        H, d, d, N, chunk, dtype, ow, hT, ws, W.core, nullptr,
+                                        nullptr, nullptr, 0, stream);
+    if (st != KDA_OK) return st;
+    e = launch_layer_post(ow, gate, norm_w, rms_eps, tokens * H, d, y, bf, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_layer_step(const void* q_in, const void* k_in, const void* v_in,
+                            const float* conv_w, void* conv_state, const float* g_logits,
+                            const float* beta_logits, const float* A, float* state,
+                            const void* gate, const float* norm_w, float l2_eps, float rms_eps,
+                            void* y, int N, int H, int d, kda_dtype_t dtype, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || d < 1) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!eps_ok(l2_eps) || !eps_ok(rms_eps)) return KDA_ERR_INVALID_ARG;
+    if (!decode_supported(d, d)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q_in || !k_in || !v_in || !conv_w || !conv_state || !g_logits || !beta_logits || !A ||
+        !state || !gate || !norm_w || !y)
+        return KDA_ERR_INVALID_ARG;
+    hipError_t e = launch_layer_step(q_in, k_in, v_in, conv_w, conv_state, g_logits, beta_logits, A,
+                                     state, gate, norm_w, l2_eps, rms_eps, y, N, H, d,
+                                     dtype == KDA_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -119,6 +119,20 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          const float* b, const float* A, float* state, void* o,
                          int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s);
 bool decode_supported(int dk, int dv);
+hipError_t launch_layer_pre(const void* q_in, const void* k_in, const void* v_in,
+                            const float* conv_w, const void* cs0, const int* cu, int N, int Tfix,
+                            int Ttot, int H, int d, float l2_eps, void* q_out, void* k_out,
+                            void* v_out, int dtype_bf16, hipStream_t s);
+hipError_t launch_layer_convstate(const void* q_in, const void* k_in, const void* v_in,
+                                  const void* cs0, const int* cu, int N, int Tfix, int Ttot,
+                                  int H, int d, void* cs_out, int dtype_bf16, hipStream_t s);
+hipError_t launch_layer_post(const void* o, const void* gate, const float* norm_w, float rms_eps,
+                             long long rows, int d, void* y, int dtype_bf16, hipStream_t s);
+hipError_t launch_layer_step(const void* q_in, const void* k_in, const void* v_in,
+                             const float* conv_w, void* conv_state, const float* z, const float* b,
+                             const float* A, float* state, const void* gate, const float* norm_w,
+                             float l2_eps, float rms_eps, void* y, int N, int H, int d,
+                             int dtype_bf16, hipStream_t s);
 hipError_t launch_fold(const void* k, const void* v, const float* z, const float* b,
                        const float* A, const int* n_accept, float* state, int N, int W, int H,
                        int dk, int dv, int dtype_bf16, hipStream_t s);

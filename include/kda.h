@@ -198,6 +198,71 @@ KDA_API kda_status_t kda_recurrent_step(const void* q, const void* k, const void
                                 void* stream);
 
 /*
+ * The KDA layer between its projections: the core with the steps either side
+ * of it that act on one token-head row.
+ *
+ *   before  q, k = L2Norm(Swish(ShortConv(q_in | k_in))),
+ *           v = Swish(ShortConv(v_in))                     [LA-KDA §5.3], [K3-ATTN §2.3]
+ *   core    the recurrence (1)-(4) of kda_chunk_fwd / kda_recurrent_step
+ *   after   y = Sigmoid(gate) * RMSNorm(o) per head        [LA-KDA §5.5], [K3-ATTN §2.3]
+ *
+ * ShortConv is a depthwise causal convolution with four taps per channel
+ * (kernel size 4), taps ordered oldest first, no bias; the three inputs
+ * before a sequence's first token come from the carried convolution state
+ * (zeros without one) [K3-NOTES].  Swish(x) = x * sigmoid(x).  L2Norm(x) =
+ * x / sqrt(sum x^2 + l2_eps) over the head's d channels; RMSNorm(o) =
+ * o / sqrt(mean o^2 + rms_eps) * norm_w, with one weight per channel shared
+ * by the heads.  Readings of the pages where they are silent: no convolution
+ * bias, the epsilons under the square roots, the shared RMSNorm weight.
+ *
+ * Prefill (d_k = d_v = d; same supported set as kda_chunk_fwd):
+ *   q_in, k_in, v_in  [B, T, H, d]      dtype  projections before the convolution
+ *   conv_w            [3, H, d, 4]      fp32   taps of q, k, v
+ *   conv_state0       [N, 3, 3, H, d]   dtype  per sequence, for q, k, v, the
+ *                                              inputs at t-3, t-2, t-1 before
+ *                                              its first token; NULL for zeros
+ *   conv_stateT       [N, 3, 3, H, d]   dtype  the last three inputs of each
+ *                                              sequence (reaching into
+ *                                              conv_state0 for sequences shorter
+ *                                              than three); NULL to skip; may be
+ *                                              conv_state0 (in place)
+ *   g_logits, beta_logits, A, h0, cu_seqlens, hT  as for kda_chunk_fwd
+ *   gate              [B, T, H, d]      dtype  output-gate logits W_g x
+ *   norm_w            [d]               fp32
+ *   y                 [B, T, H, d]      dtype  Sigmoid(gate) * RMSNorm(o), before W_o
+ * The workspace (kda_layer_fwd_workspace_bytes) holds the core's workspace
+ * and the intermediate q, k, v and o.  Outputs of tokens outside every
+ * sequence are unspecified.  Errors as for kda_chunk_fwd; negative or
+ * non-finite epsilons are KDA_ERR_INVALID_ARG.
+ */
+KDA_API size_t kda_layer_fwd_workspace_bytes(int B, int T, int H, int d, int N, int chunk,
+                                     kda_dtype_t dtype);
+KDA_API kda_status_t kda_layer_fwd(const void* q_in, const void* k_in, const void* v_in,
+                           const float* conv_w, const void* conv_state0, void* conv_stateT,
+                           const float* g_logits, const float* beta_logits, const float* A,
+                           const float* h0, const int* cu_seqlens, const void* gate,
+                           const float* norm_w, float l2_eps, float rms_eps, int B, int T, int H,
+                           int d, int N, int chunk, kda_dtype_t dtype, void* y, float* hT,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode of the same layer, one token per sequence, in one launch
+ * ([K3-ATTN §6.3]: convolution, recurrent update and gated RMSNorm fused):
+ *   q_in, k_in, v_in, gate  [N, H, d]          dtype
+ *   conv_w                  [3, H, d, 4]       fp32
+ *   conv_state              [N, 3, 3, H, d]    dtype, read and shifted in place
+ *   g_logits [N, H, d], beta_logits [N, H], A [H], state [N, H, d, d]  as for
+ *   kda_recurrent_step (state in place)
+ *   y                       [N, H, d]          dtype
+ * Same supported set as kda_recurrent_step.  N = 0 is a no-op.
+ */
+KDA_API kda_status_t kda_layer_step(const void* q_in, const void* k_in, const void* v_in,
+                            const float* conv_w, void* conv_state, const float* g_logits,
+                            const float* beta_logits, const float* A, float* state,
+                            const void* gate, const float* norm_w, float l2_eps, float rms_eps,
+                            void* y, int N, int H, int d, kda_dtype_t dtype, void* stream);
+
+/*
  * Replay fold for speculative decoding ([K3-ATTN §6.2], ReplaySSM): instead
  * of a state snapshot per draft token, the caller keeps each window token's
  * inputs; once the number of accepted tokens is known, this call advances

@@ -23,6 +23,12 @@ Recipe (one torch.Generator per call, seeded; the draw order is fixed):
   b    : N(0,1) fp32 per (token, head) (raw beta logits)
   h0   : 0.02 * N(0,1) fp32 per (sequence, head), or None for a zero state
 Decode draws A and h0 first, then (q, k, v, z, b) for every step in turn.
+
+Layer inputs (the projections before the short convolution, make_layer): the
+prefill draw above, then q_in, k_in, v_in ~ N(0,1) and gate ~ N(0,1) cast to
+the config dtype, conv_w ~ 0.5 N(0,1) fp32 [3, H, d, 4], norm_w ~ U(0.5, 1.5)
+fp32 [d], and conv_state0 ~ N(0,1) cast to the config dtype [N, 3, 3, H, d]
+(or None).
 """
 from __future__ import annotations
 
@@ -32,7 +38,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "PrefillCase", "DecodeCase", "CONFIGS", "make_prefill", "make_decode",
+    "PrefillCase", "DecodeCase", "CONFIGS", "make_prefill", "make_decode", "make_layer",
     "varlen_lengths", "dtype_of",
 ]
 
@@ -168,3 +174,26 @@ def make_decode(case: DecodeCase, device="cpu", seed: int = 0,
         b = torch.randn(n, H, generator=gen, device=dev, dtype=f32)
         per_step.append(dict(q=q, k=k, v=v, z=z, b=b))
     return dict(A=A, state=state, steps=per_step, N=n, H=H, dk=dk, dv=dv, dtype=case.dtype)
+
+
+def make_layer(case: PrefillCase, device="cpu", seed: int = 0, T: Optional[int] = None,
+               lengths: Optional[list] = None, conv_state: bool = True) -> dict:
+    """A prefill draw (make_prefill) extended with the layer's inputs:
+    q_in, k_in, v_in, gate [B, T, H, d] (config dtype), conv_w [3, H, d, 4],
+    norm_w [d] (fp32) and conv_state0 [N, 3, 3, H, d] (config dtype) or None.
+    The core's q, k, v of the prefill draw are kept but unused by the layer."""
+    d = make_prefill(case, device=device, seed=seed, T=T, lengths=lengths)
+    dev = torch.device(device)
+    gen = _gen(dev, seed + 7919)
+    dt = dtype_of(case.dtype)
+    f32 = torch.float32
+    B, Ttot, H, dk, N = d["B"], d["T"], d["H"], d["dk"], d["N"]
+    d["q_in"] = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32).to(dt)
+    d["k_in"] = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32).to(dt)
+    d["v_in"] = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32).to(dt)
+    d["gate"] = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32).to(dt)
+    d["conv_w"] = 0.5 * torch.randn(3, H, dk, 4, generator=gen, device=dev, dtype=f32)
+    d["norm_w"] = torch.rand(dk, generator=gen, device=dev, dtype=f32) + 0.5
+    d["conv_state0"] = (torch.randn(N, 3, 3, H, dk, generator=gen, device=dev, dtype=f32).to(dt)
+                        if conv_state else None)
+    return d

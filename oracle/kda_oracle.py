@@ -343,13 +343,14 @@ def rmsnorm_gated(o, g, w, eps):
 
 
 def fused_forward(q_in, k_in, v_in, conv_w, z, b, A, gate, norm_w, h0=None, conv_state=None,
-                  l2_eps=1e-6, rms_eps=1e-5):
+                  l2_eps=1e-6, rms_eps=1e-5, with_o=False):
     """One sequence through the whole KDA layer between its projections:
     q, k = L2Norm(Swish(ShortConv(.))), v = Swish(ShortConv(.)), the
     recurrence, then Sigmoid(gate) * RMSNorm(o).
     q_in, k_in, v_in, gate [T, H, d]; conv_w [3, H, d, 4] (q, k, v taps);
     conv_state [3, 3, H, d] or None (q, k, v histories); norm_w [d].
-    Returns (y [T, H, d], S [H, d, d], conv_state_out [3, 3, H, d])."""
+    Returns (y [T, H, d], S [H, d, d], conv_state_out [3, 3, H, d]), and with
+    with_o also the core's output o [T, H, d] before the gate."""
     conv_w = _f64(conv_w)
     cs = [None] * 3 if conv_state is None else [_f64(conv_state)[i] for i in range(3)]
     qc, sq = short_conv(q_in, conv_w[0], cs[0])
@@ -359,4 +360,6 @@ def fused_forward(q_in, k_in, v_in, conv_w, z, b, A, gate, norm_w, h0=None, conv
     k = l2norm(silu(kc), l2_eps)
     v = silu(vc)
     o, S = recurrence(q, k, v, z, b, A, h0)
-    return rmsnorm_gated(o, gate, norm_w, rms_eps), S, np.stack([sq, sk, sv])
+    y = rmsnorm_gated(o, gate, norm_w, rms_eps)
+    cs_out = np.stack([sq, sk, sv])
+    return (y, S, cs_out, o) if with_o else (y, S, cs_out)

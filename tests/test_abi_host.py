@@ -142,3 +142,43 @@ def test_recurrent_fold_rejects_bad_arguments(L):
     assert fn(*([FAKE] * 5 + [None, FAKE]), 4, 7, 2, 128, 128, 1, None) == 1   # n_accept missing
     assert fn(*([None] * 7), 0, 7, 2, 128, 128, 1, None) == 0    # N = 0 is a no-op
     assert fn(*([None] * 7), 4, 0, 2, 128, 128, 1, None) == 0    # an empty window is a no-op
+
+
+def test_layer_entry_points_reject_bad_arguments(L):
+    fl = ctypes.c_float
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fwd = L.kda_layer_fwd
+    fwd.restype = i
+    fwd.argtypes = [vp] * 13 + [fl, fl] + [i] * 7 + [vp, vp, vp, sz, vp]
+
+    def call(**kw):
+        a = dict(ptrs=[FAKE] * 13, l2=1e-6, rms=1e-5, B=1, T=64, H=2, d=16, N=1, chunk=16,
+                 dtype=0, y=FAKE, hT=None, ws=FAKE, wsb=1 << 40, stream=None)
+        a.update(kw)
+        p = list(a["ptrs"])
+        for idx, val in a.get("set", {}).items():
+            p[idx] = val
+        return fwd(*p, a["l2"], a["rms"], a["B"], a["T"], a["H"], a["d"], a["N"], a["chunk"],
+                   a["dtype"], a["y"], a["hT"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(l2=-1.0) == 1
+    assert call(rms=float("nan")) == 1
+    assert call(d=96) == 2
+    assert call(chunk=32) == 2
+    assert call(set={3: None}) == 1                     # conv_w missing
+    assert call(set={12: None}) == 1                    # norm_w missing
+    assert call(set={11: None}) == 1                    # gate missing
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
+    L.kda_layer_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    assert L.kda_layer_fwd_workspace_bytes(1, 64, 2, 16, 1, 16, 0) > \
+        L.kda_chunk_fwd_workspace_bytes(1, 64, 2, 16, 16, 1, 16, 0)
+    step = L.kda_layer_step
+    step.restype = i
+    step.argtypes = [vp] * 11 + [fl, fl, vp] + [i] * 4 + [vp]
+    ok = [FAKE] * 11
+    assert step(*ok, 1e-6, 1e-5, FAKE, 4, 2, 96, 1, None) == 2
+    assert step(*ok, -1.0, 1e-5, FAKE, 4, 2, 128, 1, None) == 1
+    assert step(*([FAKE] * 4 + [None] + [FAKE] * 6), 1e-6, 1e-5, FAKE, 4, 2, 128, 1, None) == 1
+    assert step(*([None] * 11), 1e-6, 1e-5, None, 0, 2, 128, 1, None) == 0
