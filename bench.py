@@ -259,6 +259,71 @@ def bench_fold(args, kda, torch, run, step_ms):
     }
 
 
+def bench_layer(args, kda, torch, KI, call_ms, step_ms):
+    """The layer entry points (short convolution, Swish and L2Norm before the
+    core, gated RMSNorm after) on the long_1m and decode_256 shapes, against
+    the core-only calls measured above."""
+    dev = torch.device("cuda:0")
+    case = KI.CONFIGS["long_1m"]
+    d = KI.make_layer(case, device=dev, seed=0)
+    B, T, H, dk, N, C = d["B"], d["T"], d["H"], d["dk"], d["N"], d["chunk"]
+    ws = torch.empty(kda.kda_layer_fwd_workspace_bytes(B, T, H, dk, N, C, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        return kda.kda_layer_fwd(d["q_in"], d["k_in"], d["v_in"], d["conv_w"], d["z"], d["b"],
+                                 d["A"], d["gate"], d["norm_w"], initial_state=d["h0"],
+                                 conv_state=d["conv_state0"], chunk_size=C, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(2, args.steps // 2)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in times) / len(times)
+    del d, ws
+    torch.cuda.empty_cache()
+    # fused decode launch on the decode workload's shapes
+    dc = KI.CONFIGS["decode_256"]
+    lc = KI.PrefillCase("decode_layer", H=dc.H, dk=dc.dk, dv=dc.dv, chunk=64, dtype=dc.dtype,
+                        B=dc.N, zero_h0=False)
+    x = KI.make_layer(lc, device=dev, seed=0, T=1)
+    tok = {k: x[k][:, 0].contiguous() for k in ("q_in", "k_in", "v_in", "gate", "z", "b")}
+    st, cs = x["h0"].clone(), x["conv_state0"].clone()
+
+    def step():
+        return kda.kda_layer_step(tok["q_in"], tok["k_in"], tok["v_in"], x["conv_w"], cs, tok["z"],
+                                  tok["b"], x["A"], st, tok["gate"], x["norm_w"])
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    stimes = []
+    for _ in range(16 * args.decode_reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        stimes.append((a, b))
+    torch.cuda.synchronize()
+    sms = sum(a.elapsed_time(b) for a, b in stimes) / len(stimes)
+    return {
+        "workload": "long_1m and decode_256 shapes with projections, convolution taps, "
+                    "carried convolution states, output-gate logits and RMSNorm weight",
+        "prefill_ms_per_call": round(ms, 4),
+        "prefill_tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "prefill_vs_core_call": round(ms / call_ms, 3),
+        "decode_ms_per_step": round(sms, 4),
+        "decode_tokens_per_s": round(dc.N / (sms * 1e-3), 1),
+        "decode_vs_core_step": round(sms / step_ms, 3),
+    }
+
+
 def cpu_baseline(inp, torch):
     import oracle
     n = inp["q"].shape[1]
@@ -280,6 +345,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer entry points (convolution and gated RMSNorm around the core)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before timing (a known-size "
                          "kernel for calibrating the HBM traffic counters)")
@@ -308,6 +375,10 @@ def main():
 
     value, ms, roof, extra, cpu_inp = bench_prefill(args, kda, torch, KI)
     dec = None if args.no_decode else bench_decode(args, kda, torch, KI)
+    layer = None
+    if not args.no_layer:
+        layer = bench_layer(args, kda, torch, KI, extra["call_ms_events"],
+                            dec["ms_per_step_mean"] if dec else float("nan"))
     cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_inp, torch)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -317,7 +388,7 @@ def main():
         "config": {"workload": "long_1m: B=1, H=12, T=1048576, d_k=d_v=128, chunk=64, bf16 "
                                "q/k/v, fp32 logits and state, seed 0",
                    "B": 1, "T": 1 << 20, "H": 12, "dk": 128, "dv": 128, "chunk": 64},
-        "roofline": roof, "cpu_baseline": cpu, "prefill": extra, "decode": dec,
+        "roofline": roof, "cpu_baseline": cpu, "prefill": extra, "decode": dec, "layer": layer,
     }
     print(json.dumps(line), flush=True)
 

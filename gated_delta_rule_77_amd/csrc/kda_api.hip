@@ -24,7 +24,9 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
                          int B, int T, int H, int dk, int dv, int N, int chunk,
                          kda_dtype_t dtype, void* o, float* hT, void* ws, size_t ws_bytes,
                          float* dbg_intra, float* dbg_state, hipEvent_t* ev, int n_ev,
-                         void* stream) {
+                         void* stream, const void* gate = nullptr, const float* norm_w = nullptr,
+                         float rms_eps = 0.f, const float* conv_w = nullptr,
+                         const void* conv_state0 = nullptr, float l2_eps = 0.f) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
     if (cu) {
@@ -50,6 +52,12 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     a.dbg_intra = dbg_intra; a.dbg_state = dbg_state; a.ev = ev;
     a.ev5 = (ev && n_ev >= 6) ? ev + 4 : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
+    a.gate = fast ? gate : nullptr;
+    a.norm_w = norm_w;
+    a.rms_eps = rms_eps;
+    a.conv_w = fast ? conv_w : nullptr;
+    a.conv_state0 = conv_state0;
+    a.l2_eps = l2_eps;
     hipError_t e = ev ? hipEventRecord(ev[0], a.stream) : hipSuccess;
     if (e == hipSuccess) e = launch_prep(a);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], a.stream);
@@ -208,17 +216,27 @@ kda_status_t kda_layer_fwd(const void* q_in, const void* k_in, const void* v_in,
     const int bf = dtype == KDA_BF16;
     const int Ttot = (int)tokens;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_layer_pre(q_in, k_in, v_in, conv_w, conv_state0, cu_seqlens, N, T, Ttot, H,
-                                    d, l2_eps, qw, kw, vw, bf, s);
+    // The MFMA path runs the steps before the core in its intra kernel and the
+    // output gate in its output kernel; the fp32 path runs them as passes of
+    // their own around the core.
+    const bool fused = use_fast_path(d, d, chunk, bf);
+    hipError_t e = hipSuccess;
+    if (!fused)
+        e = launch_layer_pre(q_in, k_in, v_in, conv_w, conv_state0, cu_seqlens, N, T, Ttot, H, d,
+                             l2_eps, qw, kw, vw, bf, s);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    const kda_status_t st =
+        fused ? run_prefill(q_in, k_in, v_in, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, d,
+                            d, N, chunk, dtype, y, hT, ws, W.core, nullptr, nullptr, nullptr, 0,
+                            stream, gate, norm_w, rms_eps, conv_w, conv_state0, l2_eps)
+              : run_prefill(qw, kw, vw, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, d, d, N,
+                            chunk, dtype, ow, hT, ws, W.core, nullptr, nullptr, nullptr, 0, stream);
+    if (st != KDA_OK) return st;
+    if (!fused) e = launch_layer_post(ow, gate, norm_w, rms_eps, tokens * H, d, y, bf, s);
+    // after the core: conv_stateT may be conv_state0, which the intra kernel reads
     if (e == hipSuccess && conv_stateT)
         e = launch_layer_convstate(q_in, k_in, v_in, conv_state0, cu_seqlens, N, T, Ttot, H, d,
                                    conv_stateT, bf, s);
-    if (e != hipSuccess) return KDA_ERR_HIP;
-    const kda_status_t st = run_prefill(qw, kw, vw, g_logits, beta_logits, A, h0, cu_seqlens, B, T,
-                                        H, d, d, N, chunk, dtype, ow, hT, ws, W.core, nullptr,
-                                        nullptr, nullptr, 0, stream);
-    if (st != KDA_OK) return st;
-    e = launch_layer_post(ow, gate, norm_w, rms_eps, tokens * H, d, y, bf, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

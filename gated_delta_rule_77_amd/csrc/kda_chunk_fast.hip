@@ -100,13 +100,20 @@ __device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : p < 3 ? 1 : 
 //   A_kk/A_qk tile (r, s):  rows (k|q) . E  with  columns (k . F) . X(r,s)
 //   K . Gamma = (k . E) . Y(r),  Q . Gamma = (q . E) . Y(r),  Kbar = (k . F) . Z(r)
 // (X(r,s) <= 1 off the diagonal, X(r,r) = 2^(L_s - L_e) < e^80 on it).
-template <bool DBG>
+// With CONV, q, k, v are the layer's projections and step 1 applies the
+// layer's steps before the core ([LA-KDA §5.3]): the depthwise causal
+// convolution (four taps oldest first, the sequence's first three inputs from
+// the carried state cs0 or zeros), Swish, and for q and k the L2Norm over the
+// head's 128 channels; the results are rounded to bf16 as the core's inputs.
+template <bool DBG, bool CONV>
 __global__ __launch_bounds__(256, 2)
 void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const float* __restrict__ z,
                        const float* __restrict__ bl, const float* __restrict__ A,
                        const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
-                       int cap, uint8_t* __restrict__ recs, float* __restrict__ dbg)
+                       int cap, uint8_t* __restrict__ recs, float* __restrict__ dbg,
+                       const float* __restrict__ conv_w, const bf16* __restrict__ cs0,
+                       float l2_eps)
 {
     const int cid = blockIdx.x / H, h = blockIdx.x % H;   // heads fastest: whole input rows
     if (cid >= hdr[0]) return;
@@ -136,12 +143,68 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // ---- 1. loads: q, k, v rows straight to registers (each element used by
     //      one lane); gate [LA-KDA §5.4] and in-chunk cumulative sum in log2 units
     uint4 kr[4], qr[4], vr[4];
+    float qkf[2][4][8];              // CONV: q, k after Swish, before the L2Norm
+    float* sL2 = reinterpret_cast<float*>(smem + kOffRK);   // CONV: [2][64 rows][4 waves], free in step 1
+    if constexpr (!CONV) {
 #pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-        const unsigned off = roff(16 * tt + n16) + cw;
-        kr[tt] = *reinterpret_cast<const uint4*>(k + base + off);
-        qr[tt] = *reinterpret_cast<const uint4*>(q + base + off);
-        vr[tt] = *reinterpret_cast<const uint4*>(v + base + off);
+        for (int tt = 0; tt < 4; tt++) {
+            const unsigned off = roff(16 * tt + n16) + cw;
+            kr[tt] = *reinterpret_cast<const uint4*>(k + base + off);
+            qr[tt] = *reinterpret_cast<const uint4*>(q + base + off);
+            vr[tt] = *reinterpret_cast<const uint4*>(v + base + off);
+        }
+    } else {
+        const int n = cd.x, p0 = cd.w;       // sequence, position of row 0 within it
+        const uint4 zero16 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int X = 0; X < 3; X++) {
+            const bf16* xin = X == 0 ? q : X == 1 ? k : v;
+            float wt[8][4];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float4 w4 = *reinterpret_cast<const float4*>(conv_w + (((size_t)X * H + h) * 128 + cw + e) * 4);
+                wt[e][0] = w4.x; wt[e][1] = w4.y; wt[e][2] = w4.z; wt[e][3] = w4.w;
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++) {
+                const int r = min(16 * tt + n16, lastrow);
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) y[e] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int src = p0 + r - 3 + j;        // position in the sequence
+                    uint4 raw;
+                    if (src >= 0)
+                        raw = *reinterpret_cast<const uint4*>(xin + ((size_t)(tok0 + r - 3 + j) * H + h) * 128 + cw);
+                    else
+                        raw = cs0 ? *reinterpret_cast<const uint4*>(
+                                        cs0 + ((((size_t)n * 3 + X) * 3 + (3 + src)) * H + h) * 128 + cw)
+                                  : zero16;
+                    const bf16x8 xv = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) y[e] = __builtin_fmaf(wt[e][j], (float)xv[e], y[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; e++) y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + ex2(-y[e] * kLog2e));
+                if (X == 2) {
+                    bf16x8 o8;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) o8[e] = (bf16)y[e];
+                    vr[tt] = __builtin_bit_cast(uint4, o8);
+                } else {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        qkf[X][tt][e] = y[e];
+                        ss = __builtin_fmaf(y[e], y[e], ss);
+                    }
+                    ss += __shfl_xor(ss, 16, 64);      // the 4 lanes of this row in the wave
+                    ss += __shfl_xor(ss, 32, 64);
+                    if (g4 == 0) sL2[(X * 64 + 16 * tt + n16) * 4 + w] = ss;
+                }
+            }
+        }
     }
     const int c = tid & 127, half = tid >> 7;
     float lr[32];
@@ -166,6 +229,19 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
     }
     __syncthreads();
+    if constexpr (CONV) {
+#pragma unroll
+        for (int X = 0; X < 2; X++)
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++) {
+                const float4 p4 = *reinterpret_cast<const float4*>(sL2 + (X * 64 + 16 * tt + n16) * 4);
+                const float inv = 1.f / sqrtf(((p4.x + p4.y) + (p4.z + p4.w)) + l2_eps);
+                bf16x8 o8;
+#pragma unroll
+                for (int e = 0; e < 8; e++) o8[e] = (bf16)(qkf[X][tt][e] * inv);
+                (X == 0 ? qr : kr)[tt] = __builtin_bit_cast(uint4, o8);
+            }
+    }
     // second half: add L at row 31; per-channel factors
     {
         float* F = sFac + c;
@@ -491,12 +567,22 @@ __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __res
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
 }
 
+// Output-gate epilogue of the layer entry point ([LA-KDA §5.5]): each stored
+// row becomes Sigmoid(gate) * RMSNorm(o) with the row's RMS over its 128
+// channels (16 lanes of 8 channels each).
+struct OutGate {
+    const bf16* gate;         // [tokens, H, 128] logits, or null for the plain output
+    float w[8];               // RMSNorm weights of this lane's 8 channels
+    float eps;
+};
+
 // One chunk for one wave over all slices.
-template <bool DBG>
+template <bool DBG, bool GATE>
 __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, int len,
                                          f32x4 (&accS)[kOutNS][2], bf16* sS, bf16* sVt, bf16* sO,
                                          bf16* __restrict__ o, float* __restrict__ dbgS, int H,
-                                         int h, int w, int lane, int n16, int g4, int tid) {
+                                         int h, int w, int lane, int n16, int g4, int tid,
+                                         const OutGate& og) {
     if (DBG) {
 #pragma unroll
         for (int sl = 0; sl < kOutNS; sl++)
@@ -560,19 +646,41 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-        if (row < len)
-            *reinterpret_cast<uint4*>(o + ((size_t)(tok0 + row) * H + h) * 128 + c8) =
-                *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
+        const size_t off = ((size_t)(tok0 + row) * H + h) * 128 + c8;
+        if constexpr (GATE) {
+            const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + row * kLdO + c8);
+            float ov[8], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                ov[e] = (float)ob[e];
+                ss = __builtin_fmaf(ov[e], ov[e], ss);
+            }
+#pragma unroll
+            for (int m = 8; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);   // the row's 16 lanes
+            const float r = 1.f / sqrtf(ss * (1.f / 128.f) + og.eps);
+            if (row < len) {
+                const bf16x8 gt = *reinterpret_cast<const bf16x8*>(og.gate + off);
+                bf16x8 yv;
+#pragma unroll
+                for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
+                *reinterpret_cast<bf16x8*>(o + off) = yv;
+            }
+        } else {
+            if (row < len)
+                *reinterpret_cast<uint4*>(o + off) = *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
+        }
     }
 }
 
-// grid: seg_cap * H blocks, block = (segment, head)
-template <bool DBG>
+// grid: seg_cap * H blocks, block = (segment, head).  With GATE the rows
+// stored are the layer's gated RMSNorm of O instead of O.
+template <bool DBG, bool GATE>
 __global__ __launch_bounds__(256, 1)
 void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
                     const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
                     const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
-                    bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS)
+                    bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS,
+                    const bf16* __restrict__ gate, const float* __restrict__ norm_w, float rms_eps)
 {
     const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
     if (seg_id >= hdr[1]) return;
@@ -606,6 +714,12 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
         seg_len = lastc.y + lastc.z - first.y;
     }
 
+    OutGate og;
+    og.gate = gate;
+    og.eps = rms_eps;
+#pragma unroll
+    for (int e = 0; e < 8; e++) og.w[e] = GATE ? norm_w[(tid & 15) * 8 + e] : 0.f;
+
     constexpr int D = kOutDepth;
     auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
     OutFrags F[D];
@@ -621,16 +735,16 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
             // unconditional prefetch (index clamped) keeps the wait counts exact
             load_out_frags(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
             const int t0 = (ci + u) * C;
-            out_step<DBG>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o, dbgS,
-                          H, h, w, lane, n16, g4, tid);
+            out_step<DBG, GATE>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
+                                dbgS, H, h, w, lane, n16, g4, tid, og);
         }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            out_step<DBG>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
-                          dbgS, H, h, w, lane, n16, g4, tid);
+            out_step<DBG, GATE>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
+                                o, dbgS, H, h, w, lane, n16, g4, tid, og);
         }
 
     if (last && hT) {
@@ -892,14 +1006,19 @@ hipError_t launch_fast(const ChunkArgs& a) {
     float* sstart = reinterpret_cast<float*>(a.ws + a.L.off_sstart);
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
     const dim3 gi((unsigned)((long long)a.L.cap * a.H));
+    const bf16* cs0 = static_cast<const bf16*>(a.conv_state0);
     if (a.dbg_intra)
-        hipLaunchKernelGGL(fast_intra_kernel<true>, gi, dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((fast_intra_kernel<true, false>), gi, dim3(256), 0, a.stream,
                            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, a.L.cap, recs, a.dbg_intra);
+                           hdr, chunks, a.H, a.L.cap, recs, a.dbg_intra, a.conv_w, cs0, a.l2_eps);
+    else if (a.conv_w)
+        hipLaunchKernelGGL((fast_intra_kernel<false, true>), gi, dim3(256), 0, a.stream,
+                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
+                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr, a.conv_w, cs0, a.l2_eps);
     else
-        hipLaunchKernelGGL(fast_intra_kernel<false>, gi, dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((fast_intra_kernel<false, false>), gi, dim3(256), 0, a.stream,
                            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr);
+                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr, a.conv_w, cs0, a.l2_eps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
@@ -915,14 +1034,22 @@ hipError_t launch_fast(const ChunkArgs& a) {
                        seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
+    const bf16* gate = static_cast<const bf16*>(a.gate);
     if (a.dbg_state)
-        hipLaunchKernelGGL(seg_out_kernel<true>, gc, dim3(256), 0, a.stream, (const uint8_t*)recs,
-                           chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, (bf16*)a.o, a.hT,
-                           a.dbg_state);
+        hipLaunchKernelGGL((seg_out_kernel<true, false>), gc, dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
+                           (const float*)sstart, (bf16*)a.o, a.hT, a.dbg_state, gate, a.norm_w,
+                           a.rms_eps);
+    else if (gate)
+        hipLaunchKernelGGL((seg_out_kernel<false, true>), gc, dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
+                           (const float*)sstart, (bf16*)a.o, a.hT, (float*)nullptr, gate, a.norm_w,
+                           a.rms_eps);
     else
-        hipLaunchKernelGGL(seg_out_kernel<false>, gc, dim3(256), 0, a.stream, (const uint8_t*)recs,
-                           chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, (bf16*)a.o, a.hT,
-                           (float*)nullptr);
+        hipLaunchKernelGGL((seg_out_kernel<false, false>), gc, dim3(256), 0, a.stream,
+                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
+                           (const float*)sstart, (bf16*)a.o, a.hT, (float*)nullptr, gate, a.norm_w,
+                           a.rms_eps);
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ namespace kda {
 // ---------------------------------------------------------------- workspace
 //
 // [0, 256)                 header: int32 total number of chunks
-// chunk table              cap x int4 (sequence, first token, length, 0)
+// chunk table              cap x int4 (sequence, first token, length, position in sequence)
 // sequence table           N x int2  (first chunk id, number of chunks)
 // chunk records            cap x H records of rec_bytes each (MFMA path: head
 //                          major, so one head's chunks are contiguous)
@@ -71,7 +71,7 @@ inline int pick_seg_chunks(int cap, int H) {
 
 // Workspace layout (all offsets 256-byte aligned):
 // [0, 256)   header: int32 total chunks, int32 total segments
-// chunks     cap x int4 (sequence, first token, length, 0)
+// chunks     cap x int4 (sequence, first token, length, position in sequence)
 // seqs       N x int2 (first chunk id, number of chunks)
 // seqsegs    N x int2 (first segment id, number of segments)      [MFMA path]
 // segs       seg_cap x int4 (sequence, first chunk id, chunks, index in sequence)
@@ -108,6 +108,11 @@ struct ChunkArgs {
     hipEvent_t* ev;            // 4 events recorded around the kernels, or null
     hipEvent_t* ev5;           // 2 more: after the transition and compose phases, or null
     hipStream_t stream;
+    // MFMA path only: with a gate, o receives the layer's Sigmoid(gate) * RMSNorm(o);
+    // with conv_w, q, k, v are the layer's projections (convolution, Swish and
+    // L2Norm applied in the intra kernel)
+    const void* gate; const float* norm_w; float rms_eps;
+    const float* conv_w; const void* conv_state0; float l2_eps;
 };
 
 // launchers (return hipError_t of the launches)

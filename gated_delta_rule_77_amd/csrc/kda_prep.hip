@@ -103,7 +103,8 @@ void prep_seg_kernel(int N, int seg_chunks, int seg_cap, const int* __restrict__
 }
 
 // One thread per chunk slot: locate the owning sequence by binary search
-// over the first-chunk ids and record (sequence, first token, length).
+// over the first-chunk ids and record (sequence, first token, length,
+// position of the first token within the sequence).
 __global__ __launch_bounds__(256)
 void prep_chunk_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
                        const int* __restrict__ hdr, const int2* __restrict__ seqs,
@@ -123,7 +124,7 @@ void prep_chunk_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, in
     int start, len;
     seq_extent(cu, lo, Tfix, Ttot, start, len);
     const int j = c - seqs[lo].x;
-    chunks[c] = make_int4(lo, start + j * C, min(C, len - j * C), 0);
+    chunks[c] = make_int4(lo, start + j * C, min(C, len - j * C), j * C);
 }
 
 hipError_t launch_prep(const ChunkArgs& a) {
