@@ -761,115 +761,88 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 
 // Transition launch: one workgroup of 8 waves per (segment, head) carries the
 // whole augmented state [R | M], 256 columns = 16 slices (R in slices 0..7,
-// M in 8..15), so each chunk's fixed cost (two barriers, LDS round trips)
-// is paid once for all columns; two waves per SIMD hide each other's MFMA
-// and LDS latencies.
-//   V~ phase:    wave (tb = w & 3, q = w >> 2) forms V~ rows [16tb, 16tb + 16)
-//                of R slices [4q, 4q + 4) and M slices [8 + 4q, 12 + 4q)
-//   state phase: wave w owns state rows [16w, 16w + 16) of all 16 slices (one
-//                C tile per slice), the half k-step fragment (w >> 1, w & 1)
-//                of the bf16 copy of S
-constexpr int kTS = 16;     // slices of [R | M]
+// M in 8..15).  Columns evolve independently, so wave w owns the 32 columns of
+// slices 2w and 2w + 1 for all 128 rows (8 row tiles x 2 slices of fp32 C
+// tiles): its S fragments for V~ = U - W S and its V~ fragments for the state
+// update come from its own registers (two stacked C tiles are exactly one
+// operand fragment).  Only the chunk's W, Kbar, U and gamma_C are shared: the
+// workgroup copies them into a double-buffered LDS stage, two chunks ahead
+// through registers, with one barrier per chunk.
+constexpr int kTS = 16;                          // slices of [R | M]
+constexpr int kStW = 0, kStK = 16384, kStU = 32768, kStG = 49152;
+constexpr int kStageBytes = 49664;               // W, Kbar, U fragments and gamma_C of one chunk
 
-struct TransFrags {
-    bf16x8 w[4];      // -W^T, token block w & 3, k-steps 0..3
-    bf16x8 k[2];      // Kbar^T rows [16w, 16w + 16), token k-steps 0..1
-    bf16x4 u[4];      // U tiles of R slices 4q .. 4q + 3, token block w & 3
-    float4 g;         // gamma_C of rows 16w + 4g .. 16w + 4g + 3
+// the 16-byte pieces of a record's W, Kbar, U and gamma_C that thread t copies
+typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
+struct StageRegs {
+    u32x4 w0, w1, k0, k1, u0, u1, g;
 };
 
-__device__ __forceinline__ void load_trans_frags(TransFrags& f, const uint8_t* __restrict__ rec,
-                                                 int w, int lane, int g4) {
-    const int tb = w & 3, q = w >> 2;
+__device__ __forceinline__ StageRegs stage_load(const uint8_t* __restrict__ rec, int t) {
+    auto ld = [&](int off) { return *reinterpret_cast<const u32x4*>(rec + off + t * 16); };
+    StageRegs r;
+    r.w0 = ld(REC_W); r.w1 = ld(REC_W + 8192);
+    r.k0 = ld(REC_K); r.k1 = ld(REC_K + 8192);
+    r.u0 = ld(REC_U); r.u1 = ld(REC_U + 8192);
+    r.g = *reinterpret_cast<const u32x4*>(rec + REC_G + (t & 31) * 16);
+    return r;
+}
+
+__device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int t) {
+    auto stv = [&](int off, u32x4 x) { *reinterpret_cast<u32x4*>(st + off + t * 16) = x; };
+    stv(kStW, r.w0); stv(kStW + 8192, r.w1);
+    stv(kStK, r.k0); stv(kStK + 8192, r.k1);
+    stv(kStU, r.u0); stv(kStU + 8192, r.u1);
+    if (t < 32) *reinterpret_cast<u32x4*>(st + kStG + t * 16) = r.g;
+}
+
+// One chunk for wave w from the staged record.
+__device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2], int w, int lane,
+                                            int g4) {
+    // S fragments of k-step ks: row tiles 2ks, 2ks + 1 of each owned slice
+    bf16x8 sf[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
-        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((tb * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < 2; j++) sf[ks][j] = pack_frag(acc[2 * ks][j], acc[2 * ks + 1][j]);
+    // V~ = U - W S for the 4 token blocks of the owned slices (U = 0 for M)
+    f32x4 vt[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            vt[tb][j] = zero4();
+            if (w < 4)
+                vt[tb][j] = unpack4(*reinterpret_cast<const bf16x4*>(
+                    st + kStU + (((2 * w + j) * 4 + tb) * 64 + lane) * 8));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + kStW + ((tb * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+            for (int j = 0; j < 2; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
+        }
+    }
+    // V~ fragments over tokens, then S <- Diag(gamma_C) S + Kbar^T V~
+    bf16x8 vf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
-        f.k[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 2 + kb) * 64 + lane) * 16);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; s4++)
-        f.u[s4] = *reinterpret_cast<const bf16x4*>(rec + REC_U + (((4 * q + s4) * 4 + tb) * 64 + lane) * 8);
-    f.g = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(rec + REC_G) + 16 * w + 4 * g4);
-}
-
-__device__ __forceinline__ void trans_step(const TransFrags& f, f32x4 (&acc)[kTS], bf16* sS,
-                                           bf16* sVt, int w, int lane) {
-    const int tb = w & 3, q = w >> 2;
-    // two slices at a time, so that two independent MFMA chains interleave
+        for (int j = 0; j < 2; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
+    const float* gC = reinterpret_cast<const float*>(st + kStG);
 #pragma unroll
-    for (int jj = 0; jj < 8; jj += 2) {
-        int sl[2];
-        bf16x8 sf[2][4];
-        f32x4 v[2];
+    for (int rt = 0; rt < 8; rt++) {
+        const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(st + kStK + ((rt * 2 + 0) * 64 + lane) * 16);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(st + kStK + ((rt * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int j = jj + t;
-            sl[t] = j < 4 ? 4 * q + j : 8 + 4 * q + (j - 4);
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++)
-                sf[t][ks] = *reinterpret_cast<const bf16x8*>(sS + ((sl[t] * 4 + ks) * 64 + lane) * 8);
-            v[t] = j < 4 ? unpack4(f.u[j & 3]) : zero4();
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-            for (int t = 0; t < 2; t++) v[t] = mfma_bf16(f.w[ks], sf[t][ks], v[t]);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-            *reinterpret_cast<bf16x4*>(sVt + ((sl[t] * 4 + tb) * 64 + lane) * 4) = pack4(v[t]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s0 = 0; s0 < kTS; s0 += 2) {
-        bf16x8 vfr[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-                vfr[t][kb] = concat44(
-                    *reinterpret_cast<const bf16x4*>(sVt + (((s0 + t) * 4 + 2 * kb) * 64 + lane) * 4),
-                    *reinterpret_cast<const bf16x4*>(sVt + (((s0 + t) * 4 + 2 * kb + 1) * 64 + lane) * 4));
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            f32x4& s = acc[s0 + t];
-            s[0] *= f.g.x; s[1] *= f.g.y; s[2] *= f.g.z; s[3] *= f.g.w;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int t = 0; t < 2; t++) acc[s0 + t] = mfma_bf16(f.k[kb], vfr[t][kb], acc[s0 + t]);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-            *reinterpret_cast<bf16x4*>(sS + (((s0 + t) * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) =
-                pack4(acc[s0 + t]);
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ void run_trans(const uint8_t* __restrict__ recs, int c0, int nch, int H,
-                                          int h, f32x4 (&acc)[kTS], bf16* sS, bf16* sVt, int w,
-                                          int lane, int g4) {
-    constexpr int D = 3;
-    auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
-    TransFrags F[D];
-    if (nch > 0) {
-#pragma unroll
-        for (int u = 0; u < D - 1; u++) load_trans_frags(F[u], rec(min(u, nch - 1)), w, lane, g4);
-    }
-    __syncthreads();
-    const int nfull = nch / D * D;
-    for (int ci = 0; ci < nfull; ci += D) {
-#pragma unroll
-        for (int u = 0; u < D; u++) {
-            // unconditional prefetch (index clamped) keeps the wait counts exact
-            load_trans_frags(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
-            trans_step(F[u], acc, sS, sVt, w, lane);
+        for (int j = 0; j < 2; j++) {
+            f32x4& a = acc[rt][j];
+            a[0] *= g.x; a[1] *= g.y; a[2] *= g.z; a[3] *= g.w;
+            a = mfma_bf16(k0, vf[0][j], a);
+            a = mfma_bf16(k1, vf[1][j], a);
         }
     }
-#pragma unroll
-    for (int u = 0; u < D - 1; u++)
-        if (nfull + u < nch) trans_step(F[u], acc, sS, sVt, w, lane);
 }
 
 // grid: seg_cap * H blocks, block = (segment, head)
@@ -883,31 +856,53 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
     const int2 ss = seqsegs[sg.x];
     if (sg.w == ss.y - 1) return;          // the last segment's transition is never needed
+    const int c0 = sg.y, nch = sg.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
 
-    __shared__ __align__(16) bf16 sS[kTS * 4 * 64 * 8];
-    __shared__ __align__(16) bf16 sVt[kTS * 4 * 64 * 4];
+    __shared__ __align__(16) uint8_t stage[2][kStageBytes];
 
-    f32x4 acc[kTS];     // R from 0, M from the identity
+    f32x4 acc[8][2];        // R from 0, M from the identity
 #pragma unroll
-    for (int sl = 0; sl < kTS; sl++) {
+    for (int rt = 0; rt < 8; rt++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 16 * w + 4 * g4 + e, col = 16 * sl + n16;
-            acc[sl][e] = (row == col - 128) ? 1.f : 0.f;
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * (2 * w + j) + n16;
+                acc[rt][j][e] = (row == col - 128) ? 1.f : 0.f;
+            }
+    if (nch > 0) {
+        auto rec = [&](int c) { return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * REC_BYTES; };
+        // chunk c sits in stage c & 1; its copy passes through register set c & 1
+        StageRegs R0 = stage_load(rec(0), tid);
+        StageRegs R1 = stage_load(rec(1), tid);
+        stage_store(R0, stage[0], tid);
+        R0 = stage_load(rec(2), tid);
+        __syncthreads();
+        int c = 0;
+        for (; c + 2 <= nch; c += 2) {
+            trans_chunk(stage[0], acc, w, lane, g4);
+            stage_store(R1, stage[1], tid);          // chunk c + 1
+            R1 = stage_load(rec(c + 3), tid);
+            __syncthreads();
+            trans_chunk(stage[1], acc, w, lane, g4);
+            stage_store(R0, stage[0], tid);          // chunk c + 2
+            R0 = stage_load(rec(c + 4), tid);
+            __syncthreads();
         }
-        *reinterpret_cast<bf16x4*>(sS + ((sl * 4 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) = pack4(acc[sl]);
+        if (c < nch) trans_chunk(stage[0], acc, w, lane, g4);
     }
-    run_trans(recs, sg.y, sg.z, H, h, acc, sS, sVt, w, lane, g4);
 #pragma unroll
-    for (int sl = 0; sl < kTS; sl++)
+    for (int rt = 0; rt < 8; rt++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 16 * w + 4 * g4 + e, col = 16 * sl + n16;
-            rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = acc[sl][e];
-        }
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * (2 * w + j) + n16;
+                rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = acc[rt][j][e];
+            }
 }
 
 // Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and

@@ -516,3 +516,27 @@ def test_fold_decode_workload_window(kda):
         r = oracle.replay_fold(win["k"][n:n + 1], win["v"][n:n + 1], win["z"][n:n + 1],
                                win["b"][n:n + 1], run["A"], run["state"][n:n + 1], [int(n_acc[n])])
         assert rel_err(folded[n], r[0]) <= TOL_F32
+
+
+# ------------------------------------------------------ segment layouts
+
+@pytest.mark.parametrize("B,T,H,heads", [(1, 8192, 1, [0]), (3, 1500, 5, [0, 4]),
+                                         (1, 4096, 40, [7, 39])])
+def test_segment_layouts_vs_oracle(kda, B, T, H, heads):
+    """The MFMA path cuts every sequence into about 256 / H segments of at
+    least 16 chunks: one head with many segments, several sequences with two
+    segments each, and many heads with few.  Sampled heads of every sequence
+    against the oracle."""
+    case = KI.PrefillCase("seg", H=H, dk=128, dv=128, chunk=64, dtype="bf16", B=B, T=T,
+                          zero_h0=False)
+    d = KI.make_prefill(case, seed=17)
+    o, hT = gpu_prefill(kda, to_dev(d))
+    torch.cuda.synchronize()
+    for bi in range(B):
+        sub = {k: d[k][bi:bi + 1] for k in ("q", "k", "v", "z", "b", "h0")}
+        sub["A"] = d["A"]
+        ro, rS = oracle_prefill(sub, heads=heads)
+        e_o = rel_err(o[bi][:, heads], ro)
+        e_s = rel_err(hT[bi][heads], rS)
+        _report(f"segments B={B} T={T} H={H} seq {bi}", o=e_o, hT=e_s)
+        assert e_o <= TOL_BF16 and e_s <= TOL_BF16
