@@ -40,6 +40,9 @@ Functions:
                                        extended with the decay (derivation in the
                                        design notes); exposes its intermediates
   packed                            -- loops `recurrence` over a cu_seqlens batch
+  recurrence_dplr_general           -- the diagonal-plus-low-rank update with its own
+                                       low-rank pair (a, b) and write key
+  chunkwise_dplr                    -- its chunked form with four C x C matrices
 All arithmetic is float64.  Inputs are converted to float64 exactly as given
 (bf16 tensors are first widened, so the oracle sees the same rounded values
 the GPU sees); nothing is rounded internally.
@@ -90,7 +93,7 @@ def beta_of(b):
     return logistic(_f64(b))
 
 
-def recurrence(q, k, v, z, b, A, h0=None, erase=True):
+def recurrence(q, k, v, z, b, A, h0=None, erase=True, decay=True):
     """Token-by-token KDA over one sequence, all heads at once.
 
     q, k: [T, H, d_k]; v: [T, H, d_v]; z: [T, H, d_k]; b: [T, H]; A: [H];
@@ -99,16 +102,22 @@ def recurrence(q, k, v, z, b, A, h0=None, erase=True):
     Each step follows the update of [K3-NOTES]: the decayed state
     S~ = Diag(alpha_t) S_{t-1}; the prediction v^ = S~^T k_t; the correction
     delta = beta_t (v_t - v^); S_t = S~ + k_t delta^T; o_t = S_t^T q_t.
-    With erase=False the correction is replaced by plain accumulation,
-    S_t = S~ + beta_t k_t v_t^T: the gated linear attention row of the
-    family table in [LA-KDA §4] (with a beta factor), used only by tests.
+    The two switches give the other rows of the family table in [LA-KDA §4]:
+    erase=False replaces the correction by plain accumulation,
+    S_t = S~ + beta_t k_t v_t^T (gated linear attention, here with the write
+    strength beta; the table's row is beta = 1), and decay=False sets
+    alpha = 1 (DeltaNet); with both off it is linear attention.  z and A are
+    not read when decay=False.
     """
-    q, k, v, z, b, A = map(_f64, (q, k, v, z, b, A))
+    q, k, v, b = map(_f64, (q, k, v, b))
     T, H, dk = k.shape
     dv = v.shape[-1]
     S = np.zeros((H, dk, dv)) if h0 is None else _f64(h0).copy()
     o = np.zeros((T, H, dv))
-    alpha = np.exp(gate_log_decay(z, A))          # [T, H, d_k]
+    if decay:
+        alpha = np.exp(gate_log_decay(_f64(z), _f64(A)))   # [T, H, d_k]
+    else:
+        alpha = np.ones((T, H, dk))
     beta = beta_of(b)                             # [T, H]
     for t in range(T):
         S = alpha[t][:, :, None] * S                          # decay
@@ -226,6 +235,104 @@ def chunkwise(q, k, v, z, b, A, h0=None, chunk=16, keep=False):
     return o, S
 
 
+def recurrence_dplr_general(q, k, v, a, bv, z, A, h0=None):
+    """Diagonal-plus-low-rank update with its own low-rank pair, one sequence,
+    all heads: the three steps of [K3-ATTN §2.2] with the rank-1 correction
+    and the write no longer tied to one key,
+        S'  = Diag(alpha_t) S_{t-1}
+        S'' = S' + a_t (b_t^T S')
+        S_t = S'' + k_t v_t^T,          o_t = S_t^T q_t.
+    KDA is the case a = -beta k, b = k with write key beta k ([K3-ATTN §2.2]
+    binds the diagonal and low-rank terms to the same k).  alpha is the KDA
+    gate of z and A ([LA-KDA §5.4]).
+    q, k, a, bv, z: [T, H, d_k]; v: [T, H, d_v]; A: [H]; h0: [H, d_k, d_v] or None.
+    Returns (o [T, H, d_v], S [H, d_k, d_v])."""
+    q, k, v, a, bv, z, A = map(_f64, (q, k, v, a, bv, z, A))
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    S = np.zeros((H, dk, dv)) if h0 is None else _f64(h0).copy()
+    o = np.zeros((T, H, dv))
+    alpha = np.exp(gate_log_decay(z, A))
+    for t in range(T):
+        S1 = alpha[t][:, :, None] * S
+        w = np.einsum("hk,hkv->hv", bv[t], S1)                   # b^T S'
+        S = S1 + a[t][:, :, None] * w[:, None, :] + k[t][:, :, None] * v[t][:, None, :]
+        o[t] = np.einsum("hkv,hk->hv", S, q[t])
+    return o, S
+
+
+def chunkwise_dplr(q, k, v, a, bv, z, A, h0=None, chunk=16, keep=False):
+    """The chunked form of `recurrence_dplr_general`, one sequence, all heads.
+
+    With the unknowns x_i = S'_i^T b_i (the low-rank read of each token) the
+    ansatz S_i = Diag(Gamma_i) S_0 + sum_{j<=i} Diag(Gamma_i / Gamma_j)
+    (a_j x_j^T + k_j v_j^T) solves the recurrence, where G is the in-chunk
+    inclusive cumulative log-decay and Gamma = e^G.  Per chunk, with
+    e_ij = e^{G_i - G_j} per channel:
+        A_ba[i,j] = sum_c b_ic a_jc e_ijc  (j < i)    A_bk[i,j] = sum_c b_ic k_jc e_ijc  (j < i)
+        A_qa[i,j] = sum_c q_ic a_jc e_ijc  (j <= i)   A_qk[i,j] = sum_c q_ic k_jc e_ijc  (j <= i)
+        T = (I - A_ba)^{-1};  Wb = T (B . Gamma);  Ub = T A_bk V
+        X = Wb S_0 + Ub
+        O = (Q . Gamma) S_0 + A_qa X + A_qk V
+        S_C = Diag(Gamma_C) S_0 + (A . e^{G_C - G})^T X + (K . e^{G_C - G})^T V
+    These are the four chunk matrices of the general form; when a and the
+    write key are both multiples of b (KDA) the pairs coincide up to row
+    and column scales and two remain ([K3-ATTN §2.2]).  The derivation is the
+    one of `chunkwise` with a second low-rank vector.  keep=True also
+    returns the per-chunk intermediates."""
+    q, k, v, a, bv, z, A = map(_f64, (q, k, v, a, bv, z, A))
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    S = np.zeros((H, dk, dv)) if h0 is None else _f64(h0).copy()
+    o = np.zeros((T, H, dv))
+    g_all = gate_log_decay(z, A)
+    inter = []
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        n = c1 - c0
+        rec = {}
+        for h in range(H):
+            Q, K, V, Av, Bv = q[c0:c1, h], k[c0:c1, h], v[c0:c1, h], a[c0:c1, h], bv[c0:c1, h]
+            G = np.cumsum(g_all[c0:c1, h], axis=0)
+            D = np.zeros((n, n, dk))
+            for i in range(n):
+                D[i, : i + 1] = np.exp(G[i][None, :] - G[: i + 1])
+            Aba = np.tril(np.einsum("ic,jc,ijc->ij", Bv, Av, D), -1)
+            Abk = np.tril(np.einsum("ic,jc,ijc->ij", Bv, K, D), -1)
+            Aqa = np.tril(np.einsum("ic,jc,ijc->ij", Q, Av, D))
+            Aqk = np.tril(np.einsum("ic,jc,ijc->ij", Q, K, D))
+            Tm = np.linalg.inv(np.eye(n) - Aba)
+            Gam = np.exp(G)
+            Wb = Tm @ (Bv * Gam)
+            Ub = Tm @ (Abk @ V)
+            S0 = S[h].copy()
+            X = Wb @ S0 + Ub
+            o[c0:c1, h] = (Q * Gam) @ S0 + Aqa @ X + Aqk @ V
+            dec = np.exp(G[-1][None, :] - G)
+            S[h] = np.exp(G[-1])[:, None] * S0 + (Av * dec).T @ X + (K * dec).T @ V
+            if keep:
+                rec[h] = dict(G=G, Aba=Aba, Abk=Abk, Aqa=Aqa, Aqk=Aqk, T=Tm, Wb=Wb, Ub=Ub,
+                              S0=S0, X=X, gammaC=np.exp(G[-1]))
+        if keep:
+            inter.append(rec)
+    if keep:
+        return o, S, inter
+    return o, S
+
+
+def decode_step_dplr(q, k, v, a, bv, z, A, state):
+    """One token of `recurrence_dplr_general` for a batch of sequences:
+    q, k, a, bv, z [N, H, d_k]; v [N, H, d_v]; state [N, H, d_k, d_v].
+    Returns (o [N, H, d_v], new state)."""
+    q, k, v, a, bv, z, A, state = map(_f64, (q, k, v, a, bv, z, A, state))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    r = lambda x: x.reshape(1, N * H, x.shape[-1])
+    o, S = recurrence_dplr_general(r(q), r(k), r(v), r(a), r(bv), r(z), np.tile(A, N),
+                                   state.reshape(N * H, dk, dv))
+    return o.reshape(N, H, dv), S.reshape(N, H, dk, dv)
+
+
 def _drop_batch(x, nd):
     x = _f64(x)
     return x[0] if x.ndim == nd + 1 else x
@@ -258,18 +365,20 @@ def packed(q, k, v, z, b, A, h0, cu_seqlens, fn=recurrence, **kw):
     return o, S
 
 
-def decode_step(q, k, v, z, b, A, state):
+def decode_step(q, k, v, z, b, A, state, **kw):
     """One single-token step for a batch of sequences (the recurrent call of
     [K3-NOTES]): q, k [N, H, d_k]; v [N, H, d_v]; z [N, H, d_k]; b [N, H];
     state [N, H, d_k, d_v].  Returns (o [N, H, d_v], new state); the input
-    state is not modified."""
-    q, k, v, z, b, A, state = map(_f64, (q, k, v, z, b, A, state))
+    state is not modified.  Keyword switches go to `recurrence`."""
+    q, k, v, b, state = map(_f64, (q, k, v, b, state))
     N, H, dk = q.shape
     dv = v.shape[2]
+    zz = None if z is None else _f64(z).reshape(1, N * H, dk)
+    AA = None if A is None else np.tile(_f64(A), N)
     # every (sequence, head) pair is an independent one-token recurrence
     o, S = recurrence(q.reshape(1, N * H, dk), k.reshape(1, N * H, dk),
-                      v.reshape(1, N * H, dv), z.reshape(1, N * H, dk),
-                      b.reshape(1, N * H), np.tile(A, N), state.reshape(N * H, dk, dv))
+                      v.reshape(1, N * H, dv), zz, b.reshape(1, N * H), AA,
+                      state.reshape(N * H, dk, dv), **kw)
     return o.reshape(N, H, dv), S.reshape(N, H, dk, dv)
 
 

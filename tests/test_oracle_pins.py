@@ -488,3 +488,155 @@ def test_fused_layer_identity_taps_reduce_to_the_core():
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
     assert np.allclose(S, S_ref, rtol=1e-13, atol=1e-14)
     assert np.allclose(y, o / rms / (1 + np.exp(-gate)), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ family modes
+# The rows of the family table in [LA-KDA §4] as switches of the oracle:
+# decay=False is DeltaNet (alpha = 1), erase=False gated linear attention.
+
+def test_decay_off_is_the_printed_delta_rule(golden_dir):
+    """[LA-KDA §7.4] printed values with decay=False: the gate logits are not
+    read (random z and A give the same S1 = 2.5, S2 = 4.3)."""
+    g = json.load(open(os.path.join(golden_dir, "delta_rule_chunk_c2.json")))
+    beta = np.array(g["beta"])
+    blog = np.log(beta / (1 - beta)).reshape(2, 1)
+    k = np.array(g["k"]).reshape(2, 1, 1)
+    v = np.array(g["v"]).reshape(2, 1, 1)
+    q = np.ones((2, 1, 1))
+    rng = np.random.default_rng(40)
+    o, S = oracle.recurrence(q, k, v, rng.standard_normal((2, 1, 1)), blog,
+                             rng.standard_normal(1), decay=False)
+    assert o[0, 0, 0] == pytest.approx(g["S1"], abs=1e-14)
+    assert o[1, 0, 0] == pytest.approx(g["S2"], abs=1e-14)
+    o2, _ = oracle.recurrence(q, k, v, None, blog, None, decay=False)
+    assert np.array_equal(o, o2)
+
+
+def test_decay_and_erase_off_is_linear_attention(golden_dir):
+    """[LA-KDA §3] printed o3 = 124 with both switches off and beta = 1."""
+    g = json.load(open(os.path.join(golden_dir, "linear_attention_1d.json")))
+    k = np.array([g["k"][0], g["k"][1], 0.0]).reshape(3, 1, 1)
+    v = np.array([g["v"][0], g["v"][1], 0.0]).reshape(3, 1, 1)
+    q = np.array([1.0, 1.0, g["q3"]]).reshape(3, 1, 1)
+    b = np.full((3, 1), BIG)
+    o, _ = oracle.recurrence(q, k, v, None, b, None, erase=False, decay=False)
+    assert o[2, 0, 0] == g["o3"]
+
+
+def test_decay_off_matches_the_deltanet_matrix_recurrence():
+    """[LA-KDA §4] DeltaNet row written as explicit matrices:
+    S_t = (I - beta k k^T) S_{t-1} + beta k v^T, o_t = S_t^T q_t."""
+    rng = np.random.default_rng(41)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 15, 2, 5, 4)
+    o, S = oracle.recurrence(q, k, v, z, b, A, h0, decay=False)
+    beta = 1 / (1 + np.exp(-b))
+    for h in range(2):
+        St = h0[h].copy()
+        for t in range(15):
+            St = (np.eye(5) - beta[t, h] * np.outer(k[t, h], k[t, h])) @ St \
+                + beta[t, h] * np.outer(k[t, h], v[t, h])
+            assert np.allclose(o[t, h], St.T @ q[t, h], atol=1e-13)
+        assert np.allclose(S[h], St, atol=1e-13)
+
+
+# ------------------------------------------------- general DPLR (a != b)
+
+def _dplr_case(rng, T, H, dk, dv):
+    q, k, v, z, b, A, h0 = _rand_case(rng, T, H, dk, dv)
+    ah = rng.standard_normal((T, H, dk))
+    ah /= np.linalg.norm(ah, axis=-1, keepdims=True)
+    bv = ah + 0.5 * rng.standard_normal((T, H, dk)) / np.sqrt(dk)
+    bv /= np.linalg.norm(bv, axis=-1, keepdims=True)
+    a = -(1 / (1 + np.exp(-b)))[..., None] * ah
+    return q, k, v, a, bv, z, A, h0
+
+
+@pytest.mark.parametrize("seed", [42, 43])
+def test_dplr_general_reduces_to_kda(seed):
+    """[K3-ATTN §2.2]: binding both low-rank vectors and the write key to k
+    (a = -beta k, b = k, write key beta k) gives KDA; checked against the
+    delta form of [K3-NOTES] (`recurrence`, pinned above)."""
+    rng = np.random.default_rng(seed)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 21, 2, 6, 4)
+    beta = 1 / (1 + np.exp(-b))
+    o1, S1 = oracle.recurrence(q, k, v, z, b, A, h0)
+    o2, S2 = oracle.recurrence_dplr_general(q, beta[..., None] * k, v, -beta[..., None] * k, k,
+                                            z, A, h0)
+    assert np.allclose(o2, o1, atol=1e-13) and np.allclose(S2, S1, atol=1e-13)
+
+
+def test_dplr_general_equals_explicit_matrices():
+    """The general update as explicit d_k x d_k matrices:
+    S_t = (I + a b^T) Diag(alpha) S_{t-1} + k v^T."""
+    rng = np.random.default_rng(44)
+    q, k, v, a, bv, z, A, h0 = _dplr_case(rng, 14, 2, 6, 3)
+    o, S = oracle.recurrence_dplr_general(q, k, v, a, bv, z, A, h0)
+    alpha = np.exp(-5 / (1 + np.exp(-np.exp(A)[None, :, None] * z)))
+    for h in range(2):
+        St = h0[h].copy()
+        for t in range(14):
+            M = (np.eye(6) + np.outer(a[t, h], bv[t, h])) @ np.diag(alpha[t, h])
+            St = M @ St + np.outer(k[t, h], v[t, h])
+            assert np.allclose(o[t, h], St.T @ q[t, h], atol=1e-13)
+        assert np.allclose(S[h], St, atol=1e-13)
+
+
+def test_dplr_general_without_low_rank_is_gla():
+    """a = 0 leaves Diag(alpha) S + k v^T: the GLA row of [LA-KDA §4] with
+    beta = 1, in the closed form of its expansion ([LA-KDA §7.2])."""
+    rng = np.random.default_rng(45)
+    q, k, v, a, bv, z, A, h0 = _dplr_case(rng, 12, 2, 4, 3)
+    o, _ = oracle.recurrence_dplr_general(q, k, v, np.zeros_like(a), bv, z, A, h0)
+    alpha = np.exp(-5 / (1 + np.exp(-np.exp(A)[None, :, None] * z)))
+    for h in range(2):
+        for t in range(12):
+            St = np.prod(alpha[: t + 1, h], axis=0)[:, None] * h0[h]
+            for i in range(t + 1):
+                St = St + np.outer(np.prod(alpha[i + 1: t + 1, h], axis=0) * k[i, h], v[i, h])
+            assert np.allclose(o[t, h], St.T @ q[t, h], atol=1e-13)
+
+
+def test_dplr_general_projection_recalls_exactly():
+    """With a = -b, |b| = 1 and write key b, (I - b b^T) removes the component
+    along b before the write ([K3-ATTN §2.1], Householder view), so the new
+    state returns v exactly at b: S_t^T b_t = v_t."""
+    rng = np.random.default_rng(46)
+    q, k, v, a, bv, z, A, h0 = _dplr_case(rng, 10, 2, 5, 4)
+    o, _ = oracle.recurrence_dplr_general(bv, bv, v, -bv, bv, z, A, h0)
+    assert np.allclose(o, v, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,chunk", [(37, 16), (40, 8), (5, 16)])
+def test_chunkwise_dplr_equals_recurrence(T, chunk):
+    """The four-matrix chunked form (derivation in `chunkwise_dplr`) against the
+    token recurrence, with a partial last chunk."""
+    rng = np.random.default_rng(47 + T)
+    args = _dplr_case(rng, T, 2, 6, 5)
+    o1, S1 = oracle.recurrence_dplr_general(*args)
+    o2, S2 = oracle.chunkwise_dplr(*args, chunk=chunk)
+    assert np.allclose(o2, o1, atol=1e-12) and np.allclose(S2, S1, atol=1e-12)
+
+
+def test_chunkwise_dplr_collapses_to_two_matrices_for_kda():
+    """For KDA inputs (a = -beta k, b = k, write key beta k) the four chunk
+    matrices are two up to scales ([K3-ATTN §2.2]): A_ba = -A_bk and
+    A_qa = -A_qk, and the chunked result is the KDA one."""
+    rng = np.random.default_rng(48)
+    q, k, v, z, b, A, h0 = _rand_case(rng, 16, 1, 6, 4)
+    beta = (1 / (1 + np.exp(-b)))[..., None]
+    o, S, inter = oracle.chunkwise_dplr(q, beta * k, v, -beta * k, k, z, A, h0, chunk=16, keep=True)
+    r = inter[0][0]
+    assert np.allclose(r["Aba"], -r["Abk"], atol=1e-14) and np.allclose(r["Aqa"], -r["Aqk"], atol=1e-14)
+    o1, S1 = oracle.recurrence(q, k, v, z, b, A, h0)
+    assert np.allclose(o, o1, atol=1e-12) and np.allclose(S, S1, atol=1e-12)
+
+
+def test_dplr_decode_step_is_one_token_of_the_recurrence():
+    rng = np.random.default_rng(49)
+    q, k, v, a, bv, z, A, h0 = _dplr_case(rng, 3, 2, 4, 3)
+    st = np.stack([h0, 0.5 * h0])
+    o, S = oracle.decode_step_dplr(q[:2], k[:2], v[:2], a[:2], bv[:2], z[:2], A, st)
+    for n in range(2):
+        r = lambda x: x[n:n + 1]
+        o1, S1 = oracle.recurrence_dplr_general(r(q), r(k), r(v), r(a), r(bv), r(z), A, st[n])
+        assert np.allclose(o[n], o1[0], atol=1e-14) and np.allclose(S[n], S1, atol=1e-14)
