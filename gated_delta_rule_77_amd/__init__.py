@@ -13,6 +13,8 @@ Names follow the C ABI in include/kda.h:
     kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, ...) -> (y, hT, conv_state)
     kda_layer_step(q_in, k_in, v_in, conv_w, conv_state, g, beta, A, state, gate, norm_w) -> y
     kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
+    kda_chunk_fwd_mode(q, k, v, g, beta, A, mode, ...) -> (o, hT)  ("kda", "gla", "deltanet")
+    kda_recurrent_step_mode(q, k, v, g, beta, A, state, mode) -> o
 `g` are the raw per-channel gate logits and `beta` the raw write-strength
 logits; both activations run inside the kernels.
 """
@@ -26,7 +28,8 @@ __all__ = [
     "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_fold",
     "kda_layer_fwd", "kda_layer_step", "kda_layer_fwd_workspace_bytes",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
-    "kda_recurrent_step_supported", "EXPORTED_SYMBOLS",
+    "kda_recurrent_step_supported", "kda_chunk_fwd_mode", "kda_recurrent_step_mode", "MODES",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,8 +40,19 @@ EXPORTED_SYMBOLS = (
     "kda_status_string", "kda_chunk_fwd_supported", "kda_recurrent_step_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_debug_floats",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
-    "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step",
+    "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step", "kda_chunk_fwd_mode",
+    "kda_recurrent_step_mode",
 )
+# family modes of kda_chunk_fwd_mode / kda_recurrent_step_mode (kda_mode_t)
+MODES = {"kda": 0, "gla": 1, "deltanet": 2}
+
+
+def _mode_code(mode) -> int:
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"mode must be one of {sorted(MODES)}, got {mode!r}")
+        return MODES[mode]
+    return int(mode)
 
 
 class KdaError(RuntimeError):
@@ -87,6 +101,10 @@ def lib() -> ctypes.CDLL:
                                 + [i] * 7 + [vp, f, vp, sz, vp])
     L.kda_layer_step.restype = i
     L.kda_layer_step.argtypes = [vp, vp, vp, f, vp, f, f, f, f, vp, f, fl, fl, vp, i, i, i, i, vp]
+    L.kda_chunk_fwd_mode.restype = i
+    L.kda_chunk_fwd_mode.argtypes = chunk_args[:16] + [i] + chunk_args[16:] + [vp]
+    L.kda_recurrent_step_mode.restype = i
+    L.kda_recurrent_step_mode.argtypes = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, i, vp]
     _lib = L
     return L
 
@@ -148,7 +166,7 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, dtype) -> int:
     return int(lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, code))
 
 
-def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens):
+def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens, gated=True):
     torch = _torch()
     _req(q, "q")
     dev = q.device
@@ -156,16 +174,18 @@ def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens):
     _dtype_code(q)
     _req(k, "k", dt, dev)
     _req(v, "v", dt, dev)
-    _req(g, "g", torch.float32, dev)
     _req(beta, "beta", torch.float32, dev)
-    _req(A, "A", torch.float32, dev)
+    if gated or g is not None:
+        _req(g, "g", torch.float32, dev)
+    if gated or A is not None:
+        _req(A, "A", torch.float32, dev)
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    if k.shape != q.shape or v.shape != (B, T, H, dv) or g.shape != q.shape:
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or (g is not None and g.shape != q.shape):
         raise ValueError("k, g must match q [B, T, H, dk] and v must be [B, T, H, dv]")
-    if beta.shape != (B, T, H) or A.shape != (H,):
+    if beta.shape != (B, T, H) or (A is not None and A.shape != (H,)):
         raise ValueError("beta must be [B, T, H] and A must be [H]")
     if cu_seqlens is not None:
         _req(cu_seqlens, "cu_seqlens", torch.int32, dev)
@@ -201,10 +221,19 @@ def kda_chunk_fwd_debug(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None
                   True, workspace, debug=True)
 
 
+def kda_chunk_fwd_mode(q, k, v, g, beta, A, mode, initial_state=None, cu_seqlens=None,
+                       chunk_size: int = 64, output_final_state: bool = True, workspace=None):
+    """kda_chunk_fwd in a family mode: "kda", "gla" (erase off) or "deltanet"
+    (alpha = 1; g and A may be None)."""
+    return _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size,
+                  output_final_state, workspace, debug=False, mode=_mode_code(mode))
+
+
 def _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size, output_final_state,
-           workspace, debug):
+           workspace, debug, mode=None):
     torch = _torch()
-    B, T, H, dk, dv, N, dev, dt = _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens)
+    B, T, H, dk, dv, N, dev, dt = _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens,
+                                                gated=mode != MODES["deltanet"])
     code = _dtype_code(q)
     L = lib()
     need = int(L.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk_size, code))
@@ -218,6 +247,10 @@ def _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size, output_fi
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(initial_state),
             _ptr(cu_seqlens), B, T, H, dk, dv, N, chunk_size, code, _ptr(o), _ptr(hT),
             _ptr(workspace), workspace.numel())
+    if mode is not None:
+        _check(L.kda_chunk_fwd_mode(*args[:16], mode, *args[16:], _stream(dev)),
+               "kda_chunk_fwd_mode")
+        return o, hT
     if not debug:
         _check(L.kda_chunk_fwd(*args, _stream(dev)), "kda_chunk_fwd")
         return o, hT
@@ -246,28 +279,44 @@ def kda_recurrent_step(q, k, v, g, beta, A, state):
     """One decode token per sequence: q, k [N, H, dk], v [N, H, dv] (bf16 or
     fp32), g [N, H, dk] fp32, beta [N, H] fp32, A [H] fp32, state
     [N, H, dk, dv] fp32 (updated in place).  Returns o [N, H, dv]."""
+    return _step(q, k, v, g, beta, A, state, None)
+
+
+def kda_recurrent_step_mode(q, k, v, g, beta, A, state, mode):
+    """kda_recurrent_step in a family mode ("kda", "gla", "deltanet"; with
+    "deltanet" g and A may be None)."""
+    return _step(q, k, v, g, beta, A, state, _mode_code(mode))
+
+
+def _step(q, k, v, g, beta, A, state, mode):
     torch = _torch()
     _req(q, "q")
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
+    gated = mode != MODES["deltanet"]
     _req(k, "k", dt, dev)
     _req(v, "v", dt, dev)
-    _req(g, "g", torch.float32, dev)
+    if gated or g is not None:
+        _req(g, "g", torch.float32, dev)
+    if gated or A is not None:
+        _req(A, "A", torch.float32, dev)
     _req(beta, "beta", torch.float32, dev)
-    _req(A, "A", torch.float32, dev)
     _req(state, "state", torch.float32, dev)
     if q.dim() != 3:
         raise ValueError("q must be [N, H, dk]")
     N, H, dk = q.shape
     dv = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, dv):
+    if k.shape != q.shape or (g is not None and g.shape != q.shape) or v.shape != (N, H, dv):
         raise ValueError("k, g must match q [N, H, dk] and v must be [N, H, dv]")
-    if beta.shape != (N, H) or A.shape != (H,) or state.shape != (N, H, dk, dv):
+    if beta.shape != (N, H) or (A is not None and A.shape != (H,)) or state.shape != (N, H, dk, dv):
         raise ValueError("beta [N, H], A [H] and state [N, H, dk, dv] expected")
     o = torch.empty((N, H, dv), dtype=dt, device=dev)
-    rc = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
-                                  _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(dev))
-    _check(rc, "kda_recurrent_step")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(state), _ptr(o),
+            N, H, dk, dv, code)
+    if mode is None:
+        _check(lib().kda_recurrent_step(*args, _stream(dev)), "kda_recurrent_step")
+    else:
+        _check(lib().kda_recurrent_step_mode(*args, mode, _stream(dev)), "kda_recurrent_step_mode")
     return o
 
 

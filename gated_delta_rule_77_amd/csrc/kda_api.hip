@@ -9,6 +9,10 @@ namespace {
 
 bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
+bool mode_ok(int m) { return m == kModeKDA || m == kModeGLA || m == kModeDeltaNet; }
+static_assert(KDA_MODE_KDA == kModeKDA && KDA_MODE_GLA == kModeGLA &&
+              KDA_MODE_DELTANET == kModeDeltaNet, "mode numbering of the ABI and the kernels");
+
 bool chunk_shape_supported(int dk, int dv, int chunk) { return generic_supported(dk, dv, chunk); }
 
 // sizes shared by the prefill entry points; false on invalid arguments
@@ -26,8 +30,9 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
                          float* dbg_intra, float* dbg_state, hipEvent_t* ev, int n_ev,
                          void* stream, const void* gate = nullptr, const float* norm_w = nullptr,
                          float rms_eps = 0.f, const float* conv_w = nullptr,
-                         const void* conv_state0 = nullptr, float l2_eps = 0.f) {
-    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+                         const void* conv_state0 = nullptr, float l2_eps = 0.f,
+                         int mode = kModeKDA) {
+    if (!dtype_ok(dtype) || !mode_ok(mode)) return KDA_ERR_INVALID_ARG;
     if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
     if (cu) {
         if (B != 1) return KDA_ERR_INVALID_ARG;
@@ -37,8 +42,9 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     if (!chunk_shape_supported(dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
     const long long tokens = (long long)B * T;
-    if (tokens > 0 && (!q || !k || !v || !z || !b || !o)) return KDA_ERR_INVALID_ARG;
-    if (!A) return KDA_ERR_INVALID_ARG;
+    const bool gated = mode != kModeDeltaNet;    // DeltaNet reads no gate logits
+    if (tokens > 0 && (!q || !k || !v || (gated && !z) || !b || !o)) return KDA_ERR_INVALID_ARG;
+    if (gated && !A) return KDA_ERR_INVALID_ARG;
     const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
     const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, fast);
     if (L.total == 0) return KDA_ERR_INVALID_ARG;
@@ -58,6 +64,7 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     a.conv_w = fast ? conv_w : nullptr;
     a.conv_state0 = conv_state0;
     a.l2_eps = l2_eps;
+    a.mode = mode;
     hipError_t e = ev ? hipEventRecord(ev[0], a.stream) : hipSuccess;
     if (e == hipSuccess) e = launch_prep(a);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], a.stream);
@@ -168,18 +175,39 @@ kda_status_t kda_chunk_fwd_timed(const void* q, const void* k, const void* v,
                        stream);
 }
 
-kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, const float* g_logits,
-                                const float* beta_logits, const float* A, float* state, void* o,
-                                int N, int H, int dk, int dv, kda_dtype_t dtype, void* stream) {
-    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+kda_status_t kda_recurrent_step_mode(const void* q, const void* k, const void* v,
+                                     const float* g_logits, const float* beta_logits,
+                                     const float* A, float* state, void* o, int N, int H, int dk,
+                                     int dv, kda_dtype_t dtype, kda_mode_t mode, void* stream) {
+    if (!dtype_ok(dtype) || !mode_ok(mode)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
     if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !g_logits || !beta_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    const bool gated = mode != KDA_MODE_DELTANET;
+    if (!q || !k || !v || (gated && (!g_logits || !A)) || !beta_logits || !state || !o)
+        return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_decode(q, k, v, g_logits, beta_logits, A, state, o, N, H, dk, dv,
-                                 dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+                                 dtype == KDA_BF16, static_cast<hipStream_t>(stream), mode);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, const float* g_logits,
+                                const float* beta_logits, const float* A, float* state, void* o,
+                                int N, int H, int dk, int dv, kda_dtype_t dtype, void* stream) {
+    return kda_recurrent_step_mode(q, k, v, g_logits, beta_logits, A, state, o, N, H, dk, dv,
+                                   dtype, KDA_MODE_KDA, stream);
+}
+
+kda_status_t kda_chunk_fwd_mode(const void* q, const void* k, const void* v,
+                                const float* g_logits, const float* beta_logits, const float* A,
+                                const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                int dk, int dv, int N, int chunk, kda_dtype_t dtype,
+                                kda_mode_t mode, void* o, float* hT, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
+                       chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, nullptr, 0,
+                       stream, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f, mode);
 }
 
 size_t kda_layer_fwd_workspace_bytes(int B, int T, int H, int d, int N, int chunk,

@@ -105,7 +105,10 @@ __device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : p < 3 ? 1 : 
 // convolution (four taps oldest first, the sequence's first three inputs from
 // the carried state cs0 or zeros), Swish, and for q and k the L2Norm over the
 // head's 128 channels; the results are rounded to bf16 as the core's inputs.
-template <bool DBG, bool CONV>
+// MODE selects a row of the family table ([LA-KDA §4]): kModeDeltaNet skips
+// the gate (G = 0, every factor 1); kModeGLA drops A_kk (T = Diag(beta)) and
+// stores W = 0, so the chain kernels see V~ = U = Diag(beta) V.
+template <bool DBG, bool CONV, int MODE>
 __global__ __launch_bounds__(256, 2)
 void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const float* __restrict__ z,
@@ -209,17 +212,21 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int c = tid & 127, half = tid >> 7;
     float lr[32];
     {
-        const float a2 = -expf(A[h]) * kLog2e;     // e^{-e^A z} = 2^(a2 z)
-        const float c5 = kGMin * kLog2e;
+        float a2 = 0.f;                                 // e^{-e^A z} = 2^(a2 z)
+        if constexpr (MODE != kModeDeltaNet) {
+            a2 = -expf(A[h]) * kLog2e;
 #pragma unroll
-        for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
+            for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
+        }
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             const int row = 32 * half + i;
-            float sg = __builtin_amdgcn_rcpf(1.f + ex2(lr[i] * a2));
-            sg = row < len ? sg : 0.f;
-            run = fmaf(sg, c5, run);
+            if constexpr (MODE != kModeDeltaNet) {
+                float sg = __builtin_amdgcn_rcpf(1.f + ex2(lr[i] * a2));
+                sg = row < len ? sg : 0.f;
+                run = fmaf(sg, kGMin * kLog2e, run);
+            }
             lr[i] = run;
             sG[row * kLdG + c] = run;
         }
@@ -375,7 +382,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 bf16x8 col;
 #pragma unroll
                 for (int e = 0; e < 8; e++) col[e] = (bf16)(kf[e] * X8[e]);
-                akk[sl] = mfma_bf16(rk, col, akk[sl]);
+                if constexpr (MODE != kModeGLA) akk[sl] = mfma_bf16(rk, col, akk[sl]);
                 aqk[sl] = mfma_bf16(rq, col, aqk[sl]);
             }
         }
@@ -493,10 +500,12 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) {
         f32x4 wt0 = zero4(), wt1 = zero4();
+        if constexpr (MODE != kModeGLA) {
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            wt0 = mfma_bf16(kgf[kb][0], tf[tb][kb], wt0);
-            wt1 = mfma_bf16(kgf[kb][1], tf[tb][kb], wt1);
+            for (int kb = 0; kb < 2; kb++) {
+                wt0 = mfma_bf16(kgf[kb][0], tf[tb][kb], wt0);
+                wt1 = mfma_bf16(kgf[kb][1], tf[tb][kb], wt1);
+            }
         }
         *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
     }
@@ -1002,18 +1011,17 @@ hipError_t launch_fast(const ChunkArgs& a) {
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
     const dim3 gi((unsigned)((long long)a.L.cap * a.H));
     const bf16* cs0 = static_cast<const bf16*>(a.conv_state0);
-    if (a.dbg_intra)
-        hipLaunchKernelGGL((fast_intra_kernel<true, false>), gi, dim3(256), 0, a.stream,
-                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, a.L.cap, recs, a.dbg_intra, a.conv_w, cs0, a.l2_eps);
-    else if (a.conv_w)
-        hipLaunchKernelGGL((fast_intra_kernel<false, true>), gi, dim3(256), 0, a.stream,
-                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr, a.conv_w, cs0, a.l2_eps);
-    else
-        hipLaunchKernelGGL((fast_intra_kernel<false, false>), gi, dim3(256), 0, a.stream,
-                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A,
-                           hdr, chunks, a.H, a.L.cap, recs, (float*)nullptr, a.conv_w, cs0, a.l2_eps);
+#define KDA_INTRA(DBG, CONV, MODE, DBGP)                                                      \
+    hipLaunchKernelGGL((fast_intra_kernel<DBG, CONV, MODE>), gi, dim3(256), 0, a.stream,         \
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A, hdr, \
+                       chunks, a.H, a.L.cap, recs, DBGP, a.conv_w, cs0, a.l2_eps)
+    // the debug and layer variants exist for KDA only (the API enforces it)
+    if (a.dbg_intra) KDA_INTRA(true, false, kModeKDA, a.dbg_intra);
+    else if (a.conv_w) KDA_INTRA(false, true, kModeKDA, (float*)nullptr);
+    else if (a.mode == kModeGLA) KDA_INTRA(false, false, kModeGLA, (float*)nullptr);
+    else if (a.mode == kModeDeltaNet) KDA_INTRA(false, false, kModeDeltaNet, (float*)nullptr);
+    else KDA_INTRA(false, false, kModeKDA, (float*)nullptr);
+#undef KDA_INTRA
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;

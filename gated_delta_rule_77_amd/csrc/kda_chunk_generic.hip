@@ -11,6 +11,9 @@
 //   V~ = U - W S,  O = (Q . Gamma) S + A_qk V~,  S <- Diag(Gamma_C) S + (K . e^{G_C - G})^T V~
 // Here every decay factor is evaluated as e^{difference} with a non-positive
 // exponent, so nothing can overflow whatever the chunk length.
+// The family modes ([LA-KDA §4] table): kModeDeltaNet takes G = 0 without
+// reading the gate logits; kModeGLA drops A_kk and stores W = 0, so that
+// V~ = U = Diag(beta) V.
 // Sources: [LA-KDA] "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制" §5.4, §7.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -36,7 +39,7 @@ void gen_intra_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                       const Tin* __restrict__ v, const float* __restrict__ z,
                       const float* __restrict__ bl, const float* __restrict__ A,
                       const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
-                      float* __restrict__ recs, float* __restrict__ dbg)
+                      float* __restrict__ recs, float* __restrict__ dbg, int mode)
 {
     using R = GenRec<DK, DV, C>;
     const int cid = blockIdx.x, h = blockIdx.y;
@@ -63,11 +66,12 @@ void gen_intra_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 
     // gate [LA-KDA §5.4] and in-chunk cumulative sum; positions past the end
     // of the sequence get g = 0 (alpha = 1) and beta = 0 (no write)
-    const float ea = expf(A[h]);
+    const bool gated = mode != kModeDeltaNet;
+    const float ea = gated ? expf(A[h]) : 1.f;
     for (int c = tid; c < DK; c += 256) {
         float run = 0.f;
         for (int i = 0; i < C; i++) {
-            if (i < len) run += log_decay<true>(ea, z[((size_t)(tok0 + i) * H + h) * DK + c]);
+            if (gated && i < len) run += log_decay<true>(ea, z[((size_t)(tok0 + i) * H + h) * DK + c]);
             sG[i][c] = run;
         }
     }
@@ -85,6 +89,7 @@ void gen_intra_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                 aqk += at_q(i, c) * kj;
             }
         }
+        if (mode == kModeGLA) akk = 0.f;
         sAkk[i][j] = j < i ? sBeta[i] * akk : 0.f;
         rec[R::A + idx] = aqk;
         if (dbg) {
@@ -108,7 +113,8 @@ void gen_intra_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     for (int idx = tid; idx < C * DK; idx += 256) {
         const int i = idx / DK, c = idx % DK;
         float acc = 0.f;
-        for (int j = 0; j <= i; j++) acc += sN[i][j] * sBeta[j] * at_k(j, c) * expf(sG[j][c]);
+        if (mode != kModeGLA)
+            for (int j = 0; j <= i; j++) acc += sN[i][j] * sBeta[j] * at_k(j, c) * expf(sG[j][c]);
         rec[R::W + idx] = acc;
         rec[R::Q + idx] = at_q(i, c) * expf(sG[i][c]);
         rec[R::K + idx] = at_k(i, c) * expf(sG[C - 1][c] - sG[i][c]);
@@ -193,7 +199,7 @@ hipError_t launch_generic_t(const ChunkArgs& a) {
     float* recs = reinterpret_cast<float*>(a.ws + a.L.off_recs);
     hipLaunchKernelGGL((gen_intra_kernel<D, D, C, Tin>), dim3((unsigned)a.L.cap, (unsigned)a.H),
                        dim3(256), 0, a.stream, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v,
-                       a.z, a.b, a.A, hdr, chunks, a.H, recs, a.dbg_intra);
+                       a.z, a.b, a.A, hdr, chunks, a.H, recs, a.dbg_intra, a.mode);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;

@@ -11,7 +11,7 @@
 
 namespace kda {
 
-template <int DK, int DV, typename Tin>
+template <int DK, int DV, typename Tin, int MODE>
 __global__ __launch_bounds__((DV / 4) * (DK / 16))
 void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                    const Tin* __restrict__ v, const float* __restrict__ z,
@@ -25,9 +25,9 @@ void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     // the state stream is the cost of this kernel: issue its loads first
     float4 Sv[16];
     load_state<DK, DV>(Sv, S);
-    const float ea = expf(A[nh % H]);
-    kda_token_step<DK, DV, Tin, true>(Sv, k + (size_t)nh * DK, v + (size_t)nh * DV,
-                                      z + (size_t)nh * DK, bl[nh], ea, q + (size_t)nh * DK,
+    const float ea = MODE == kModeDeltaNet ? 1.f : expf(A[nh % H]);
+    kda_token_step<DK, DV, Tin, true, MODE>(Sv, k + (size_t)nh * DK, v + (size_t)nh * DV,
+                                      MODE == kModeDeltaNet ? z : z + (size_t)nh * DK, bl[nh], ea, q + (size_t)nh * DK,
                                       o + (size_t)nh * DV, s_al, s_k, s_q, s_red);
     store_state<DK, DV>(Sv, S);
 }
@@ -70,21 +70,26 @@ bool decode_supported(int dk, int dv) {
 template <int D, typename Tin>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* z,
                                   const float* b, const float* A, float* state, void* o,
-                                  int N, int H, hipStream_t s) {
+                                  int N, int H, hipStream_t s, int mode) {
     constexpr int NT = (D / 4) * (D / 16);
-    hipLaunchKernelGGL((decode_kernel<D, D, Tin>), dim3((unsigned)N * H), dim3(NT), 0, s,
-                       (const Tin*)q, (const Tin*)k, (const Tin*)v, z, b, A, state, (Tin*)o, H);
+#define KDA_DEC_MODE(M)                                                                     \
+    hipLaunchKernelGGL((decode_kernel<D, D, Tin, M>), dim3((unsigned)N * H), dim3(NT), 0, s, \
+                       (const Tin*)q, (const Tin*)k, (const Tin*)v, z, b, A, state, (Tin*)o, H)
+    if (mode == kModeGLA) KDA_DEC_MODE(kModeGLA);
+    else if (mode == kModeDeltaNet) KDA_DEC_MODE(kModeDeltaNet);
+    else KDA_DEC_MODE(kModeKDA);
+#undef KDA_DEC_MODE
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* z,
                          const float* b, const float* A, float* state, void* o,
-                         int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s) {
+                         int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s, int mode) {
     (void)dv;
 #define KDA_DEC(D)                                                                          \
     if (dk == D) return dtype_bf16                                                          \
-        ? launch_decode_t<D, bf16>(q, k, v, z, b, A, state, o, N, H, s)                    \
-        : launch_decode_t<D, float>(q, k, v, z, b, A, state, o, N, H, s);
+        ? launch_decode_t<D, bf16>(q, k, v, z, b, A, state, o, N, H, s, mode)              \
+        : launch_decode_t<D, float>(q, k, v, z, b, A, state, o, N, H, s, mode);
     KDA_DEC(16) KDA_DEC(32) KDA_DEC(64) KDA_DEC(128)
 #undef KDA_DEC
     return hipErrorInvalidValue;

@@ -97,6 +97,11 @@ inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, boo
     return L;
 }
 
+// Family modes ([LA-KDA §4] table): KDA; gated linear attention (the erase
+// step off: S <- Diag(alpha) S + beta k v^T); DeltaNet (alpha = 1, the gate
+// logits unread).
+constexpr int kModeKDA = 0, kModeGLA = 1, kModeDeltaNet = 2;
+
 struct ChunkArgs {
     const void* q; const void* k; const void* v;
     const float* z; const float* b; const float* A;
@@ -113,6 +118,7 @@ struct ChunkArgs {
     // L2Norm applied in the intra kernel)
     const void* gate; const float* norm_w; float rms_eps;
     const float* conv_w; const void* conv_state0; float l2_eps;
+    int mode;                  // kModeKDA, kModeGLA or kModeDeltaNet
 };
 
 // launchers (return hipError_t of the launches)
@@ -122,7 +128,8 @@ hipError_t launch_generic(const ChunkArgs& a, int dtype_bf16);
 bool generic_supported(int dk, int dv, int C);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* z,
                          const float* b, const float* A, float* state, void* o,
-                         int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s);
+                         int N, int H, int dk, int dv, int dtype_bf16, hipStream_t s,
+                         int mode = kModeKDA);
 bool decode_supported(int dk, int dv);
 hipError_t launch_layer_pre(const void* q_in, const void* k_in, const void* v_in,
                             const float* conv_w, const void* cs0, const int* cu, int N, int Tfix,

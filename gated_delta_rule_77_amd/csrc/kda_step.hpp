@@ -15,6 +15,7 @@
 // groups), held in registers as 16 float4.
 #pragma once
 #include "kda_device.hpp"
+#include "kda_internal.hpp"
 
 namespace kda {
 
@@ -24,7 +25,10 @@ namespace kda {
 // other contraction is allowed, so the arithmetic of a step is fixed by this
 // source: the decode kernel and the replay fold below run the same step and
 // produce the same bits.
-template <int DK, int DV, typename Tin, bool WITH_Q>
+// MODE picks a row of the family table ([LA-KDA §4]): kModeGLA writes
+// u = beta v without the erase (no p), kModeDeltaNet takes alpha = 1 without
+// reading zt.
+template <int DK, int DV, typename Tin, bool WITH_Q, int MODE = kModeKDA>
 __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __restrict__ kt,
                                                const Tin* __restrict__ vt, const float* __restrict__ zt,
                                                float b_logit, float ea, const Tin* __restrict__ qt,
@@ -35,7 +39,7 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
     for (int i = t; i < DK; i += NT) {
-        s_al[i] = expf(log_decay<true>(ea, zt[i]));
+        s_al[i] = MODE == kModeDeltaNet ? 1.f : expf(log_decay<true>(ea, zt[i]));
         s_k[i] = to_f32(kt[i]);
         if (WITH_Q) s_q[i] = to_f32(qt[i]);
     }
@@ -50,11 +54,13 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         const int i = rg * 16 + r;
-        const float ka = s_al[i] * s_k[i];
-        p[0] = __builtin_fmaf(ka, Sv[r].x, p[0]);
-        p[1] = __builtin_fmaf(ka, Sv[r].y, p[1]);
-        p[2] = __builtin_fmaf(ka, Sv[r].z, p[2]);
-        p[3] = __builtin_fmaf(ka, Sv[r].w, p[3]);
+        if (MODE != kModeGLA) {
+            const float ka = s_al[i] * s_k[i];
+            p[0] = __builtin_fmaf(ka, Sv[r].x, p[0]);
+            p[1] = __builtin_fmaf(ka, Sv[r].y, p[1]);
+            p[2] = __builtin_fmaf(ka, Sv[r].z, p[2]);
+            p[3] = __builtin_fmaf(ka, Sv[r].w, p[3]);
+        }
         if (WITH_Q) {
             const float qa = s_al[i] * s_q[i];
             r4[0] = __builtin_fmaf(qa, Sv[r].x, r4[0]);
@@ -79,7 +85,7 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
     }
     float u[4];
 #pragma unroll
-    for (int c = 0; c < 4; c++) u[c] = beta * (vj[c] - P[c]);
+    for (int c = 0; c < 4; c++) u[c] = MODE == kModeGLA ? beta * vj[c] : beta * (vj[c] - P[c]);
     if (WITH_Q) {
         float qk = 0.f;
 #pragma unroll 8

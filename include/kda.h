@@ -198,6 +198,45 @@ KDA_API kda_status_t kda_recurrent_step(const void* q, const void* k, const void
                                 void* stream);
 
 /*
+ * Family modes: the other rows of the family table of [LA-KDA §4], run by the
+ * same kernels.
+ *   KDA_MODE_KDA       (3) as above.
+ *   KDA_MODE_GLA       gated linear attention: the erase step is off,
+ *                      S_t = Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T.  The
+ *                      table's row has no write strength; it is beta = 1
+ *                      here (a large beta logit).
+ *   KDA_MODE_DELTANET  DeltaNet: alpha = 1,
+ *                      S_t = (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T;
+ *                      g_logits and A are not read and may be NULL.
+ * With both switches of the table off (GLA at alpha = 1) the update is plain
+ * linear attention ([LA-KDA §3]); pass very negative gate logits to GLA.
+ */
+typedef enum { KDA_MODE_KDA = 0, KDA_MODE_GLA = 1, KDA_MODE_DELTANET = 2 } kda_mode_t;
+
+/*
+ * kda_chunk_fwd in a family mode: same arguments, layouts, supported shapes,
+ * workspace and errors, plus `mode` (KDA_ERR_INVALID_ARG outside the enum).
+ * KDA_MODE_KDA gives exactly kda_chunk_fwd.
+ */
+KDA_API kda_status_t kda_chunk_fwd_mode(const void* q, const void* k, const void* v,
+                                        const float* g_logits, const float* beta_logits,
+                                        const float* A, const float* h0,
+                                        const int* cu_seqlens, int B, int T, int H, int dk,
+                                        int dv, int N, int chunk, kda_dtype_t dtype,
+                                        kda_mode_t mode, void* o, float* hT, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
+ * kda_recurrent_step in a family mode: same arguments and errors, plus `mode`.
+ * KDA_MODE_GLA writes u = beta v without forming S'^T k.
+ */
+KDA_API kda_status_t kda_recurrent_step_mode(const void* q, const void* k, const void* v,
+                                             const float* g_logits, const float* beta_logits,
+                                             const float* A, float* state, void* o, int N,
+                                             int H, int dk, int dv, kda_dtype_t dtype,
+                                             kda_mode_t mode, void* stream);
+
+/*
  * The KDA layer between its projections: the core with the steps either side
  * of it that act on one token-head row.
  *

@@ -182,3 +182,24 @@ def test_layer_entry_points_reject_bad_arguments(L):
     assert step(*ok, -1.0, 1e-5, FAKE, 4, 2, 128, 1, None) == 1
     assert step(*([FAKE] * 4 + [None] + [FAKE] * 6), 1e-6, 1e-5, FAKE, 4, 2, 128, 1, None) == 1
     assert step(*([None] * 11), 1e-6, 1e-5, None, 0, 2, 128, 1, None) == 0
+
+
+def test_mode_entry_points_validate_the_mode(L):
+    fn = L.kda_chunk_fwd_mode
+    fn.restype = ctypes.c_int
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn.argtypes = [vp] * 8 + [i] * 9 + [vp, vp, vp, ctypes.c_size_t, vp]
+
+    def call(mode, z=FAKE, A=FAKE, ws=None):
+        return fn(FAKE, FAKE, FAKE, z, FAKE, A, None, None, 1, 64, 2, 16, 16, 1, 16, 0, mode,
+                  FAKE, None, ws, 0, None)
+
+    assert call(3) == 1 and call(-1) == 1
+    assert call(0, A=None) == 1 and call(1, z=None) == 1   # KDA and GLA read the gate logits
+    assert call(2, z=None, A=None) == 3                    # DeltaNet does not: on to the workspace check
+    step = L.kda_recurrent_step_mode
+    step.restype = i
+    step.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    assert step(*[FAKE] * 8, 4, 2, 128, 128, 1, 3, None) == 1
+    assert step(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 4, 2, 128, 128, 1, 0, None) == 1
+    assert step(None, None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 2, None) == 0
