@@ -15,6 +15,8 @@ Names follow the C ABI in include/kda.h:
     kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
     kda_chunk_fwd_mode(q, k, v, g, beta, A, mode, ...) -> (o, hT)  ("kda", "gla", "deltanet")
     kda_recurrent_step_mode(q, k, v, g, beta, A, state, mode) -> o
+    kda_dplr_chunk_fwd(q, k, v, a, b, g, A, ...) -> (o, hT)      (general DPLR update)
+    kda_dplr_recurrent_step(q, k, v, a, b, g, A, state) -> o
 `g` are the raw per-channel gate logits and `beta` the raw write-strength
 logits; both activations run inside the kernels.
 """
@@ -29,6 +31,7 @@ __all__ = [
     "kda_layer_fwd", "kda_layer_step", "kda_layer_fwd_workspace_bytes",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
     "kda_recurrent_step_supported", "kda_chunk_fwd_mode", "kda_recurrent_step_mode", "MODES",
+    "kda_dplr_chunk_fwd", "kda_dplr_recurrent_step", "kda_dplr_chunk_fwd_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -41,7 +44,8 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_debug_floats",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
     "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step", "kda_chunk_fwd_mode",
-    "kda_recurrent_step_mode",
+    "kda_recurrent_step_mode", "kda_dplr_chunk_fwd_workspace_bytes", "kda_dplr_chunk_fwd",
+    "kda_dplr_recurrent_step",
 )
 # family modes of kda_chunk_fwd_mode / kda_recurrent_step_mode (kda_mode_t)
 MODES = {"kda": 0, "gla": 1, "deltanet": 2}
@@ -105,6 +109,12 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd_mode.argtypes = chunk_args[:16] + [i] + chunk_args[16:] + [vp]
     L.kda_recurrent_step_mode.restype = i
     L.kda_recurrent_step_mode.argtypes = [vp, vp, vp, f, f, f, f, vp, i, i, i, i, i, i, vp]
+    L.kda_dplr_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_dplr_chunk_fwd_workspace_bytes.argtypes = [i] * 8
+    L.kda_dplr_chunk_fwd.restype = i
+    L.kda_dplr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 8 + [vp, f, vp, sz, vp]
+    L.kda_dplr_recurrent_step.restype = i
+    L.kda_dplr_recurrent_step.argtypes = [vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 5 + [vp]
     _lib = L
     return L
 
@@ -174,7 +184,8 @@ def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens, gated=True):
     _dtype_code(q)
     _req(k, "k", dt, dev)
     _req(v, "v", dt, dev)
-    _req(beta, "beta", torch.float32, dev)
+    if beta is not None:            # None only for the general DPLR call, which has no beta
+        _req(beta, "beta", torch.float32, dev)
     if gated or g is not None:
         _req(g, "g", torch.float32, dev)
     if gated or A is not None:
@@ -185,7 +196,7 @@ def _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens, gated=True):
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or (g is not None and g.shape != q.shape):
         raise ValueError("k, g must match q [B, T, H, dk] and v must be [B, T, H, dv]")
-    if beta.shape != (B, T, H) or (A is not None and A.shape != (H,)):
+    if (beta is not None and beta.shape != (B, T, H)) or (A is not None and A.shape != (H,)):
         raise ValueError("beta must be [B, T, H] and A must be [H]")
     if cu_seqlens is not None:
         _req(cu_seqlens, "cu_seqlens", torch.int32, dev)
@@ -273,6 +284,68 @@ def _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size, output_fi
         capacity=Cn,
     )
     return o, hT, inter
+
+
+def kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(lib().kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, code))
+
+
+def kda_dplr_chunk_fwd(q, k, v, a, b, g, A, initial_state=None, cu_seqlens=None,
+                       chunk_size: int = 64, output_final_state: bool = True, workspace=None):
+    """General DPLR prefill: S' = Diag(alpha) S, S'' = S' + a (b^T S'),
+    S = S'' + k v^T, o = S^T q.  q, k, a, b [B, T, H, dk], v [B, T, H, dv]
+    (bf16 or fp32), g [B, T, H, dk] fp32 gate logits, A [H] fp32; the rest as
+    kda_chunk_fwd.  Returns (o, final_state or None)."""
+    torch = _torch()
+    B, T, H, dk, dv, N, dev, dt = _prefill_args(q, k, v, g, None, A, initial_state, cu_seqlens)
+    _req(a, "a", dt, dev)
+    _req(b, "b", dt, dev)
+    if a.shape != q.shape or b.shape != q.shape:
+        raise ValueError("a and b must match q [B, T, H, dk]")
+    code = _dtype_code(q)
+    L = lib()
+    need = int(L.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk_size, code))
+    if need == 0:
+        _check(2 if not L.kda_chunk_fwd_supported(dk, dv, chunk_size, code) else 1,
+               "kda_dplr_chunk_fwd_workspace_bytes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    _check(L.kda_dplr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(A),
+                                _ptr(initial_state), _ptr(cu_seqlens), B, T, H, dk, dv, N,
+                                chunk_size, code, _ptr(o), _ptr(hT), _ptr(workspace),
+                                workspace.numel(), _stream(dev)), "kda_dplr_chunk_fwd")
+    return o, hT
+
+
+def kda_dplr_recurrent_step(q, k, v, a, b, g, A, state):
+    """One general-DPLR token per sequence: q, k, a, b [N, H, dk], v [N, H, dv]
+    (bf16 or fp32), g [N, H, dk] fp32, A [H] fp32, state [N, H, dk, dv] fp32
+    (updated in place).  Returns o [N, H, dv]."""
+    torch = _torch()
+    _req(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, name in ((k, "k"), (v, "v"), (a, "a"), (b, "b")):
+        _req(t, name, dt, dev)
+    _req(g, "g", torch.float32, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(state, "state", torch.float32, dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if any(t.shape != q.shape for t in (k, a, b, g)) or v.shape != (N, H, dv):
+        raise ValueError("k, a, b, g must match q [N, H, dk] and v must be [N, H, dv]")
+    if A.shape != (H,) or state.shape != (N, H, dk, dv):
+        raise ValueError("A [H] and state [N, H, dk, dv] expected")
+    o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _check(lib().kda_dplr_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g),
+                                         _ptr(A), _ptr(state), _ptr(o), N, H, dk, dv, code,
+                                         _stream(dev)), "kda_dplr_recurrent_step")
+    return o
 
 
 def kda_recurrent_step(q, k, v, g, beta, A, state):

@@ -210,6 +210,56 @@ kda_status_t kda_chunk_fwd_mode(const void* q, const void* k, const void* v,
                        stream, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f, mode);
 }
 
+size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int chunk,
+                                          kda_dtype_t dtype) {
+    if (!dtype_ok(dtype) || !prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return 0;
+    if (!chunk_shape_supported(dk, dv, chunk)) return 0;
+    return ws_layout(B, T, H, dk, dv, N, chunk, false, true).total;
+}
+
+kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a,
+                                const void* b, const float* g_logits, const float* A,
+                                const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                float* hT, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
+    if (!chunk_shape_supported(dk, dv, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if ((long long)B * T > 0 && (!q || !k || !v || !a || !b || !g_logits || !o))
+        return KDA_ERR_INVALID_ARG;
+    if (!A) return KDA_ERR_INVALID_ARG;
+    const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, false, true);
+    if (L.total == 0) return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
+    ChunkArgs c{};
+    c.q = q; c.k = k; c.v = v; c.la = a; c.lb = b; c.z = g_logits; c.A = A; c.h0 = h0;
+    c.cu = cu_seqlens;
+    c.B = B; c.T = T; c.H = H; c.dk = dk; c.dv = dv; c.N = N; c.C = chunk;
+    c.o = o; c.hT = hT; c.ws = static_cast<uint8_t*>(workspace); c.L = L;
+    c.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_prep(c);
+    if (e == hipSuccess) e = launch_dplr_generic(c, dtype == KDA_BF16);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_dplr_recurrent_step(const void* q, const void* k, const void* v, const void* a,
+                                     const void* b, const float* g_logits, const float* A,
+                                     float* state, void* o, int N, int H, int dk, int dv,
+                                     kda_dtype_t dtype, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !a || !b || !g_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    hipError_t e = launch_dplr_decode(q, k, v, a, b, g_logits, A, state, o, N, H, dk,
+                                      dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_layer_fwd_workspace_bytes(int B, int T, int H, int d, int N, int chunk,
                                      kda_dtype_t dtype) {
     return layer_ws(B, T, H, d, N, chunk, dtype).total;

@@ -39,6 +39,12 @@ inline size_t generic_rec_floats(int dk, int dv, int C) {
     return (size_t)C * dk * 3 + (size_t)C * dv + (size_t)C * C + dk;
 }
 
+// fp32 record of the general DPLR path: Wb, Q . Gamma, A . dec, K . dec
+// [C][DK] each, Ub [C][DV], A_qa and A_qk [C][C], gamma_C [DK]
+constexpr size_t dplr_generic_rec_floats(int dk, int dv, int C) {
+    return (size_t)C * dk * 4 + (size_t)C * dv + 2 * (size_t)C * C + dk;
+}
+
 // record of the MFMA path (bf16 operand fragments + fp32 gamma_C); offsets in
 // bytes, see kda_chunk_fast.hip for the fragment orders
 namespace fast {
@@ -78,7 +84,8 @@ inline int pick_seg_chunks(int cap, int H) {
 // recs       H x cap chunk records (MFMA path), cap x H (fp32 path)
 // sstart     seg_cap x H x 128 x 128 fp32: state entering each segment
 // rm         seg_cap x H x 128 x 256 fp32: [R | M] of each segment
-inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, bool fast) {
+inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, bool fast,
+                          bool dplr = false) {
     WsLayout L{};
     L.cap = chunk_capacity(B, T, N, C);
     if (L.cap < 0) { L.total = 0; return L; }
@@ -90,7 +97,8 @@ inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, boo
     L.seg_cap = fast ? (L.cap + L.seg_chunks - 1) / L.seg_chunks + (N > 0 ? N : 1) : 0;
     L.off_segs = align_up(L.off_seqsegs + n1 * 8, 256);
     L.off_recs = align_up(L.off_segs + (size_t)L.seg_cap * 16, 256);
-    L.rec_bytes = fast ? (size_t)fast::REC_BYTES : generic_rec_floats(dk, dv, C) * 4;
+    L.rec_bytes = dplr ? dplr_generic_rec_floats(dk, dv, C) * 4
+                : fast ? (size_t)fast::REC_BYTES : generic_rec_floats(dk, dv, C) * 4;
     L.off_sstart = align_up(L.off_recs + (size_t)L.cap * H * L.rec_bytes, 256);
     L.off_rm = align_up(L.off_sstart + (size_t)L.seg_cap * H * 128 * 128 * 4, 256);
     L.total = L.off_rm + (size_t)L.seg_cap * H * 128 * 256 * 4;
@@ -119,6 +127,7 @@ struct ChunkArgs {
     const void* gate; const float* norm_w; float rms_eps;
     const float* conv_w; const void* conv_state0; float l2_eps;
     int mode;                  // kModeKDA, kModeGLA or kModeDeltaNet
+    const void* la; const void* lb;   // general DPLR only: the low-rank pair a, b [.., DK]
 };
 
 // launchers (return hipError_t of the launches)
@@ -145,6 +154,10 @@ hipError_t launch_layer_step(const void* q_in, const void* k_in, const void* v_i
                              const float* A, float* state, const void* gate, const float* norm_w,
                              float l2_eps, float rms_eps, void* y, int N, int H, int d,
                              int dtype_bf16, hipStream_t s);
+hipError_t launch_dplr_generic(const ChunkArgs& a, int dtype_bf16);
+hipError_t launch_dplr_decode(const void* q, const void* k, const void* v, const void* la,
+                              const void* lb, const float* z, const float* A, float* state,
+                              void* o, int N, int H, int d, int dtype_bf16, hipStream_t s);
 hipError_t launch_fold(const void* k, const void* v, const float* z, const float* b,
                        const float* A, const int* n_accept, float* state, int N, int W, int H,
                        int dk, int dv, int dtype_bf16, hipStream_t s);

@@ -237,6 +237,51 @@ KDA_API kda_status_t kda_recurrent_step_mode(const void* q, const void* k, const
                                              kda_mode_t mode, void* stream);
 
 /*
+ * General diagonal-plus-low-rank (DPLR) update.  [K3-ATTN §2.2] writes the
+ * KDA step as three steps (decay, a rank-1 correction, the write) and credits
+ * binding the diagonal and low-rank terms to one key with halving the chunk
+ * matrices.  These entry points lift the binding: the rank-1 correction has
+ * its own pair (a_t, b_t) and the write its own key k_t,
+ *   S'  = Diag(alpha_t) S_{t-1}          alpha_t as in (1)
+ *   S'' = S' + a_t (b_t^T S')
+ *   S_t = S'' + k_t v_t^T,   o_t = S_t^T q_t.
+ * KDA is the case a = -beta k, b = k with write key beta k.  There is no
+ * write-strength logit (it is folded into a and k).  The chunked form needs
+ * four C x C matrices (A_ba, A_bk, A_qa, A_qk) where KDA needs two.
+ *
+ *   q, k, a, b   [B, T, H, dk]  dtype
+ *   v            [B, T, H, dv]  dtype
+ *   g_logits     [B, T, H, dk]  fp32     A [H] fp32
+ *   h0, hT, cu_seqlens, o, the batch layout, empty sequences, chunking and
+ *   the workspace rules: as kda_chunk_fwd, with the workspace sized by
+ *   kda_dplr_chunk_fwd_workspace_bytes.
+ * Supported shapes: as kda_chunk_fwd.  Results are unspecified (not an
+ * error) when I - A_ba is ill-conditioned, i.e. when the low-rank steps
+ * amplify the state strongly.
+ */
+KDA_API size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                  int chunk, kda_dtype_t dtype);
+KDA_API kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v,
+                                        const void* a, const void* b, const float* g_logits,
+                                        const float* A, const float* h0,
+                                        const int* cu_seqlens, int B, int T, int H, int dk,
+                                        int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                        float* hT, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * One DPLR token per sequence, state updated in place (layouts as
+ * kda_recurrent_step, plus a, b [N, H, dk] dtype).  One pass over
+ * S' = Diag(alpha) S forms x = S'^T b and r = S'^T q; then
+ * S = S' + a x^T + k v^T and o = r + (q . a) x + (q . k) v.
+ */
+KDA_API kda_status_t kda_dplr_recurrent_step(const void* q, const void* k, const void* v,
+                                             const void* a, const void* b,
+                                             const float* g_logits, const float* A,
+                                             float* state, void* o, int N, int H, int dk,
+                                             int dv, kda_dtype_t dtype, void* stream);
+
+/*
  * The KDA layer between its projections: the core with the steps either side
  * of it that act on one token-head row.
  *

@@ -176,6 +176,27 @@ def make_decode(case: DecodeCase, device="cpu", seed: int = 0,
     return dict(A=A, state=state, steps=per_step, N=n, H=H, dk=dk, dv=dv, dtype=case.dtype)
 
 
+def make_dplr(case: PrefillCase, device="cpu", seed: int = 0, T: Optional[int] = None,
+              lengths: Optional[list] = None) -> dict:
+    """A prefill draw (make_prefill) extended with the low-rank pair of the
+    general DPLR update: la = -sigmoid(b) * a_hat and lb = unit(a_hat + 0.5 n / sqrt(dk)),
+    with a_hat a unit direction and n standard normal, so that b leans on a
+    (the erase is strong) without being tied to it or to the write key k.
+    Both [B, T, H, dk] in the config dtype.  The beta logits b of the draw
+    only set the erase strength."""
+    d = make_prefill(case, device=device, seed=seed, T=T, lengths=lengths)
+    dev = torch.device(device)
+    gen = _gen(dev, seed + 104729)
+    dt = dtype_of(case.dtype)
+    f32 = torch.float32
+    B, Ttot, H, dk = d["B"], d["T"], d["H"], d["dk"]
+    ah = _unit_rows(torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32))
+    nz = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32)
+    d["lb"] = _unit_rows(ah + 0.5 * nz / dk ** 0.5).to(dt)
+    d["la"] = (-torch.sigmoid(d["b"].to(f32))[..., None] * ah).to(dt)
+    return d
+
+
 def make_layer(case: PrefillCase, device="cpu", seed: int = 0, T: Optional[int] = None,
                lengths: Optional[list] = None, conv_state: bool = True) -> dict:
     """A prefill draw (make_prefill) extended with the layer's inputs:

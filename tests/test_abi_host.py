@@ -203,3 +203,33 @@ def test_mode_entry_points_validate_the_mode(L):
     assert step(*[FAKE] * 8, 4, 2, 128, 128, 1, 3, None) == 1
     assert step(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 4, 2, 128, 128, 1, 0, None) == 1
     assert step(None, None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 2, None) == 0
+
+
+def test_dplr_entry_points_reject_bad_arguments(L):
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fn = L.kda_dplr_chunk_fwd
+    fn.restype = i
+    fn.argtypes = [vp] * 9 + [i] * 8 + [vp, vp, vp, sz, vp]
+
+    def call(ptrs=None, **kw):
+        a = dict(B=1, T=64, H=2, dk=16, dv=16, N=1, chunk=16, dtype=0, ws=None, wsb=0)
+        a.update(kw)
+        p = [FAKE] * 7 + [None, None] if ptrs is None else ptrs
+        return fn(*p, a["B"], a["T"], a["H"], a["dk"], a["dv"], a["N"], a["chunk"], a["dtype"],
+                  FAKE, None, a["ws"], a["wsb"], None)
+
+    assert call(dk=96, dv=96) == 2
+    assert call(dtype=4) == 1
+    assert call([FAKE] * 3 + [None] + [FAKE] * 3 + [None, None]) == 1    # a missing
+    assert call([FAKE] * 4 + [None] + [FAKE] * 2 + [None, None]) == 1    # b missing
+    assert call() == 3                                                   # no workspace
+    L.kda_dplr_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    assert L.kda_dplr_chunk_fwd_workspace_bytes(1, 64, 2, 16, 16, 1, 16, 0) > 0
+    assert L.kda_dplr_chunk_fwd_workspace_bytes(1, 64, 2, 96, 96, 1, 16, 0) == 0
+    st = L.kda_dplr_recurrent_step
+    st.restype = i
+    st.argtypes = [vp] * 9 + [i] * 5 + [vp]
+    assert st(*[FAKE] * 9, 4, 2, 96, 96, 1, None) == 2
+    assert st(*([FAKE] * 3 + [None] + [FAKE] * 5), 4, 2, 128, 128, 1, None) == 1
+    assert st(*[None] * 9, 0, 2, 128, 128, 1, None) == 0

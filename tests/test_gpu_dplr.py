@@ -1,0 +1,144 @@
+"""GPU parity of the general DPLR entry points against the oracle's
+`recurrence_dplr_general` (pinned on the CPU: it reduces to KDA, matches the
+explicit-matrix form, the GLA closed form without its low-rank term, and
+the four-matrix chunked form).
+
+The update generalises the three steps of [K3-ATTN §2.2] with its own
+low-rank pair (a, b) and write key k: S' = Diag(alpha) S,
+S'' = S' + a (b^T S'), S = S'' + k v^T, o = S^T q.
+Page tags: [K3-ATTN] "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构".
+"""
+import pytest
+import torch
+
+import kda_inputs as KI
+import oracle
+from kda_testutil import TOL_BF16, TOL_F32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_77_amd as m
+    m.lib()
+    return m
+
+
+def _report(tag, **errs):
+    print(f"[dplr] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def _dev(d):
+    keys = ("q", "k", "v", "la", "lb", "z", "A", "h0", "cu_seqlens")
+    return {x: (d[x].cuda().contiguous() if d.get(x) is not None else None) for x in keys}
+
+
+def _gpu(kda, g, chunk):
+    return kda.kda_dplr_chunk_fwd(g["q"], g["k"], g["v"], g["la"], g["lb"], g["z"], g["A"],
+                                  initial_state=g["h0"], cu_seqlens=g["cu_seqlens"],
+                                  chunk_size=chunk)
+
+
+def _oracle(d, bi, sl, h0, heads=None):
+    hs = slice(None) if heads is None else list(heads)
+    pick = lambda x: x[bi, sl][:, hs].cpu()   # noqa: E731
+    return oracle.recurrence_dplr_general(pick(d["q"]), pick(d["k"]), pick(d["v"]),
+                                          pick(d["la"]), pick(d["lb"]), pick(d["z"]),
+                                          d["A"].cpu()[hs], None if h0 is None else h0.cpu()[hs])
+
+
+@pytest.mark.parametrize("dtype,dk,chunk,B,T,H", [("fp32", 16, 16, 2, 100, 2),
+                                                   ("fp32", 64, 64, 1, 150, 2),
+                                                   ("bf16", 16, 16, 1, 90, 3),
+                                                   ("bf16", 128, 64, 2, 300, 3)])
+def test_dplr_prefill_vs_oracle(kda, dtype, dk, chunk, B, T, H):
+    case = KI.PrefillCase("dplr", H=H, dk=dk, dv=dk, chunk=chunk, dtype=dtype, B=B, T=T,
+                          zero_h0=False)
+    d = KI.make_dplr(case, seed=51)
+    o, hT = _gpu(kda, _dev(d), chunk)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    for bi in range(B):
+        ro, rS = _oracle(d, bi, slice(0, T), d["h0"][bi])
+        eo, eS = rel_err(o[bi], ro), rel_err(hT[bi], rS)
+        _report(f"{dtype} d={dk} C={chunk} B={B} T={T} seq {bi}", o=eo, hT=eS)
+        assert eo <= tol and eS <= tol
+
+
+@pytest.mark.parametrize("dtype,dk,chunk", [("bf16", 128, 64), ("fp32", 16, 16)])
+def test_dplr_packed_vs_oracle(kda, dtype, dk, chunk):
+    """Packed batch with an empty sequence, a one-token sequence and ragged tails."""
+    case = KI.PrefillCase("dplrvar", H=2, dk=dk, dv=dk, chunk=chunk, dtype=dtype, n_seqs=4,
+                          len_lo=1, len_hi=200, zero_h0=False)
+    lens = [130, 0, 1, 77]
+    d = KI.make_dplr(case, seed=52, lengths=lens)
+    o, hT = _gpu(kda, _dev(d), chunk)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    cu = [int(x) for x in d["cu_seqlens"].tolist()]
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s].cpu(), d["h0"][s])
+            continue
+        ro, rS = _oracle(d, 0, slice(cu[s], cu[s + 1]), d["h0"][s])
+        eo, eS = rel_err(o[0, cu[s]:cu[s + 1]], ro), rel_err(hT[s], rS)
+        _report(f"packed {dtype} seq {s} (len {n})", o=eo, hT=eS)
+        assert eo <= tol and eS <= tol
+
+
+def test_dplr_without_initial_state_and_split_resume(kda):
+    """No h0 (zeros), and a run split at a chunk-unaligned point resumes from
+    the returned state to the same result."""
+    case = KI.PrefillCase("dplrres", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=250,
+                          zero_h0=True)
+    d = KI.make_dplr(case, seed=53)
+    g = _dev(d)
+    o, hT = _gpu(kda, g, 64)
+    cut = 101
+    part = lambda x, sl: x[:, sl].contiguous()   # noqa: E731
+    g1 = {x: (part(g[x], slice(0, cut)) if x in ("q", "k", "v", "la", "lb", "z") else g[x])
+          for x in g}
+    g2 = {x: (part(g[x], slice(cut, None)) if x in ("q", "k", "v", "la", "lb", "z") else g[x])
+          for x in g}
+    o1, h1 = _gpu(kda, g1, 64)
+    g2["h0"] = h1
+    o2, h2 = _gpu(kda, g2, 64)
+    torch.cuda.synchronize()
+    ro, rS = _oracle(d, 0, slice(0, 250), None)
+    e = dict(o=rel_err(o[0], ro), hT=rel_err(hT[0], rS),
+             o_split=rel_err(torch.cat([o1, o2], 1)[0], ro), hT_split=rel_err(h2[0], rS))
+    _report("no h0 / split at 101", **e)
+    assert all(x <= TOL_BF16 for x in e.values())
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("fp32", 32)])
+def test_dplr_decode_vs_oracle_and_prefill(kda, dtype, dk):
+    """Each decode step against the oracle's step, and the steps together
+    against a prefill over the same tokens."""
+    N, H, steps = 5, 3, 9
+    case = KI.PrefillCase("dplrdec", H=H, dk=dk, dv=dk, chunk=16 if dk < 128 else 64,
+                          dtype=dtype, B=N, T=steps, zero_h0=False)
+    d = KI.make_dplr(case, seed=54)
+    g = _dev(d)
+    st = g["h0"].clone()
+    S = d["h0"]
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    outs = []
+    for t in range(steps):
+        tk = lambda x: g[x][:, t].contiguous()   # noqa: E731
+        outs.append(kda.kda_dplr_recurrent_step(tk("q"), tk("k"), tk("v"), tk("la"), tk("lb"),
+                                                tk("z"), g["A"], st))
+        hk = lambda x: d[x][:, t]                # noqa: E731
+        ro, S = oracle.decode_step_dplr(hk("q"), hk("k"), hk("v"), hk("la"), hk("lb"), hk("z"),
+                                        d["A"], S)
+        torch.cuda.synchronize()
+        assert rel_err(outs[-1], ro) <= tol
+    assert rel_err(st, S) <= tol
+    op, hp = _gpu(kda, g, case.chunk)
+    torch.cuda.synchronize()
+    e1, e2 = rel_err(torch.stack(outs, 1), op), rel_err(st, hp)
+    _report(f"decode {dtype} d={dk} vs prefill", o=e1, state=e2)
+    assert e1 <= tol and e2 <= tol
