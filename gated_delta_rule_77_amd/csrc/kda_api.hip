@@ -214,7 +214,8 @@ size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, i
                                           kda_dtype_t dtype) {
     if (!dtype_ok(dtype) || !prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return 0;
     if (!chunk_shape_supported(dk, dv, chunk)) return 0;
-    return ws_layout(B, T, H, dk, dv, N, chunk, false, true).total;
+    const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
+    return ws_layout(B, T, H, dk, dv, N, chunk, fast, true).total;
 }
 
 kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a,
@@ -230,7 +231,8 @@ kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, con
     if ((long long)B * T > 0 && (!q || !k || !v || !a || !b || !g_logits || !o))
         return KDA_ERR_INVALID_ARG;
     if (!A) return KDA_ERR_INVALID_ARG;
-    const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, false, true);
+    const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
+    const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, fast, true);
     if (L.total == 0) return KDA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
@@ -241,7 +243,7 @@ kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, con
     c.o = o; c.hT = hT; c.ws = static_cast<uint8_t*>(workspace); c.L = L;
     c.stream = static_cast<hipStream_t>(stream);
     hipError_t e = launch_prep(c);
-    if (e == hipSuccess) e = launch_dplr_generic(c, dtype == KDA_BF16);
+    if (e == hipSuccess) e = fast ? launch_fast_dplr(c) : launch_dplr_generic(c, dtype == KDA_BF16);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -36,59 +36,22 @@
 // column factor e^{G_ref - G_j} <= 1 off the diagonal and < e^{80} on it.
 // Gamma, Kbar and gamma_C only ever carry factors <= 1.
 #include "kda_device.hpp"
+#include "kda_fast_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 
 using namespace fast;
+using namespace fastc;
 
 namespace {
 
-// acc += A (16x16, row-major, lda) * B (16x16, row-major, ldb), fp32 MFMA
-__device__ __forceinline__ f32x4 mm16_f32(f32x4 acc, const float* A, int lda, const float* B,
-                                          int ldb, int n16, int g4) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-        acc = mfma_f32(A[n16 * lda + 4 * ks + g4], B[(4 * ks + g4) * ldb + n16], acc);
-    return acc;
-}
-
-__device__ __forceinline__ void load8f(const float* p, float* out) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-}
-
-// LDS row strides (elements), padded so that 16-byte fragment reads whose
-// rows vary across lanes fall on distinct banks: 528-byte fp32 rows of L and
-// K.F, 272-byte bf16 rows, 272-byte rows of the 64x64 fp32 matrices.
-constexpr int kLdG = 132;   // fp32 [64][kLdG]: L, then K.F in place
-constexpr int kLdK = 136;   // bf16 row operands [64][kLdK]
-constexpr int kLdA = 68;    // fp32 64x64 matrices [64][kLdA]
-// per-channel factor rows (fp32 [128] each); L_s(r) = L at row 16r - 1
-// (0 for r = 0), L_e(r) = L at row 16r + 15, L_C = L at row 63:
-constexpr int kFX = 0;      // X(r,s) = 2^(L_s(r) - L_e(s)), row r(r+1)/2 + s, s <= r
-constexpr int kFY = 10;     // Y(r) = 2^L_s(r)
-constexpr int kFZ = 14;     // Z(r) = 2^(L_C - L_e(r))
-constexpr int kFL = 18;     // L_e(r) itself
-constexpr int kNFac = 22;
 constexpr int kOffRK = 64 * kLdG * 4;
 constexpr int kOffRQ = kOffRK + 64 * kLdK * 2;
 constexpr int kOffFac = kOffRQ + 64 * kLdK * 2;
 constexpr int kOffBeta = kOffFac + kNFac * 128 * 4;
 constexpr int kSmemIntra = kOffBeta + 64 * 4;            // 80128 bytes: two workgroups per CU
 static_assert(3 * 64 * kLdA * 4 + 4 * 256 * 4 <= kOffFac, "A_kk, A_qk, N and P alias L/K.F and the row operands");
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 16x16 tile pairs (r, s), s <= r, numbered p = r(r+1)/2 + s; wave w takes
-// p in [pair_beg(w), pair_beg(w + 1)): 3, 3, 2 and 2 tiles.
-__device__ __forceinline__ int pair_beg(int w) { return w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : w == 3 ? 8 : 10; }
-__device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
 
 // One workgroup per (chunk, head), 4 waves.  Work on single elements is split
 // by channel: wave w owns channels [32w, 32w + 32) of all 64 tokens, lane
@@ -428,42 +391,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
 
     // ---- 4. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
-    // diagonal blocks: forward substitution, lane = (block, column)
-    if (w == 0) {
-        const int rb = g4, cc = n16;
-        const float* Ab = sAkk + (16 * rb) * kLdA + 16 * rb;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            float acc = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; m++) acc -= Ab[i * kLdA + m] * x[m];
-            x[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; i++) sN[(16 * rb + i) * kLdA + 16 * rb + cc] = x[i];
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance d: N_rs = -N_rr sum_{m=s}^{r-1} A_rm N_ms
-    for (int d = 1; d < 4; d++) {
-        const bool act = w < 4 - d;
-        const int r = w + d, s = w;
-        if (act) {
-            f32x4 P = zero4();
-            for (int m = s; m < r; m++)
-                P = mm16_f32(P, sAkk + 16 * r * kLdA + 16 * m, kLdA, sN + 16 * m * kLdA + 16 * s, kLdA,
-                             n16, g4);
-#pragma unroll
-            for (int e = 0; e < 4; e++) sP[w * 256 + (4 * g4 + e) * 16 + n16] = P[e];
-        }
-        __syncthreads();
-        if (act) {
-            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * kLdA + 16 * r, kLdA, sP + w * 256, 16, n16, g4);
-#pragma unroll
-            for (int e = 0; e < 4; e++) sN[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = -R[e];
-        }
-        __syncthreads();
-    }
+    unit_lower_inverse(sAkk, sN, sP, w, n16, g4);
     if (DBG)
         for (int idx = tid; idx < 4096; idx += 256)
             dbase[8192 + 8192 + idx] = sN[(idx >> 6) * kLdA + (idx & 63)] * sBeta[idx & 63];
@@ -549,29 +477,41 @@ constexpr int kOutNS = 8;       // 16-column slices
 constexpr int kOutDepth = 3;    // record prefetch ring depth (chunks)
 constexpr int kLdO = 136;       // bf16 output staging rows [64][kLdO]
 
+// per wave and chunk; KDA uses a (A_qk), DPLR c (Cs), the rest is common
 struct OutFrags {
-    bf16x8 w[4], q[4];          // -W^T, (Q . Gamma)^T of token block w, k-steps 0..3
-    bf16x8 k[4];                // Kbar^T rows [32w, 32w + 32): [16-row half][token kstep]
+    bf16x8 w[4], q[4];          // -W^T (Wb^T), (Q . Gamma)^T (Q'^T) of token block w, k-steps 0..3
+    bf16x8 k[4];                // Kbar^T (Abar^T) rows [32w, 32w + 32): [16-row half][token kstep]
     bf16x8 a[2];                // A_qk rows of token block w, token k-steps 0..1
-    bf16x4 u[kOutNS];           // U tiles of token block w
+    bf16x4 u[kOutNS];           // U (Uo) tiles of token block w
+    bf16x4 c[2][kOutNS];        // Cs tiles of the wave's two row tiles
     float4 g0, g1;              // gamma_C for the wave's two row tiles
 };
 
+template <bool DPLR>
 __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __restrict__ rec, int w,
                                                int lane, int g4) {
+    using RL = RecLayout<DPLR>;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_W + ((w * 4 + ks) * 64 + lane) * 16);
-        f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_K + ((w * 4 + ks) * 64 + lane) * 16);
-        f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + REC_Q + ((w * 4 + ks) * 64 + lane) * 16);
+        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::W + ((w * 4 + ks) * 64 + lane) * 16);
+        f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::K + ((w * 4 + ks) * 64 + lane) * 16);
+        f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::Q + ((w * 4 + ks) * 64 + lane) * 16);
+    }
+    if constexpr (DPLR) {
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int sl = 0; sl < kOutNS; sl++)
+                f.c[b][sl] = *reinterpret_cast<const bf16x4*>(rec + RL::C + (((2 * w + b) * 8 + sl) * 64 + lane) * 8);
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+            f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + RL::A + ((w * 2 + kb) * 64 + lane) * 16);
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-        f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16);
-#pragma unroll
     for (int sl = 0; sl < kOutNS; sl++)
-        f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + REC_U + ((sl * 4 + w) * 64 + lane) * 8);
-    const float* gC = reinterpret_cast<const float*>(rec + REC_G);
+        f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + RL::U + ((sl * 4 + w) * 64 + lane) * 8);
+    const float* gC = reinterpret_cast<const float*>(rec + RL::G);
     f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
 }
@@ -585,8 +525,10 @@ struct OutGate {
     float eps;
 };
 
-// One chunk for one wave over all slices.
-template <bool DBG, bool GATE>
+// One chunk for one wave over all slices.  KDA: V~ = U - W S,
+// O = (Q . Gamma) S + A_qk V~, S <- Diag(gamma_C) S + Kbar^T V~.  DPLR:
+// X~ = Wb S, O = Q' S + Uo, S <- Diag(gamma_C) S + Abar^T X~ + Cs.
+template <bool DBG, bool GATE, bool DPLR>
 __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, int len,
                                          f32x4 (&accS)[kOutNS][2], bf16* sS, bf16* sVt, bf16* sO,
                                          bf16* __restrict__ o, float* __restrict__ dbgS, int H,
@@ -616,8 +558,8 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
 #pragma unroll
         for (int s4 = 0; s4 < 4; s4++) {
             const int sl = 4 * bb + s4;
-            f32x4 accV = unpack4(f.u[sl]);
-            f32x4 acc = zero4();
+            f32x4 accV = DPLR ? zero4() : unpack4(f.u[sl]);
+            f32x4 acc = DPLR ? unpack4(f.u[sl]) : zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
                 accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
@@ -639,12 +581,16 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
         f32x4& s1 = accS[sl][1];
         s0[0] *= f.g0.x; s0[1] *= f.g0.y; s0[2] *= f.g0.z; s0[3] *= f.g0.w;
         s1[0] *= f.g1.x; s1[1] *= f.g1.y; s1[2] *= f.g1.z; s1[3] *= f.g1.w;
+        if constexpr (DPLR) {
+            s0 += unpack4(f.c[0][sl]);
+            s1 += unpack4(f.c[1][sl]);
+        }
         f32x4 acc = accO[sl];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             s0 = mfma_bf16(f.k[kb], vfr[kb], s0);
             s1 = mfma_bf16(f.k[2 + kb], vfr[kb], s1);
-            acc = mfma_bf16(f.a[kb], vfr[kb], acc);
+            if constexpr (!DPLR) acc = mfma_bf16(f.a[kb], vfr[kb], acc);
         }
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(s0, s1);
 #pragma unroll
@@ -683,7 +629,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
 
 // grid: seg_cap * H blocks, block = (segment, head).  With GATE the rows
 // stored are the layer's gated RMSNorm of O instead of O.
-template <bool DBG, bool GATE>
+template <bool DBG, bool GATE, bool DPLR>
 __global__ __launch_bounds__(256, 1)
 void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
                     const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
@@ -730,11 +676,11 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
     for (int e = 0; e < 8; e++) og.w[e] = GATE ? norm_w[(tid & 15) * 8 + e] : 0.f;
 
     constexpr int D = kOutDepth;
-    auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * REC_BYTES; };
+    auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * RecLayout<DPLR>::BYTES; };
     OutFrags F[D];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < D - 1; u++) load_out_frags(F[u], rec(min(u, nch - 1)), w, lane, g4);
+        for (int u = 0; u < D - 1; u++) load_out_frags<DPLR>(F[u], rec(min(u, nch - 1)), w, lane, g4);
     }
     __syncthreads();
     const int nfull = nch / D * D;
@@ -742,9 +688,9 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 #pragma unroll
         for (int u = 0; u < D; u++) {
             // unconditional prefetch (index clamped) keeps the wait counts exact
-            load_out_frags(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
+            load_out_frags<DPLR>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
             const int t0 = (ci + u) * C;
-            out_step<DBG, GATE>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
+            out_step<DBG, GATE, DPLR>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
                                 dbgS, H, h, w, lane, n16, g4, tid, og);
         }
     }
@@ -752,7 +698,7 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            out_step<DBG, GATE>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
+            out_step<DBG, GATE, DPLR>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
                                 o, dbgS, H, h, w, lane, n16, g4, tid, og);
         }
 
@@ -778,36 +724,56 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 // workgroup copies them into a double-buffered LDS stage, two chunks ahead
 // through registers, with one barrier per chunk.
 constexpr int kTS = 16;                          // slices of [R | M]
-constexpr int kStW = 0, kStK = 16384, kStU = 32768, kStG = 49152;
-constexpr int kStageBytes = 49664;               // W, Kbar, U fragments and gamma_C of one chunk
-
-// the 16-byte pieces of a record's W, Kbar, U and gamma_C that thread t copies
-typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
-struct StageRegs {
-    u32x4 w0, w1, k0, k1, u0, u1, g;
+// stage of one chunk: W, Kbar, U (KDA) or Cs (DPLR) and gamma_C
+template <bool DPLR> struct TransStage {
+    static constexpr int W = 0, K = 16384, U = 32768, C = 32768;
+    static constexpr int G = DPLR ? 65536 : 49152;
+    static constexpr int BYTES = G + 512;
 };
 
+// the 16-byte pieces of a record's stage that thread t copies
+typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
+struct StageRegs {
+    u32x4 w0, w1, k0, k1, x0, x1, x2, x3, g;      // x: U (two pieces) or Cs (four)
+};
+
+template <bool DPLR>
 __device__ __forceinline__ StageRegs stage_load(const uint8_t* __restrict__ rec, int t) {
+    using RL = RecLayout<DPLR>;
     auto ld = [&](int off) { return *reinterpret_cast<const u32x4*>(rec + off + t * 16); };
     StageRegs r;
-    r.w0 = ld(REC_W); r.w1 = ld(REC_W + 8192);
-    r.k0 = ld(REC_K); r.k1 = ld(REC_K + 8192);
-    r.u0 = ld(REC_U); r.u1 = ld(REC_U + 8192);
-    r.g = *reinterpret_cast<const u32x4*>(rec + REC_G + (t & 31) * 16);
+    r.w0 = ld(RL::W); r.w1 = ld(RL::W + 8192);
+    r.k0 = ld(RL::K); r.k1 = ld(RL::K + 8192);
+    if constexpr (DPLR) {
+        r.x0 = ld(RL::C); r.x1 = ld(RL::C + 8192); r.x2 = ld(RL::C + 16384); r.x3 = ld(RL::C + 24576);
+    } else {
+        r.x0 = ld(RL::U); r.x1 = ld(RL::U + 8192);
+    }
+    r.g = *reinterpret_cast<const u32x4*>(rec + RL::G + (t & 31) * 16);
     return r;
 }
 
+template <bool DPLR>
 __device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int t) {
+    using TS = TransStage<DPLR>;
     auto stv = [&](int off, u32x4 x) { *reinterpret_cast<u32x4*>(st + off + t * 16) = x; };
-    stv(kStW, r.w0); stv(kStW + 8192, r.w1);
-    stv(kStK, r.k0); stv(kStK + 8192, r.k1);
-    stv(kStU, r.u0); stv(kStU + 8192, r.u1);
-    if (t < 32) *reinterpret_cast<u32x4*>(st + kStG + t * 16) = r.g;
+    stv(TS::W, r.w0); stv(TS::W + 8192, r.w1);
+    stv(TS::K, r.k0); stv(TS::K + 8192, r.k1);
+    if constexpr (DPLR) {
+        stv(TS::C, r.x0); stv(TS::C + 8192, r.x1); stv(TS::C + 16384, r.x2); stv(TS::C + 24576, r.x3);
+    } else {
+        stv(TS::U, r.x0); stv(TS::U + 8192, r.x1);
+    }
+    if (t < 32) *reinterpret_cast<u32x4*>(st + TS::G + t * 16) = r.g;
 }
 
-// One chunk for wave w from the staged record.
+// One chunk for wave w from the staged record.  KDA: V~ = U - W S (U = 0 for
+// M), S <- Diag(gamma_C) S + Kbar^T V~.  DPLR: X~ = Wb S,
+// S <- Diag(gamma_C) S + Abar^T X~ + Cs (Cs for R only).
+template <bool DPLR>
 __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2], int w, int lane,
                                             int g4) {
+    using TS = TransStage<DPLR>;
     // S fragments of k-step ks: row tiles 2ks, 2ks + 1 of each owned slice
     bf16x8 sf[4][2];
 #pragma unroll
@@ -821,13 +787,13 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             vt[tb][j] = zero4();
-            if (w < 4)
+            if (!DPLR && w < 4)
                 vt[tb][j] = unpack4(*reinterpret_cast<const bf16x4*>(
-                    st + kStU + (((2 * w + j) * 4 + tb) * 64 + lane) * 8));
+                    st + TS::U + (((2 * w + j) * 4 + tb) * 64 + lane) * 8));
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
-            const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + kStW + ((tb * 4 + ks) * 64 + lane) * 16);
+            const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + TS::W + ((tb * 4 + ks) * 64 + lane) * 16);
 #pragma unroll
             for (int j = 0; j < 2; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
         }
@@ -838,16 +804,19 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int j = 0; j < 2; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
-    const float* gC = reinterpret_cast<const float*>(st + kStG);
+    const float* gC = reinterpret_cast<const float*>(st + TS::G);
 #pragma unroll
     for (int rt = 0; rt < 8; rt++) {
         const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(st + kStK + ((rt * 2 + 0) * 64 + lane) * 16);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(st + kStK + ((rt * 2 + 1) * 64 + lane) * 16);
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 0) * 64 + lane) * 16);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             f32x4& a = acc[rt][j];
             a[0] *= g.x; a[1] *= g.y; a[2] *= g.z; a[3] *= g.w;
+            if (DPLR && w < 4)
+                a += unpack4(*reinterpret_cast<const bf16x4*>(
+                    st + TS::C + ((rt * 8 + 2 * w + j) * 64 + lane) * 8));
             a = mfma_bf16(k0, vf[0][j], a);
             a = mfma_bf16(k1, vf[1][j], a);
         }
@@ -855,6 +824,7 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
 }
 
 // grid: seg_cap * H blocks, block = (segment, head)
+template <bool DPLR>
 __global__ __launch_bounds__(512, 1)
 void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
                       const int2* __restrict__ seqsegs, const int* __restrict__ hdr, int H,
@@ -870,7 +840,7 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
 
-    __shared__ __align__(16) uint8_t stage[2][kStageBytes];
+    __shared__ __align__(16) uint8_t stage[2][TransStage<DPLR>::BYTES];
 
     f32x4 acc[8][2];        // R from 0, M from the identity
 #pragma unroll
@@ -883,25 +853,27 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
                 acc[rt][j][e] = (row == col - 128) ? 1.f : 0.f;
             }
     if (nch > 0) {
-        auto rec = [&](int c) { return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * REC_BYTES; };
+        auto rec = [&](int c) {
+            return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * RecLayout<DPLR>::BYTES;
+        };
         // chunk c sits in stage c & 1; its copy passes through register set c & 1
-        StageRegs R0 = stage_load(rec(0), tid);
-        StageRegs R1 = stage_load(rec(1), tid);
-        stage_store(R0, stage[0], tid);
-        R0 = stage_load(rec(2), tid);
+        StageRegs R0 = stage_load<DPLR>(rec(0), tid);
+        StageRegs R1 = stage_load<DPLR>(rec(1), tid);
+        stage_store<DPLR>(R0, stage[0], tid);
+        R0 = stage_load<DPLR>(rec(2), tid);
         __syncthreads();
         int c = 0;
         for (; c + 2 <= nch; c += 2) {
-            trans_chunk(stage[0], acc, w, lane, g4);
-            stage_store(R1, stage[1], tid);          // chunk c + 1
-            R1 = stage_load(rec(c + 3), tid);
+            trans_chunk<DPLR>(stage[0], acc, w, lane, g4);
+            stage_store<DPLR>(R1, stage[1], tid);    // chunk c + 1
+            R1 = stage_load<DPLR>(rec(c + 3), tid);
             __syncthreads();
-            trans_chunk(stage[1], acc, w, lane, g4);
-            stage_store(R0, stage[0], tid);          // chunk c + 2
-            R0 = stage_load(rec(c + 4), tid);
+            trans_chunk<DPLR>(stage[1], acc, w, lane, g4);
+            stage_store<DPLR>(R0, stage[0], tid);    // chunk c + 2
+            R0 = stage_load<DPLR>(rec(c + 4), tid);
             __syncthreads();
         }
-        if (c < nch) trans_chunk(stage[0], acc, w, lane, g4);
+        if (c < nch) trans_chunk<DPLR>(stage[0], acc, w, lane, g4);
     }
 #pragma unroll
     for (int rt = 0; rt < 8; rt++)
@@ -1001,7 +973,8 @@ void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_fast(const ChunkArgs& a) {
+template <bool DPLR>
+hipError_t launch_chain(const ChunkArgs& a) {
     const int* hdr = reinterpret_cast<const int*>(a.ws);
     const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
     const int2* seqsegs = reinterpret_cast<const int2*>(a.ws + a.L.off_seqsegs);
@@ -1009,6 +982,39 @@ hipError_t launch_fast(const ChunkArgs& a) {
     uint8_t* recs = a.ws + a.L.off_recs;
     float* sstart = reinterpret_cast<float*>(a.ws + a.L.off_sstart);
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
+    hipError_t e;
+    const dim3 gc((unsigned)((long long)a.L.seg_cap * a.H));
+    hipLaunchKernelGGL((seg_trans_kernel<DPLR>), gc, dim3(512), 0, a.stream, (const uint8_t*)recs,
+                       segs, seqsegs, hdr, a.H, rm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
+    const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
+    hipLaunchKernelGGL(compose_kernel, dim3(cblk), dim3(256), 0, a.stream,
+                       seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
+    const bf16* gate = static_cast<const bf16*>(a.gate);
+#define KDA_OUT(DBG, GATE)                                                                       \
+    hipLaunchKernelGGL((seg_out_kernel<DBG, GATE, DPLR>), gc, dim3(256), 0, a.stream,            \
+                       (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, \
+                       (bf16*)a.o, a.hT, DBG ? a.dbg_state : (float*)nullptr, gate, a.norm_w,    \
+                       a.rms_eps)
+    // the debug and gated variants exist for KDA only (the API enforces it)
+    if constexpr (DPLR) {
+        KDA_OUT(false, false);
+    } else {
+        if (a.dbg_state) KDA_OUT(true, false);
+        else if (gate) KDA_OUT(false, true);
+        else KDA_OUT(false, false);
+    }
+#undef KDA_OUT
+    return hipGetLastError();
+}
+
+hipError_t launch_fast(const ChunkArgs& a) {
+    const int* hdr = reinterpret_cast<const int*>(a.ws);
+    const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
+    uint8_t* recs = a.ws + a.L.off_recs;
     const dim3 gi((unsigned)((long long)a.L.cap * a.H));
     const bf16* cs0 = static_cast<const bf16*>(a.conv_state0);
 #define KDA_INTRA(DBG, CONV, MODE, DBGP)                                                      \
@@ -1025,35 +1031,14 @@ hipError_t launch_fast(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
+    return launch_chain<false>(a);
+}
 
-    const long long pairs = (long long)a.L.seg_cap * a.H;
-    const dim3 gc((unsigned)pairs);
-    hipLaunchKernelGGL(seg_trans_kernel, gc, dim3(512), 0, a.stream, (const uint8_t*)recs, segs,
-                       seqsegs, hdr, a.H, rm);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
-    const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
-    hipLaunchKernelGGL(compose_kernel, dim3(cblk), dim3(256), 0, a.stream,
-                       seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
-    const bf16* gate = static_cast<const bf16*>(a.gate);
-    if (a.dbg_state)
-        hipLaunchKernelGGL((seg_out_kernel<true, false>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
-                           (const float*)sstart, (bf16*)a.o, a.hT, a.dbg_state, gate, a.norm_w,
-                           a.rms_eps);
-    else if (gate)
-        hipLaunchKernelGGL((seg_out_kernel<false, true>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
-                           (const float*)sstart, (bf16*)a.o, a.hT, (float*)nullptr, gate, a.norm_w,
-                           a.rms_eps);
-    else
-        hipLaunchKernelGGL((seg_out_kernel<false, false>), gc, dim3(256), 0, a.stream,
-                           (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,
-                           (const float*)sstart, (bf16*)a.o, a.hT, (float*)nullptr, gate, a.norm_w,
-                           a.rms_eps);
-    return hipGetLastError();
+hipError_t launch_fast_dplr(const ChunkArgs& a) {
+    hipError_t e = launch_dplr_intra(a);
+    if (e != hipSuccess) return e;
+    if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
+    return launch_chain<true>(a);
 }
 
 }  // namespace kda

@@ -1,0 +1,429 @@
+// Intra-chunk kernel of the general DPLR update on MFMA: bf16 inputs,
+// d_k = d_v = 128, chunk C = 64.  The chain kernels are the KDA ones with
+// their DPLR variant (kda_chunk_fast.hip).
+//
+// Update (per sequence and head): S' = Diag(alpha) S, S'' = S' + a (b^T S'),
+// S = S'' + k v^T, o = S^T q -- the three steps of [K3-ATTN §2.2] with the
+// low-rank pair and the write key untied.  With G the in-chunk inclusive
+// cumulative log-decay, Gamma = e^G, e_ij = e^{G_i - G_j}:
+//   A_ba[i,j] = sum_c b_ic a_jc e_ijc (j < i)    A_bk[i,j] = sum_c b_ic k_jc e_ijc (j < i)
+//   A_qa[i,j] = sum_c q_ic a_jc e_ijc (j <= i)   A_qk[i,j] = sum_c q_ic k_jc e_ijc (j <= i)
+//   T = (I - A_ba)^{-1}, Wb = T (B . Gamma), M = T A_bk, Ub = M V
+//   X = Wb S + Ub (the low-rank reads x_i = S'_i^T b_i)
+//   O = (Q . Gamma) S + A_qa X + A_qk V
+//   S <- Diag(Gamma_C) S + Abar^T X + Kbar^T V      (Abar, Kbar: rows decayed to the chunk end)
+// Everything that does not depend on S is folded here, so the chain runs
+//   X~ = Wb S,  O = Q' S + Uo,  S <- Diag(Gamma_C) S + Abar^T X~ + Cs
+// with R = A_qa T, P = R A_bk + A_qk and
+//   Q' = Q . Gamma + R (B . Gamma),  Uo = P V,  Cs = Abar^T Ub + Kbar^T V.
+// Four C x C matrices are formed where KDA forms two: the cost [K3-ATTN §2.2]
+// attributes to untying the low-rank terms from k.
+//
+// Layout of the work: one workgroup of 4 waves per (chunk, head) as in the
+// KDA kernel; wave w owns channels [32w, 32w + 32) in the per-element work.
+// The decay factors are the powers of two of that kernel (row factor
+// E = 2^(L - L_s), column factor F = 2^(L_e - L), per-channel table X, Y, Z).
+// Both column operands (K.F and A.F) stay fp32 in LDS until each tile pair
+// scales them, so one workgroup fills a CU (113 KB of LDS).
+// Sources: [K3-ATTN] "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构" §2.2;
+//          [LA-KDA] "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制" §5.4, §7, §8.
+#include "kda_device.hpp"
+#include "kda_fast_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+using namespace fastc;
+using namespace fast_dplr;
+
+namespace {
+
+// LDS, steps 1-3
+constexpr int kDG = 0;                                  // fp32 [64][kLdG]: L, then K.F
+constexpr int kDAF = kDG + 64 * kLdG * 4;               // fp32 [64][kLdG]: A.F
+constexpr int kDRB = kDAF + 64 * kLdG * 4;              // bf16 [64][kLdK]: B.E
+constexpr int kDRQ = kDRB + 64 * kLdK * 2;              // bf16 [64][kLdK]: Q.E
+constexpr int kDFac = kDRQ + 64 * kLdK * 2;             // fp32 [kNFac][128]
+constexpr int kDSmem = kDFac + kNFac * 128 * 4;         // 113664 bytes
+// LDS from the masks on (aliases the above): fp32 64 x 64 matrices
+constexpr int kMat = 64 * kLdA * 4;
+constexpr int kDNegAba = 0;          // -A_ba, then R = A_qa T
+constexpr int kDAbk = kMat;
+constexpr int kDAqa = 2 * kMat;
+constexpr int kDAqk = 3 * kMat;      // A_qk, then P = R A_bk + A_qk in place
+constexpr int kDT = 4 * kMat;        // T
+constexpr int kDM = 5 * kMat;        // M = T A_bk
+constexpr int kDScr = 6 * kMat;      // 4 x 256 floats of inverse scratch
+static_assert(kDScr + 4096 <= kDSmem, "the matrices fit in the step 1-3 buffers");
+// LDS at the end: Ub and V as token-contracting B fragments of all 8 slices
+constexpr int kDStU = 0;             // [8 slice][2 kstep][64 lane][8] bf16
+constexpr int kDStV = 16384;
+
+// Z (+)= X Y over 16 x 16 tiles of lower-triangular 64 x 64 fp32 matrices in
+// LDS ([64][kLdA]); only tiles (r, s) with s <= r, k-blocks m in [s, r].
+// Wave w takes its tile pairs; the result overwrites Z's tile (which may be
+// Z_init's tile: each tile is read and written by one wave only).
+__device__ __forceinline__ void tri_mm(const float* X, const float* Y, const float* Zinit, float* Z,
+                                       int w, int n16, int g4) {
+    const int pb = pair_beg(w), pe = pair_beg(w + 1);
+    for (int p = pb; p < pe; p++) {
+        const int r = pair_row(p), s = p - r * (r + 1) / 2;
+        f32x4 acc = zero4();
+        if (Zinit) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] = Zinit[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16];
+        }
+        for (int m = s; m <= r; m++)
+            acc = mm16_f32(acc, X + 16 * r * kLdA + 16 * m, kLdA, Y + 16 * m * kLdA + 16 * s, kLdA,
+                           n16, g4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) Z[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = acc[e];
+    }
+}
+
+// token-contracting bf16 fragment of row 16 tb + n16 of a 64 x 64 fp32 matrix
+// (k-slot order of two stacked C tiles: tokens 32 kb + 4 g + e, 32 kb + 16 + 4 g + e)
+__device__ __forceinline__ bf16x8 row_frag(const float* Mx, int tb, int kb, int n16, int g4) {
+    const int row = 16 * tb + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
+    const float4 a = *reinterpret_cast<const float4*>(Mx + row * kLdA + j0);
+    const float4 b = *reinterpret_cast<const float4*>(Mx + row * kLdA + j1);
+    const f32x4 x0 = {a.x, a.y, a.z, a.w}, x1 = {b.x, b.y, b.z, b.w};
+    return pack_frag(x0, x1);
+}
+
+__global__ __launch_bounds__(256, 1)
+void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, const bf16* __restrict__ la,
+                       const bf16* __restrict__ lb, const float* __restrict__ z,
+                       const float* __restrict__ A, const int* __restrict__ hdr,
+                       const int4* __restrict__ chunks, int H, uint8_t* __restrict__ recs)
+{
+    const int cid = blockIdx.x / H, h = blockIdx.x % H;
+    if (cid >= hdr[0]) return;
+    const int4 cd = chunks[cid];
+    const int tok0 = cd.y, len = cd.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    uint8_t* rec = recs + ((size_t)cid * H + h) * RD_BYTES;
+
+    __shared__ __align__(16) uint8_t smem[kDSmem];
+    float* sG = reinterpret_cast<float*>(smem + kDG);
+    float* sAF = reinterpret_cast<float*>(smem + kDAF);
+    bf16* sRB = reinterpret_cast<bf16*>(smem + kDRB);
+    bf16* sRQ = reinterpret_cast<bf16*>(smem + kDRQ);
+    float* sFac = reinterpret_cast<float*>(smem + kDFac);
+
+    const unsigned tstride = (unsigned)H * 128u;
+    const size_t base = (size_t)tok0 * tstride + (size_t)h * 128;
+    const int lastrow = len - 1;
+    auto roff = [&](int row) { return (unsigned)min(row, lastrow) * tstride; };
+    const int cw = 32 * w + 8 * g4;
+
+    // ---- 1. loads; rows past the end of the sequence are zero (no write
+    //      strength switches them off here, unlike KDA's beta)
+    uint4 kr[4], qr[4], vr[4], ar[4], br[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+        const int row = 16 * tt + n16;
+        const unsigned off = roff(row) + cw;
+        kr[tt] = *reinterpret_cast<const uint4*>(k + base + off);
+        qr[tt] = *reinterpret_cast<const uint4*>(q + base + off);
+        vr[tt] = *reinterpret_cast<const uint4*>(v + base + off);
+        ar[tt] = *reinterpret_cast<const uint4*>(la + base + off);
+        br[tt] = *reinterpret_cast<const uint4*>(lb + base + off);
+        if (row >= len) {
+            const uint4 z4 = make_uint4(0, 0, 0, 0);
+            kr[tt] = z4; qr[tt] = z4; vr[tt] = z4; ar[tt] = z4; br[tt] = z4;
+        }
+    }
+    // gate [LA-KDA §5.4] and in-chunk cumulative sum in log2 units
+    const int c = tid & 127, half = tid >> 7;
+    float lr[32];
+    {
+        const float a2 = -expf(A[h]) * kLog2e;     // e^{-e^A z} = 2^(a2 z)
+#pragma unroll
+        for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const int row = 32 * half + i;
+            float sg = __builtin_amdgcn_rcpf(1.f + ex2(lr[i] * a2));
+            sg = row < len ? sg : 0.f;
+            run = fmaf(sg, kGMin * kLog2e, run);
+            lr[i] = run;
+            sG[row * kLdG + c] = run;
+        }
+    }
+    __syncthreads();
+    {
+        float* F = sFac + c;
+        if (half == 0) {
+            const float L15 = lr[15], L31 = lr[31];
+            F[(kFX + 0) * 128] = ex2(-L15);
+            F[(kFX + 1) * 128] = 1.f;
+            F[(kFX + 2) * 128] = ex2(L15 - L31);
+            F[(kFX + 3) * 128] = ex2(L31 - L15);
+            F[(kFX + 4) * 128] = 1.f;
+            F[(kFX + 8) * 128] = 1.f;
+            F[(kFY + 0) * 128] = 1.f;
+            F[(kFY + 1) * 128] = ex2(L15);
+            F[(kFY + 2) * 128] = ex2(L31);
+            F[(kFZ + 3) * 128] = 1.f;
+            F[(kFL + 0) * 128] = L15;
+            F[(kFL + 1) * 128] = L31;
+        } else {
+            const float L15 = sG[15 * kLdG + c], L31 = sG[31 * kLdG + c];
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                lr[i] += L31;
+                sG[(32 + i) * kLdG + c] = lr[i];
+            }
+            const float L47 = lr[15], L63 = lr[31];
+            F[(kFX + 5) * 128] = ex2(L31 - L47);
+            F[(kFX + 6) * 128] = ex2(L47 - L15);
+            F[(kFX + 7) * 128] = ex2(L47 - L31);
+            F[(kFX + 9) * 128] = ex2(L47 - L63);
+            F[(kFY + 3) * 128] = ex2(L47);
+            F[(kFZ + 0) * 128] = ex2(L63 - L15);
+            F[(kFZ + 1) * 128] = ex2(L63 - L31);
+            F[(kFZ + 2) * 128] = ex2(L63 - L47);
+            F[(kFL + 2) * 128] = L47;
+            F[(kFL + 3) * 128] = L63;
+            reinterpret_cast<float*>(rec + RD_G)[c] = ex2(L63);
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. per element: factors, row operands (B.E, Q.E), column operands
+    //      (K.F, A.F, fp32), and by exact selection products the transposed
+    //      fragments (B . Gamma)^T, V, Kbar^T, Abar^T and the (Q . Gamma)^T tiles
+    bf16x8 sel[2];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        sel[0][e] = (bf16)((8 * g4 + e == n16) ? 1.f : 0.f);
+        sel[1][e] = (bf16)((8 * g4 + e == 16 + n16) ? 1.f : 0.f);
+    }
+    bf16x8 bgf[2][2], vf[2][2], kbf[2][2], abf[2][2];   // [token kstep][16-channel half]
+    f32x4 qt[4][2];                                     // (Q . Gamma)^T [token block][half]
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        f32x4 tbg[2][2], tkb[2][2], tab[2][2], tv[2][2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; t2++) {
+            const int tt = 2 * kb + t2, row = 16 * tt + n16;
+            float L8[8], Ls[8], Le[8], Y8[8], Z8[8], AF8[8];
+            load8f(sG + row * kLdG + cw, L8);
+            if (tt > 0) load8f(sFac + (kFL + tt - 1) * 128 + cw, Ls);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) Ls[e] = 0.f;
+            }
+            load8f(sFac + (kFL + tt) * 128 + cw, Le);
+            load8f(sFac + (kFY + tt) * 128 + cw, Y8);
+            load8f(sFac + (kFZ + tt) * 128 + cw, Z8);
+            const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[tt]);
+            const bf16x8 qq = __builtin_bit_cast(bf16x8, qr[tt]);
+            const bf16x8 aa = __builtin_bit_cast(bf16x8, ar[tt]);
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, br[tt]);
+            bf16x8 rb, rq, abg, aq, akb, aab;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float E = ex2(L8[e] - Ls[e]), F = ex2(Le[e] - L8[e]);
+                const float bE = (float)bb[e] * E, qE = (float)qq[e] * E;
+                const float kF = (float)kk[e] * F, aF = (float)aa[e] * F;
+                rb[e] = (bf16)bE;
+                rq[e] = (bf16)qE;
+                abg[e] = (bf16)(bE * Y8[e]);
+                aq[e] = (bf16)(qE * Y8[e]);
+                akb[e] = (bf16)(kF * Z8[e]);
+                aab[e] = (bf16)(aF * Z8[e]);
+                L8[e] = kF;
+                AF8[e] = aF;
+            }
+            *reinterpret_cast<float4*>(sG + row * kLdG + cw) = make_float4(L8[0], L8[1], L8[2], L8[3]);
+            *reinterpret_cast<float4*>(sG + row * kLdG + cw + 4) = make_float4(L8[4], L8[5], L8[6], L8[7]);
+            *reinterpret_cast<float4*>(sAF + row * kLdG + cw) = make_float4(AF8[0], AF8[1], AF8[2], AF8[3]);
+            *reinterpret_cast<float4*>(sAF + row * kLdG + cw + 4) = make_float4(AF8[4], AF8[5], AF8[6], AF8[7]);
+            *reinterpret_cast<bf16x8*>(sRB + row * kLdK + cw) = rb;
+            *reinterpret_cast<bf16x8*>(sRQ + row * kLdK + cw) = rq;
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                tbg[t2][cb] = mfma_bf16(abg, sel[cb], zero4());
+                tkb[t2][cb] = mfma_bf16(akb, sel[cb], zero4());
+                tab[t2][cb] = mfma_bf16(aab, sel[cb], zero4());
+                tv[t2][cb] = mfma_bf16(__builtin_bit_cast(bf16x8, vr[tt]), sel[cb], zero4());
+                qt[tt][cb] = mfma_bf16(sel[cb], aq, zero4());
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+            bgf[kb][cb] = pack_frag(tbg[0][cb], tbg[1][cb]);
+            vf[kb][cb] = pack_frag(tv[0][cb], tv[1][cb]);
+            kbf[kb][cb] = pack_frag(tkb[0][cb], tkb[1][cb]);
+            abf[kb][cb] = pack_frag(tab[0][cb], tab[1][cb]);
+            *reinterpret_cast<bf16x8*>(rec + RD_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16) = abf[kb][cb];
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. the four chunk matrices, balanced over the waves
+    const int pb = pair_beg(w), pe = pair_beg(w + 1);
+    f32x4 aba[3], abk[3], aqa[3], aqk[3];
+#pragma unroll
+    for (int sl = 0; sl < 3; sl++) {
+        aba[sl] = zero4(); abk[sl] = zero4(); aqa[sl] = zero4(); aqk[sl] = zero4();
+        const int p = pb + sl;
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const int c0 = 32 * ks + 8 * g4;
+                const bf16x8 rbv = *reinterpret_cast<const bf16x8*>(sRB + (16 * r + n16) * kLdK + c0);
+                const bf16x8 rqv = *reinterpret_cast<const bf16x8*>(sRQ + (16 * r + n16) * kLdK + c0);
+                float kf[8], af[8], X8[8];
+                load8f(sG + (16 * s + n16) * kLdG + c0, kf);
+                load8f(sAF + (16 * s + n16) * kLdG + c0, af);
+                load8f(sFac + (kFX + p) * 128 + c0, X8);
+                bf16x8 colk, cola;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    colk[e] = (bf16)(kf[e] * X8[e]);
+                    cola[e] = (bf16)(af[e] * X8[e]);
+                }
+                aba[sl] = mfma_bf16(rbv, cola, aba[sl]);
+                abk[sl] = mfma_bf16(rbv, colk, abk[sl]);
+                aqa[sl] = mfma_bf16(rqv, cola, aqa[sl]);
+                aqk[sl] = mfma_bf16(rqv, colk, aqk[sl]);
+            }
+        }
+    }
+    __syncthreads();   // every step 1-3 buffer is dead from here
+
+    float* sNegAba = reinterpret_cast<float*>(smem + kDNegAba);
+    float* sAbk = reinterpret_cast<float*>(smem + kDAbk);
+    float* sAqa = reinterpret_cast<float*>(smem + kDAqa);
+    float* sAqk = reinterpret_cast<float*>(smem + kDAqk);
+    float* sT = reinterpret_cast<float*>(smem + kDT);
+    float* sM = reinterpret_cast<float*>(smem + kDM);
+    float* sScr = reinterpret_cast<float*>(smem + kDScr);
+    // causal masks: A_ba, A_bk strictly lower, A_qa, A_qk lower; tiles above
+    // the diagonal are zero.  -A_ba is stored so that T = (I + (-A_ba))^{-1}.
+#pragma unroll
+    for (int sl = 0; sl < 3; sl++) {
+        const int p = pb + sl;
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int ii = 4 * g4 + e, idx = (16 * r + ii) * kLdA + 16 * s + n16;
+                const bool strict = s == r && n16 >= ii, incl = s == r && n16 > ii;
+                sNegAba[idx] = strict ? 0.f : -aba[sl][e];
+                sAbk[idx] = strict ? 0.f : abk[sl][e];
+                sAqa[idx] = incl ? 0.f : aqa[sl][e];
+                sAqk[idx] = incl ? 0.f : aqk[sl][e];
+            }
+        }
+    }
+    for (int idx = tid; idx < 6 * 256; idx += 256) {     // tiles (r, s), s > r
+        const int t = idx >> 8, e = idx & 255;
+        const int r = t < 3 ? 0 : t < 5 ? 1 : 2, s = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
+        const int o = (16 * r + (e >> 4)) * kLdA + 16 * s + (e & 15);
+        sNegAba[o] = 0.f; sAbk[o] = 0.f; sAqa[o] = 0.f; sAqk[o] = 0.f; sM[o] = 0.f;
+    }
+    for (int idx = tid; idx < 4096; idx += 256) sT[(idx >> 6) * kLdA + (idx & 63)] = 0.f;
+    __syncthreads();
+
+    // ---- 4. T = (I - A_ba)^{-1} in fp32; then M = T A_bk, R = A_qa T (R over
+    //      -A_ba, which is dead), P = R A_bk + A_qk (over A_qk), all fp32
+    unit_lower_inverse(sNegAba, sT, sScr, w, n16, g4);
+    tri_mm(sT, sAbk, nullptr, sM, w, n16, g4);
+    tri_mm(sAqa, sT, nullptr, sNegAba, w, n16, g4);
+    __syncthreads();
+    float* sR = sNegAba;
+    tri_mm(sR, sAbk, sAqk, sAqk, w, n16, g4);
+    __syncthreads();
+    float* sP = sAqk;
+
+    // ---- 5. products over tokens (wave w: channels [32w, 32w + 32))
+    bf16x8 tf[4][2], rf[4][2], mf[4][2], pf[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            tf[tb][kb] = row_frag(sT, tb, kb, n16, g4);
+            rf[tb][kb] = row_frag(sR, tb, kb, n16, g4);
+            mf[tb][kb] = row_frag(sM, tb, kb, n16, g4);
+            pf[tb][kb] = row_frag(sP, tb, kb, n16, g4);
+        }
+    __syncthreads();   // the matrices are dead; LDS takes the Ub / V staging
+    // Wb^T = (B . Gamma)^T T^T and Q'^T = (Q . Gamma)^T + (B . Gamma)^T R^T,
+    // tiles [channel][token] as the chain's A operand (token block tb, k-step w)
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++) {
+        f32x4 w0 = zero4(), w1 = zero4(), q0 = qt[tb][0], q1 = qt[tb][1];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            w0 = mfma_bf16(bgf[kb][0], tf[tb][kb], w0);
+            w1 = mfma_bf16(bgf[kb][1], tf[tb][kb], w1);
+            q0 = mfma_bf16(bgf[kb][0], rf[tb][kb], q0);
+            q1 = mfma_bf16(bgf[kb][1], rf[tb][kb], q1);
+        }
+        *reinterpret_cast<bf16x8*>(rec + RD_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag(w0, w1);
+        *reinterpret_cast<bf16x8*>(rec + RD_Q + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag(q0, q1);
+    }
+    // Ub = M V and Uo = P V: tiles (slice 2w + cb, token block tb)
+    bf16* sStU = reinterpret_cast<bf16*>(smem + kDStU);
+    bf16* sStV = reinterpret_cast<bf16*>(smem + kDStV);
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++) {
+        f32x4 ub[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) {
+            f32x4 u = zero4(), uo = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                u = mfma_bf16(mf[tb][kb], vf[kb][cb], u);
+                uo = mfma_bf16(pf[tb][kb], vf[kb][cb], uo);
+            }
+            ub[tb] = u;
+            *reinterpret_cast<bf16x4*>(rec + RD_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(uo);
+        }
+        const int sl = 2 * w + cb;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            *reinterpret_cast<bf16x8*>(sStU + ((sl * 2 + kb) * 64 + lane) * 8) = pack_frag(ub[2 * kb], ub[2 * kb + 1]);
+            *reinterpret_cast<bf16x8*>(sStV + ((sl * 2 + kb) * 64 + lane) * 8) = vf[kb][cb];
+        }
+    }
+    __syncthreads();
+    // Cs = Abar^T Ub + Kbar^T V: rows = this wave's channels (row tiles 2w, 2w + 1), all slices
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int sl = 0; sl < 8; sl++) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                const bf16x8 uf = *reinterpret_cast<const bf16x8*>(sStU + ((sl * 2 + kb) * 64 + lane) * 8);
+                const bf16x8 vv = *reinterpret_cast<const bf16x8*>(sStV + ((sl * 2 + kb) * 64 + lane) * 8);
+                acc = mfma_bf16(abf[kb][cb], uf, acc);
+                acc = mfma_bf16(kbf[kb][cb], vv, acc);
+            }
+            *reinterpret_cast<bf16x4*>(rec + RD_C + (((2 * w + cb) * 8 + sl) * 64 + lane) * 8) = pack4(acc);
+        }
+}
+
+}  // namespace
+
+hipError_t launch_dplr_intra(const ChunkArgs& a) {
+    const int* hdr = reinterpret_cast<const int*>(a.ws);
+    const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
+    uint8_t* recs = a.ws + a.L.off_recs;
+    hipLaunchKernelGGL(dplr_intra_kernel, dim3((unsigned)((long long)a.L.cap * a.H)), dim3(256), 0,
+                       a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.la, (const bf16*)a.lb, a.z, a.A, hdr, chunks, a.H, recs);
+    return hipGetLastError();
+}
+
+}  // namespace kda

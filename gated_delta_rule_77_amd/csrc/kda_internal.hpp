@@ -58,6 +58,31 @@ constexpr int REC_G = 73728;    // gamma_C [128] fp32
 constexpr int REC_BYTES = 74240;
 }  // namespace fast
 
+// record of the MFMA path of the general DPLR update: what the chain needs
+// with the S-independent terms folded in, X = Wb S, O = Q' S + Uo,
+// S <- Diag(gamma_C) S + Abar^T X + Cs
+namespace fast_dplr {
+constexpr int RD_W = 0;         // Wb^T fragments, layout of REC_W (not negated)
+constexpr int RD_Q = 16384;     // Q'^T fragments, layout of REC_Q
+constexpr int RD_K = 32768;     // Abar^T fragments, layout of REC_K
+constexpr int RD_U = 49152;     // Uo tiles, layout of REC_U
+constexpr int RD_C = 65536;     // Cs tiles [8 row tile][8 slice][64 lane][4] bf16
+constexpr int RD_G = 98304;     // gamma_C [128] fp32
+constexpr int RD_BYTES = 98816;
+}  // namespace fast_dplr
+
+// record offsets by kind, for the chain kernels shared by both updates
+template <bool DPLR> struct RecLayout;
+template <> struct RecLayout<false> {
+    static constexpr int W = fast::REC_W, Q = fast::REC_Q, K = fast::REC_K, U = fast::REC_U,
+                         A = fast::REC_A, C = -1, G = fast::REC_G, BYTES = fast::REC_BYTES;
+};
+template <> struct RecLayout<true> {
+    static constexpr int W = fast_dplr::RD_W, Q = fast_dplr::RD_Q, K = fast_dplr::RD_K,
+                         U = fast_dplr::RD_U, A = -1, C = fast_dplr::RD_C, G = fast_dplr::RD_G,
+                         BYTES = fast_dplr::RD_BYTES;
+};
+
 inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
     return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
 }
@@ -97,8 +122,8 @@ inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, boo
     L.seg_cap = fast ? (L.cap + L.seg_chunks - 1) / L.seg_chunks + (N > 0 ? N : 1) : 0;
     L.off_segs = align_up(L.off_seqsegs + n1 * 8, 256);
     L.off_recs = align_up(L.off_segs + (size_t)L.seg_cap * 16, 256);
-    L.rec_bytes = dplr ? dplr_generic_rec_floats(dk, dv, C) * 4
-                : fast ? (size_t)fast::REC_BYTES : generic_rec_floats(dk, dv, C) * 4;
+    L.rec_bytes = fast ? (size_t)(dplr ? fast_dplr::RD_BYTES : fast::REC_BYTES)
+                : (dplr ? dplr_generic_rec_floats(dk, dv, C) : generic_rec_floats(dk, dv, C)) * 4;
     L.off_sstart = align_up(L.off_recs + (size_t)L.cap * H * L.rec_bytes, 256);
     L.off_rm = align_up(L.off_sstart + (size_t)L.seg_cap * H * 128 * 128 * 4, 256);
     L.total = L.off_rm + (size_t)L.seg_cap * H * 128 * 256 * 4;
@@ -133,6 +158,7 @@ struct ChunkArgs {
 // launchers (return hipError_t of the launches)
 hipError_t launch_prep(const ChunkArgs& a);
 hipError_t launch_fast(const ChunkArgs& a);
+hipError_t launch_fast_dplr(const ChunkArgs& a);    // general DPLR on the MFMA path
 hipError_t launch_generic(const ChunkArgs& a, int dtype_bf16);
 bool generic_supported(int dk, int dv, int C);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* z,
@@ -155,6 +181,7 @@ hipError_t launch_layer_step(const void* q_in, const void* k_in, const void* v_i
                              float l2_eps, float rms_eps, void* y, int N, int H, int d,
                              int dtype_bf16, hipStream_t s);
 hipError_t launch_dplr_generic(const ChunkArgs& a, int dtype_bf16);
+hipError_t launch_dplr_intra(const ChunkArgs& a);   // MFMA path: the DPLR intra-chunk launch
 hipError_t launch_dplr_decode(const void* q, const void* k, const void* v, const void* la,
                               const void* lb, const float* z, const float* A, float* state,
                               void* o, int N, int H, int d, int dtype_bf16, hipStream_t s);

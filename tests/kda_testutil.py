@@ -3,7 +3,14 @@ running the oracle on the same (already rounded) values, and the error metric.
 
 Tolerance metric, per tensor: max|gpu - ref| / max|ref|.  Bars: 1e-4 for the
 fp32 path, 1e-2 for bf16 inputs on the MFMA path (oracle on the same
-bf16-rounded inputs).
+bf16-rounded inputs).  A packed batch's output is one tensor: its sequences
+are checked one at a time against the largest reference value of the whole
+tensor (`scale`).  Dividing by a sequence's own maximum would be stricter than
+the metric and, for a one-token sequence, measure something else: its output
+is dominated by (q . k) v with |q . k| ~ 1/sqrt(d_k) for the unit-norm random
+q, k of the input recipe, and the MFMA operands round q and k (scaled by
+their decay factors) to bf16, which alone moves that small dot product by
+about 1% of itself (reproduced by a CPU emulation of the rounding points).
 """
 import numpy as np
 import torch
@@ -14,10 +21,11 @@ TOL_F32 = 1e-4
 TOL_BF16 = 1e-2
 
 
-def rel_err(got, ref) -> float:
+def rel_err(got, ref, scale=None) -> float:
     got = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
     ref = ref.detach().double().cpu().numpy() if isinstance(ref, torch.Tensor) else np.asarray(ref)
-    scale = np.abs(ref).max()
+    if scale is None:
+        scale = np.abs(ref).max()
     if scale == 0:
         return float(np.abs(got).max())
     return float(np.abs(got - ref).max() / scale)
