@@ -12,8 +12,9 @@ of the whole call (prep + intra + chain kernels), inputs already in HBM.
 Also reported: per-kernel durations from HIP events recorded by libkda on the
 stream its kernels run on (kda_chunk_fwd_timed), the roofline of the dominant
 kernel, the decode workload (256 sequences x 12 heads, 16 single-token
-steps), and the fp64 CPU oracle timed on a bounded prefix of the same
-workload.  Prints ONE JSON line.
+steps), the layer entry points, the family modes and the general DPLR
+update on the same shapes, and the fp64 CPU oracle timed on a bounded prefix
+of the same workload.  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -43,6 +44,13 @@ INTRA_BYTES = 1284
 CHAIN_BYTES = 256
 # decode: read + write one fp32 state (2 x 64 KiB) + 1540 B of per-token I/O
 DECODE_BYTES = 2 * 128 * 128 * 4 + PREFILL_BYTES
+# general DPLR update, per token and head: q, k, v, a, b bf16 (5 x 256) + z fp32
+# (512) + o bf16 (256); its intra kernel must read all but o
+DPLR_BYTES = 2048
+DPLR_INTRA_BYTES = 1792
+# chunk records the intra kernels write (bytes per chunk and head)
+KDA_RECORD_BYTES = 74240
+DPLR_RECORD_BYTES = 98816
 
 
 def _hip():
@@ -324,6 +332,97 @@ def bench_layer(args, kda, torch, KI, call_ms, step_ms):
     }
 
 
+def _stage_ms(h, evs):
+    keys = {"prep": (0, 1), "intra": (1, 2), "transition": (2, 4), "compose": (4, 5),
+            "output": (5, 3), "call": (0, 3)}
+    return {k: sum(_elapsed(h, e[a], e[b]) for e in evs) / len(evs) for k, (a, b) in keys.items()}
+
+
+def bench_family(args, kda, torch, KI, kda_stages):
+    """The other rows of the family table (GLA with the erase step off,
+    DeltaNet with alpha = 1) and the general DPLR update with the low-rank pair
+    untied from k, on the long_1m shapes.  The DPLR line is the measurement
+    behind the 2-vs-4 chunk-matrix comparison: KDA forms A_kk and A_qk per
+    chunk, the general form A_ba, A_bk, A_qa and A_qk."""
+    dev = torch.device("cuda:0")
+    case = KI.CONFIGS["long_1m"]
+    reps = max(2, args.steps // 2)
+    out = {"workload": "long_1m shapes (B=1, H=12, T=1048576, d=128, C=64, bf16, seed 0)"}
+    d = KI.make_prefill(case, device=dev, seed=0)
+    B, T, H, dk, dv, N, C = d["B"], d["T"], d["H"], d["dk"], d["dv"], d["N"], d["chunk"]
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, C, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    modes = {}
+    for mode in ("gla", "deltanet"):
+        g, A = (None, None) if mode == "deltanet" else (d["z"], d["A"])
+
+        def run():
+            return kda.kda_chunk_fwd_mode(d["q"], d["k"], d["v"], g, d["b"], A, mode,
+                                          initial_state=d["h0"], chunk_size=C, workspace=ws)
+        run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ts) / len(ts)
+        modes[mode] = {"ms_per_call": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1)}
+    out["modes"] = modes
+    del d, ws
+    torch.cuda.empty_cache()
+
+    d = KI.make_dplr(case, device=dev, seed=0)
+    L = kda.lib()
+    wsb = kda.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, C, torch.bfloat16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    h = _hip()
+    evs = [[_event(h) for _ in range(6)] for _ in range(reps + 1)]
+    ptrs = (d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["la"].data_ptr(),
+            d["lb"].data_ptr(), d["z"].data_ptr(), d["A"].data_ptr(), d["h0"].data_ptr(), None,
+            B, T, H, dk, dv, N, C, 1, o.data_ptr(), hT.data_ptr(), ws.data_ptr(), wsb)
+    for i in range(reps + 1):
+        arr = (ctypes.c_void_p * 6)(*[e.value for e in evs[i]])
+        rc = L.kda_dplr_chunk_fwd_timed(*ptrs, arr, 6, stream)
+        if rc != 0:
+            raise RuntimeError(L.kda_status_string(rc).decode())
+    torch.cuda.synchronize()
+    st = _stage_ms(h, evs[1:])
+    for row in evs:
+        for e in row:
+            h.hipEventDestroy(e)
+    units = B * T * H
+    intra_gbs = DPLR_INTRA_BYTES * units / (st["intra"] * 1e-3) / 1e9
+    out["dplr"] = {
+        "call_ms_events": round(st["call"], 4),
+        "tokens_per_s": round(B * T / (st["call"] * 1e-3), 1),
+        "kernels_ms": {k: round(v, 4) for k, v in st.items() if k != "call"},
+        "intra_alg_GBps": round(intra_gbs, 1),
+        "intra_hbm_frac": round(intra_gbs / HBM_PEAK_GBS, 4),
+        "path_alg_GBps": round(DPLR_BYTES * units / (st["call"] * 1e-3) / 1e9, 1),
+    }
+    out["study_2_vs_4"] = {
+        "chunk_matrices": {"kda": 2, "dplr": 4},
+        "intra_ms": {"kda": round(kda_stages["intra"], 4), "dplr": round(st["intra"], 4)},
+        "call_ms": {"kda": round(kda_stages["call"], 4), "dplr": round(st["call"], 4)},
+        "intra_time_ratio": round(st["intra"] / kda_stages["intra"], 3),
+        "call_time_ratio": round(st["call"] / kda_stages["call"], 3),
+        "input_bytes_per_token_head": {"kda": INTRA_BYTES, "dplr": DPLR_INTRA_BYTES},
+        "record_bytes_per_chunk_head": {"kda": KDA_RECORD_BYTES, "dplr": DPLR_RECORD_BYTES},
+    }
+    print(f"[bench] family: modes {modes}; dplr call {st['call']:.3f} ms, intra {st['intra']:.3f} ms "
+          f"(KDA {kda_stages['intra']:.3f})", flush=True)
+    del d, ws, o, hT
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, torch):
     import oracle
     n = inp["q"].shape[1]
@@ -347,6 +446,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer entry points (convolution and gated RMSNorm around the core)")
+    ap.add_argument("--no-family", action="store_true",
+                    help="skip the family modes and the general DPLR update")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before timing (a known-size "
                          "kernel for calibrating the HBM traffic counters)")
@@ -379,6 +480,10 @@ def main():
     if not args.no_layer:
         layer = bench_layer(args, kda, torch, KI, extra["call_ms_events"],
                             dec["ms_per_step_mean"] if dec else float("nan"))
+    family = None
+    if not args.no_family:
+        family = bench_family(args, kda, torch, KI, {"intra": extra["kernels_ms"]["intra"],
+                                                     "call": extra["call_ms_events"]})
     cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_inp, torch)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -389,6 +494,7 @@ def main():
                                "q/k/v, fp32 logits and state, seed 0",
                    "B": 1, "T": 1 << 20, "H": 12, "dk": 128, "dv": 128, "chunk": 64},
         "roofline": roof, "cpu_baseline": cpu, "prefill": extra, "decode": dec, "layer": layer,
+        "family": family,
     }
     print(json.dumps(line), flush=True)
 

@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
     "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step", "kda_chunk_fwd_mode",
     "kda_recurrent_step_mode", "kda_dplr_chunk_fwd_workspace_bytes", "kda_dplr_chunk_fwd",
-    "kda_dplr_recurrent_step",
+    "kda_dplr_chunk_fwd_timed", "kda_dplr_recurrent_step",
 )
 # family modes of kda_chunk_fwd_mode / kda_recurrent_step_mode (kda_mode_t)
 MODES = {"kda": 0, "gla": 1, "deltanet": 2}
@@ -113,6 +113,9 @@ def lib() -> ctypes.CDLL:
     L.kda_dplr_chunk_fwd_workspace_bytes.argtypes = [i] * 8
     L.kda_dplr_chunk_fwd.restype = i
     L.kda_dplr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 8 + [vp, f, vp, sz, vp]
+    L.kda_dplr_chunk_fwd_timed.restype = i
+    L.kda_dplr_chunk_fwd_timed.argtypes = ([vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 8
+                                           + [vp, f, vp, sz, ctypes.POINTER(vp), i, vp])
     L.kda_dplr_recurrent_step.restype = i
     L.kda_dplr_recurrent_step.argtypes = [vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 5 + [vp]
     _lib = L

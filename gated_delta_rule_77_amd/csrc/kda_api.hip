@@ -218,11 +218,12 @@ size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, i
     return ws_layout(B, T, H, dk, dv, N, chunk, fast, true).total;
 }
 
-kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a,
-                                const void* b, const float* g_logits, const float* A,
-                                const float* h0, const int* cu_seqlens, int B, int T, int H,
-                                int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
-                                float* hT, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+kda_status_t run_dplr(const void* q, const void* k, const void* v, const void* a, const void* b,
+                      const float* g_logits, const float* A, const float* h0,
+                      const int* cu_seqlens, int B, int T, int H, int dk, int dv, int N, int chunk,
+                      kda_dtype_t dtype, void* o, float* hT, void* workspace,
+                      size_t workspace_bytes, hipEvent_t* ev, int n_ev, void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (!prefill_sizes_ok(B, T, H, dk, dv, N, chunk)) return KDA_ERR_INVALID_ARG;
     if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
@@ -242,9 +243,41 @@ kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, con
     c.B = B; c.T = T; c.H = H; c.dk = dk; c.dv = dv; c.N = N; c.C = chunk;
     c.o = o; c.hT = hT; c.ws = static_cast<uint8_t*>(workspace); c.L = L;
     c.stream = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_prep(c);
+    c.ev = ev;
+    c.ev5 = (ev && n_ev >= 6) ? ev + 4 : nullptr;
+    hipError_t e = ev ? hipEventRecord(ev[0], c.stream) : hipSuccess;
+    if (e == hipSuccess) e = launch_prep(c);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], c.stream);
     if (e == hipSuccess) e = fast ? launch_fast_dplr(c) : launch_dplr_generic(c, dtype == KDA_BF16);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], c.stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a,
+                                const void* b, const float* g_logits, const float* A,
+                                const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                float* hT, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_dplr(q, k, v, a, b, g_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N, chunk, dtype,
+                    o, hT, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+kda_status_t kda_dplr_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* a,
+                                      const void* b, const float* g_logits, const float* A,
+                                      const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                      int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                      float* hT, void* workspace, size_t workspace_bytes,
+                                      void* const* events, int n_events, void* stream) {
+    if (!events || n_events < 4) return KDA_ERR_INVALID_ARG;
+    const int n = n_events >= 6 ? 6 : 4;
+    hipEvent_t ev[6];
+    for (int i = 0; i < n; i++) {
+        if (!events[i]) return KDA_ERR_INVALID_ARG;
+        ev[i] = static_cast<hipEvent_t>(events[i]);
+    }
+    return run_dplr(q, k, v, a, b, g_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N, chunk, dtype,
+                    o, hT, workspace, workspace_bytes, ev, n, stream);
 }
 
 kda_status_t kda_dplr_recurrent_step(const void* q, const void* k, const void* v, const void* a,

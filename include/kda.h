@@ -270,6 +270,23 @@ KDA_API kda_status_t kda_dplr_chunk_fwd(const void* q, const void* k, const void
                                         void* stream);
 
 /*
+ * kda_dplr_chunk_fwd that also records caller-created HIP events on `stream`
+ * around its stages, as kda_chunk_fwd_timed does (events[0..3]: before the
+ * chunk bookkeeping, after it, after the intra-chunk kernel, after the
+ * chain; with n_events >= 6 on the MFMA path events[4], events[5] after the
+ * segment transition and composition).  Results are identical to
+ * kda_dplr_chunk_fwd.
+ */
+KDA_API kda_status_t kda_dplr_chunk_fwd_timed(const void* q, const void* k, const void* v,
+                                              const void* a, const void* b,
+                                              const float* g_logits, const float* A,
+                                              const float* h0, const int* cu_seqlens, int B,
+                                              int T, int H, int dk, int dv, int N, int chunk,
+                                              kda_dtype_t dtype, void* o, float* hT,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* const* events, int n_events, void* stream);
+
+/*
  * One DPLR token per sequence, state updated in place (layouts as
  * kda_recurrent_step, plus a, b [N, H, dk] dtype).  One pass over
  * S' = Diag(alpha) S forms x = S'^T b and r = S'^T q; then
