@@ -23,8 +23,10 @@
 // KDA kernel; wave w owns channels [32w, 32w + 32) in the per-element work.
 // The decay factors are the powers of two of that kernel (row factor
 // E = 2^(L - L_s), column factor F = 2^(L_e - L), per-channel table X, Y, Z).
-// Both column operands (K.F and A.F) stay fp32 in LDS until each tile pair
-// scales them, so one workgroup fills a CU (113 KB of LDS).
+// The column operands (K.F, then A.F) take turns in one fp32 LDS buffer until
+// each tile pair scales them; A_qk stays in the registers of the wave that
+// formed it; the small products go through registers before they overwrite
+// dead buffers.  78 KiB of LDS: two workgroups per CU.
 // Sources: [K3-ATTN] "Kimi K3 注意力机制深度解析：KDA、Gated MLA 与 AttnRes 的混合架构" §2.2;
 //          [LA-KDA] "从线性注意力到 KDA：拆解 Kimi K3 的核心注意力机制" §5.4, §7, §8.
 #include "kda_device.hpp"
@@ -39,45 +41,53 @@ using namespace fast_dplr;
 namespace {
 
 // LDS, steps 1-3
-constexpr int kDG = 0;                                  // fp32 [64][kLdG]: L, then K.F
-constexpr int kDAF = kDG + 64 * kLdG * 4;               // fp32 [64][kLdG]: A.F
-constexpr int kDRB = kDAF + 64 * kLdG * 4;              // bf16 [64][kLdK]: B.E
+constexpr int kDG = 0;                                  // fp32 [64][kLdG]: L, then K.F, then A.F
+constexpr int kDRB = kDG + 64 * kLdG * 4;               // bf16 [64][kLdK]: B.E
 constexpr int kDRQ = kDRB + 64 * kLdK * 2;              // bf16 [64][kLdK]: Q.E
 constexpr int kDFac = kDRQ + 64 * kLdK * 2;             // fp32 [kNFac][128]
-constexpr int kDSmem = kDFac + kNFac * 128 * 4;         // 113664 bytes
+constexpr int kDSmem = kDFac + kNFac * 128 * 4;         // 79872 bytes
 // LDS from the masks on (aliases the above): fp32 64 x 64 matrices
 constexpr int kMat = 64 * kLdA * 4;
-constexpr int kDNegAba = 0;          // -A_ba, then R = A_qa T
-constexpr int kDAbk = kMat;
-constexpr int kDAqa = 2 * kMat;
-constexpr int kDAqk = 3 * kMat;      // A_qk, then P = R A_bk + A_qk in place
-constexpr int kDT = 4 * kMat;        // T
-constexpr int kDM = 5 * kMat;        // M = T A_bk
-constexpr int kDScr = 6 * kMat;      // 4 x 256 floats of inverse scratch
+constexpr int kDB0 = 0;              // -A_ba, then R = A_qa T
+constexpr int kDB1 = kMat;           // A_bk, then P = R A_bk + A_qk
+constexpr int kDB2 = 2 * kMat;       // A_qa, then M = T A_bk
+constexpr int kDT = 3 * kMat;        // T
+constexpr int kDScr = 4 * kMat;      // 4 x 256 floats of inverse scratch
 static_assert(kDScr + 4096 <= kDSmem, "the matrices fit in the step 1-3 buffers");
 // LDS at the end: Ub and V as token-contracting B fragments of all 8 slices
 constexpr int kDStU = 0;             // [8 slice][2 kstep][64 lane][8] bf16
 constexpr int kDStV = 16384;
 
-// Z (+)= X Y over 16 x 16 tiles of lower-triangular 64 x 64 fp32 matrices in
-// LDS ([64][kLdA]); only tiles (r, s) with s <= r, k-blocks m in [s, r].
-// Wave w takes its tile pairs; the result overwrites Z's tile (which may be
-// Z_init's tile: each tile is read and written by one wave only).
-__device__ __forceinline__ void tri_mm(const float* X, const float* Y, const float* Zinit, float* Z,
-                                       int w, int n16, int g4) {
+// The tiles (r, s), s <= r, of wave w (its tile pairs) of Z = X Y (+ Zinit)
+// for lower-triangular 64 x 64 fp32 matrices in LDS ([64][kLdA]); k-blocks m
+// in [s, r].  Results stay in registers, so Z may later overwrite X or Y
+// after a barrier.
+__device__ __forceinline__ void tri_mm(const float* X, const float* Y, const f32x4 (&Zinit)[3],
+                                       f32x4 (&Z)[3], int w, int n16, int g4) {
     const int pb = pair_beg(w), pe = pair_beg(w + 1);
-    for (int p = pb; p < pe; p++) {
-        const int r = pair_row(p), s = p - r * (r + 1) / 2;
-        f32x4 acc = zero4();
-        if (Zinit) {
 #pragma unroll
-            for (int e = 0; e < 4; e++) acc[e] = Zinit[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16];
+    for (int sl = 0; sl < 3; sl++) {
+        const int p = pb + sl;
+        Z[sl] = Zinit[sl];
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+            for (int m = s; m <= r; m++)
+                Z[sl] = mm16_f32(Z[sl], X + 16 * r * kLdA + 16 * m, kLdA, Y + 16 * m * kLdA + 16 * s,
+                                 kLdA, n16, g4);
         }
-        for (int m = s; m <= r; m++)
-            acc = mm16_f32(acc, X + 16 * r * kLdA + 16 * m, kLdA, Y + 16 * m * kLdA + 16 * s, kLdA,
-                           n16, g4);
+    }
+}
+
+__device__ __forceinline__ void store_tiles(float* Z, const f32x4 (&t)[3], int w, int n16, int g4) {
+    const int pb = pair_beg(w), pe = pair_beg(w + 1);
 #pragma unroll
-        for (int e = 0; e < 4; e++) Z[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = acc[e];
+    for (int sl = 0; sl < 3; sl++) {
+        const int p = pb + sl;
+        if (p < pe) {
+            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; e++) Z[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = t[sl][e];
+        }
     }
 }
 
@@ -91,7 +101,7 @@ __device__ __forceinline__ bf16x8 row_frag(const float* Mx, int tb, int kb, int 
     return pack_frag(x0, x1);
 }
 
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, 2)
 void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const bf16* __restrict__ la,
                        const bf16* __restrict__ lb, const float* __restrict__ z,
@@ -109,7 +119,6 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     __shared__ __align__(16) uint8_t smem[kDSmem];
     float* sG = reinterpret_cast<float*>(smem + kDG);
-    float* sAF = reinterpret_cast<float*>(smem + kDAF);
     bf16* sRB = reinterpret_cast<bf16*>(smem + kDRB);
     bf16* sRQ = reinterpret_cast<bf16*>(smem + kDRQ);
     float* sFac = reinterpret_cast<float*>(smem + kDFac);
@@ -206,13 +215,14 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     bf16x8 bgf[2][2], vf[2][2], kbf[2][2], abf[2][2];   // [token kstep][16-channel half]
     f32x4 qt[4][2];                                     // (Q . Gamma)^T [token block][half]
+    float afr[4][8];                                    // A.F of this lane's elements (second pass)
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
         f32x4 tbg[2][2], tkb[2][2], tab[2][2], tv[2][2];
 #pragma unroll
         for (int t2 = 0; t2 < 2; t2++) {
             const int tt = 2 * kb + t2, row = 16 * tt + n16;
-            float L8[8], Ls[8], Le[8], Y8[8], Z8[8], AF8[8];
+            float L8[8], Ls[8], Le[8], Y8[8], Z8[8];
             load8f(sG + row * kLdG + cw, L8);
             if (tt > 0) load8f(sFac + (kFL + tt - 1) * 128 + cw, Ls);
             else {
@@ -239,12 +249,10 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 akb[e] = (bf16)(kF * Z8[e]);
                 aab[e] = (bf16)(aF * Z8[e]);
                 L8[e] = kF;
-                AF8[e] = aF;
+                afr[tt][e] = aF;
             }
             *reinterpret_cast<float4*>(sG + row * kLdG + cw) = make_float4(L8[0], L8[1], L8[2], L8[3]);
             *reinterpret_cast<float4*>(sG + row * kLdG + cw + 4) = make_float4(L8[4], L8[5], L8[6], L8[7]);
-            *reinterpret_cast<float4*>(sAF + row * kLdG + cw) = make_float4(AF8[0], AF8[1], AF8[2], AF8[3]);
-            *reinterpret_cast<float4*>(sAF + row * kLdG + cw + 4) = make_float4(AF8[4], AF8[5], AF8[6], AF8[7]);
             *reinterpret_cast<bf16x8*>(sRB + row * kLdK + cw) = rb;
             *reinterpret_cast<bf16x8*>(sRQ + row * kLdK + cw) = rq;
 #pragma unroll
@@ -267,48 +275,55 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 3. the four chunk matrices, balanced over the waves
+    // ---- 3. the four chunk matrices, balanced over the waves: the K.F column
+    //      operands first (A_bk, A_qk), then the A.F ones in the same buffer
     const int pb = pair_beg(w), pe = pair_beg(w + 1);
     f32x4 aba[3], abk[3], aqa[3], aqk[3];
+    auto tiles = [&](f32x4 (&tb)[3], f32x4 (&tq)[3]) {
 #pragma unroll
-    for (int sl = 0; sl < 3; sl++) {
-        aba[sl] = zero4(); abk[sl] = zero4(); aqa[sl] = zero4(); aqk[sl] = zero4();
-        const int p = pb + sl;
-        if (p < pe) {
-            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+        for (int sl = 0; sl < 3; sl++) {
+            tb[sl] = zero4();
+            tq[sl] = zero4();
+            const int p = pb + sl;
+            if (p < pe) {
+                const int r = pair_row(p), s = p - r * (r + 1) / 2;
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int c0 = 32 * ks + 8 * g4;
-                const bf16x8 rbv = *reinterpret_cast<const bf16x8*>(sRB + (16 * r + n16) * kLdK + c0);
-                const bf16x8 rqv = *reinterpret_cast<const bf16x8*>(sRQ + (16 * r + n16) * kLdK + c0);
-                float kf[8], af[8], X8[8];
-                load8f(sG + (16 * s + n16) * kLdG + c0, kf);
-                load8f(sAF + (16 * s + n16) * kLdG + c0, af);
-                load8f(sFac + (kFX + p) * 128 + c0, X8);
-                bf16x8 colk, cola;
+                for (int ks = 0; ks < 4; ks++) {
+                    const int c0 = 32 * ks + 8 * g4;
+                    const bf16x8 rbv = *reinterpret_cast<const bf16x8*>(sRB + (16 * r + n16) * kLdK + c0);
+                    const bf16x8 rqv = *reinterpret_cast<const bf16x8*>(sRQ + (16 * r + n16) * kLdK + c0);
+                    float cf[8], X8[8];
+                    load8f(sG + (16 * s + n16) * kLdG + c0, cf);
+                    load8f(sFac + (kFX + p) * 128 + c0, X8);
+                    bf16x8 col;
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    colk[e] = (bf16)(kf[e] * X8[e]);
-                    cola[e] = (bf16)(af[e] * X8[e]);
+                    for (int e = 0; e < 8; e++) col[e] = (bf16)(cf[e] * X8[e]);
+                    tb[sl] = mfma_bf16(rbv, col, tb[sl]);
+                    tq[sl] = mfma_bf16(rqv, col, tq[sl]);
                 }
-                aba[sl] = mfma_bf16(rbv, cola, aba[sl]);
-                abk[sl] = mfma_bf16(rbv, colk, abk[sl]);
-                aqa[sl] = mfma_bf16(rqv, cola, aqa[sl]);
-                aqk[sl] = mfma_bf16(rqv, colk, aqk[sl]);
             }
         }
+    };
+    tiles(abk, aqk);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+        float* dst = sG + (16 * tt + n16) * kLdG + cw;
+        *reinterpret_cast<float4*>(dst) = make_float4(afr[tt][0], afr[tt][1], afr[tt][2], afr[tt][3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(afr[tt][4], afr[tt][5], afr[tt][6], afr[tt][7]);
     }
+    __syncthreads();
+    tiles(aba, aqa);
     __syncthreads();   // every step 1-3 buffer is dead from here
 
-    float* sNegAba = reinterpret_cast<float*>(smem + kDNegAba);
-    float* sAbk = reinterpret_cast<float*>(smem + kDAbk);
-    float* sAqa = reinterpret_cast<float*>(smem + kDAqa);
-    float* sAqk = reinterpret_cast<float*>(smem + kDAqk);
+    float* sB0 = reinterpret_cast<float*>(smem + kDB0);
+    float* sB1 = reinterpret_cast<float*>(smem + kDB1);
+    float* sB2 = reinterpret_cast<float*>(smem + kDB2);
     float* sT = reinterpret_cast<float*>(smem + kDT);
-    float* sM = reinterpret_cast<float*>(smem + kDM);
     float* sScr = reinterpret_cast<float*>(smem + kDScr);
     // causal masks: A_ba, A_bk strictly lower, A_qa, A_qk lower; tiles above
-    // the diagonal are zero.  -A_ba is stored so that T = (I + (-A_ba))^{-1}.
+    // the diagonal are zero.  -A_ba is stored so that T = (I + (-A_ba))^{-1};
+    // A_qk stays in registers.
 #pragma unroll
     for (int sl = 0; sl < 3; sl++) {
         const int p = pb + sl;
@@ -318,10 +333,10 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             for (int e = 0; e < 4; e++) {
                 const int ii = 4 * g4 + e, idx = (16 * r + ii) * kLdA + 16 * s + n16;
                 const bool strict = s == r && n16 >= ii, incl = s == r && n16 > ii;
-                sNegAba[idx] = strict ? 0.f : -aba[sl][e];
-                sAbk[idx] = strict ? 0.f : abk[sl][e];
-                sAqa[idx] = incl ? 0.f : aqa[sl][e];
-                sAqk[idx] = incl ? 0.f : aqk[sl][e];
+                sB0[idx] = strict ? 0.f : -aba[sl][e];
+                sB1[idx] = strict ? 0.f : abk[sl][e];
+                sB2[idx] = incl ? 0.f : aqa[sl][e];
+                if (incl) aqk[sl][e] = 0.f;
             }
         }
     }
@@ -329,21 +344,29 @@ void dplr_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int t = idx >> 8, e = idx & 255;
         const int r = t < 3 ? 0 : t < 5 ? 1 : 2, s = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
         const int o = (16 * r + (e >> 4)) * kLdA + 16 * s + (e & 15);
-        sNegAba[o] = 0.f; sAbk[o] = 0.f; sAqa[o] = 0.f; sAqk[o] = 0.f; sM[o] = 0.f;
+        sB0[o] = 0.f; sB1[o] = 0.f; sB2[o] = 0.f;
     }
     for (int idx = tid; idx < 4096; idx += 256) sT[(idx >> 6) * kLdA + (idx & 63)] = 0.f;
     __syncthreads();
 
-    // ---- 4. T = (I - A_ba)^{-1} in fp32; then M = T A_bk, R = A_qa T (R over
-    //      -A_ba, which is dead), P = R A_bk + A_qk (over A_qk), all fp32
-    unit_lower_inverse(sNegAba, sT, sScr, w, n16, g4);
-    tri_mm(sT, sAbk, nullptr, sM, w, n16, g4);
-    tri_mm(sAqa, sT, nullptr, sNegAba, w, n16, g4);
+    // ---- 4. T = (I - A_ba)^{-1} in fp32; R = A_qa T and M = T A_bk, then
+    //      P = R A_bk + A_qk, all fp32 through registers
+    unit_lower_inverse(sB0, sT, sScr, w, n16, g4);
+    const f32x4 none[3] = {zero4(), zero4(), zero4()};
+    f32x4 rt[3], mt[3], pt[3];
+    tri_mm(sB2, sT, none, rt, w, n16, g4);
+    tri_mm(sT, sB1, none, mt, w, n16, g4);
     __syncthreads();
-    float* sR = sNegAba;
-    tri_mm(sR, sAbk, sAqk, sAqk, w, n16, g4);
+    store_tiles(sB0, rt, w, n16, g4);      // R over -A_ba
+    store_tiles(sB2, mt, w, n16, g4);      // M over A_qa
     __syncthreads();
-    float* sP = sAqk;
+    float* sR = sB0;
+    float* sM = sB2;
+    tri_mm(sR, sB1, aqk, pt, w, n16, g4);
+    __syncthreads();
+    store_tiles(sB1, pt, w, n16, g4);      // P over A_bk
+    __syncthreads();
+    float* sP = sB1;
 
     // ---- 5. products over tokens (wave w: channels [32w, 32w + 32))
     bf16x8 tf[4][2], rf[4][2], mf[4][2], pf[4][2];
