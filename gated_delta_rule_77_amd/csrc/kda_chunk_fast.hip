@@ -46,6 +46,27 @@ using namespace fastc;
 
 namespace {
 
+// Lane n of each 16-lane row (a 16-token block, lanes n = token) receives the
+// row D tokens before its own: lane n - D of the same block when n >= D,
+// else lane n - D + 16 of the previous block.  Each source lane sends its
+// current row if that row stays inside the block, its previous-block row
+// otherwise; a DPP rotate within the 16-lane row moves it (no LDS).
+template <int D>
+__device__ __forceinline__ unsigned row_ror(unsigned x) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x120 + D, 0xF, 0xF, false);
+}
+
+template <int D>
+__device__ __forceinline__ uint4 rows_back(uint4 prev, uint4 cur, int n16) {
+    const bool own = n16 < 16 - D;
+    uint4 r;
+    r.x = row_ror<D>(own ? cur.x : prev.x);
+    r.y = row_ror<D>(own ? cur.y : prev.y);
+    r.z = row_ror<D>(own ? cur.z : prev.z);
+    r.w = row_ror<D>(own ? cur.w : prev.w);
+    return r;
+}
+
 constexpr int kOffRK = 64 * kLdG * 4;
 constexpr int kOffRQ = kOffRK + 64 * kLdK * 2;
 constexpr int kOffFac = kOffRQ + 64 * kLdK * 2;
@@ -121,7 +142,6 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
     } else {
         const int n = cd.x, p0 = cd.w;       // sequence, position of row 0 within it
-        const uint4 zero16 = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int X = 0; X < 3; X++) {
             const bf16* xin = X == 0 ? q : X == 1 ? k : v;
@@ -131,23 +151,34 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const float4 w4 = *reinterpret_cast<const float4*>(conv_w + (((size_t)X * H + h) * 128 + cw + e) * 4);
                 wt[e][0] = w4.x; wt[e][1] = w4.y; wt[e][2] = w4.z; wt[e][3] = w4.w;
             }
+            // every lane loads its own row of each block once; lanes 13..15 also
+            // hold the three rows before the chunk (block -1), from the sequence
+            // or, before its start, from the carried state (zeros without one)
+            uint4 xr[5];
+            xr[0] = make_uint4(0, 0, 0, 0);
+            if (n16 >= 13) {
+                const int src = p0 + n16 - 16;     // position in the sequence
+                if (src >= 0)
+                    xr[0] = *reinterpret_cast<const uint4*>(xin + ((size_t)(tok0 + n16 - 16) * H + h) * 128 + cw);
+                else if (cs0)
+                    xr[0] = *reinterpret_cast<const uint4*>(
+                        cs0 + ((((size_t)n * 3 + X) * 3 + (3 + src)) * H + h) * 128 + cw);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++)
+                xr[tt + 1] = *reinterpret_cast<const uint4*>(xin + base + roff(16 * tt + n16) + cw);
 #pragma unroll
             for (int tt = 0; tt < 4; tt++) {
-                const int r = min(16 * tt + n16, lastrow);
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) y[e] = 0.f;
+                // tap j (oldest first) reads the row 3 - j before this lane's row
+                const uint4 taps[4] = {rows_back<3>(xr[tt], xr[tt + 1], n16),
+                                       rows_back<2>(xr[tt], xr[tt + 1], n16),
+                                       rows_back<1>(xr[tt], xr[tt + 1], n16), xr[tt + 1]};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const int src = p0 + r - 3 + j;        // position in the sequence
-                    uint4 raw;
-                    if (src >= 0)
-                        raw = *reinterpret_cast<const uint4*>(xin + ((size_t)(tok0 + r - 3 + j) * H + h) * 128 + cw);
-                    else
-                        raw = cs0 ? *reinterpret_cast<const uint4*>(
-                                        cs0 + ((((size_t)n * 3 + X) * 3 + (3 + src)) * H + h) * 128 + cw)
-                                  : zero16;
-                    const bf16x8 xv = __builtin_bit_cast(bf16x8, raw);
+                    const bf16x8 xv = __builtin_bit_cast(bf16x8, taps[j]);
 #pragma unroll
                     for (int e = 0; e < 8; e++) y[e] = __builtin_fmaf(wt[e][j], (float)xv[e], y[e]);
                 }
