@@ -576,6 +576,18 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
                     dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * sl + n16] = accS[sl][b][e];
                 }
     }
+    // the gate logits of the rows this thread stores, issued before the
+    // chunk's products so that their latency hides under them
+    bf16x8 gpre[4];
+    if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
+            gpre[i] = bf16x8{};
+            if (row < len)
+                gpre[i] = *reinterpret_cast<const bf16x8*>(og.gate + ((size_t)(tok0 + row) * H + h) * 128 + c8);
+        }
+    }
     f32x4 accO[kOutNS];
     // V~ and the (Q . Gamma) S part of O, four slices at a time
 #pragma unroll
@@ -645,7 +657,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
             for (int m = 8; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);   // the row's 16 lanes
             const float r = 1.f / sqrtf(ss * (1.f / 128.f) + og.eps);
             if (row < len) {
-                const bf16x8 gt = *reinterpret_cast<const bf16x8*>(og.gate + off);
+                const bf16x8 gt = gpre[i];
                 bf16x8 yv;
 #pragma unroll
                 for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
