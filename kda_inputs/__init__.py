@@ -179,11 +179,10 @@ def make_decode(case: DecodeCase, device="cpu", seed: int = 0,
 def make_dplr(case: PrefillCase, device="cpu", seed: int = 0, T: Optional[int] = None,
               lengths: Optional[list] = None) -> dict:
     """A prefill draw (make_prefill) extended with the low-rank pair of the
-    general DPLR update: la = -sigmoid(b) * a_hat and lb = unit(a_hat + 0.5 n / sqrt(dk)),
-    with a_hat a unit direction and n standard normal, so that b leans on a
-    (the erase is strong) without being tied to it or to the write key k.
-    Both [B, T, H, dk] in the config dtype.  The beta logits b of the draw
-    only set the erase strength."""
+    general DPLR update: la = -s * a_hat and lb = unit(a_hat + 0.5 n / sqrt(dk)),
+    with a_hat a unit direction, s ~ U(0, 1) per token and head, and n
+    standard normal, so that b leans on a (a strong erase) without being tied
+    to it or to the write key k.  Both [B, T, H, dk] in the config dtype."""
     d = make_prefill(case, device=device, seed=seed, T=T, lengths=lengths)
     dev = torch.device(device)
     gen = _gen(dev, seed + 104729)
@@ -192,8 +191,9 @@ def make_dplr(case: PrefillCase, device="cpu", seed: int = 0, T: Optional[int] =
     B, Ttot, H, dk = d["B"], d["T"], d["H"], d["dk"]
     ah = _unit_rows(torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32))
     nz = torch.randn(B, Ttot, H, dk, generator=gen, device=dev, dtype=f32)
+    sc = torch.rand(B, Ttot, H, 1, generator=gen, device=dev, dtype=f32)
     d["lb"] = _unit_rows(ah + 0.5 * nz / dk ** 0.5).to(dt)
-    d["la"] = (-torch.sigmoid(d["b"].to(f32))[..., None] * ah).to(dt)
+    d["la"] = (-sc * ah).to(dt)
     return d
 
 
