@@ -257,6 +257,23 @@ def bench_fold(args, kda, torch, run, step_ms):
     mean = sum(ms) / len(ms)
     per_unit = 2 * 128 * 128 * 4 + W * FOLD_TOKEN_BYTES
     gbs = per_unit * N * H / (mean * 1e-3) / 1e9
+    # the verify pass over the same window: outputs of every draft token from
+    # the checkpoint (read once, not written)
+    qw = torch.stack([s["q"] for s in steps], dim=1).contiguous()
+    for _ in range(2):
+        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, st)
+    torch.cuda.synchronize()
+    vt = []
+    for _ in range(max(4, args.decode_reps * 4)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, st)
+        b.record()
+        vt.append((a, b))
+    torch.cuda.synchronize()
+    vms = sum(a.elapsed_time(b) for a, b in vt) / len(vt)
+    v_unit = 128 * 128 * 4 + W * (FOLD_TOKEN_BYTES + 2 * 128 + 2 * 128)   # state read + window in (+q) + o out
     return {
         "workload": f"decode_256 states, window of {W} draft tokens per sequence, all accepted",
         "calls_timed": len(ms),
@@ -264,6 +281,12 @@ def bench_fold(args, kda, torch, run, step_ms):
         "tokens_per_s": round(N * W / (mean * 1e-3), 1),
         "alg_GBps": round(gbs, 1),
         "vs_token_steps": round(W * step_ms / mean, 2),
+        "verify": {
+            "ms_per_call_mean": round(vms, 4),
+            "tokens_per_s": round(N * W / (vms * 1e-3), 1),
+            "alg_GBps": round(v_unit * N * H / (vms * 1e-3) / 1e9, 1),
+            "vs_token_steps": round(W * step_ms / vms, 2),
+        },
     }
 
 

@@ -9,6 +9,7 @@ Names follow the C ABI in include/kda.h:
     kda_chunk_fwd(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
                   chunk_size=64, output_final_state=True, workspace=None) -> (o, hT)
     kda_recurrent_step(q, k, v, g, beta, A, state) -> o     (state updated in place)
+    kda_recurrent_verify(q, k, v, g, beta, A, state) -> o    (window outputs, state read only)
     kda_recurrent_fold(k, v, g, beta, A, n_accept, state)    (state updated in place)
     kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, ...) -> (y, hT, conv_state)
     kda_layer_step(q_in, k_in, v_in, conv_w, conv_state, g, beta, A, state, gate, norm_w) -> y
@@ -28,7 +29,7 @@ from typing import Optional
 
 __all__ = [
     "KdaError", "lib", "lib_path", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_fold",
-    "kda_layer_fwd", "kda_layer_step", "kda_layer_fwd_workspace_bytes",
+    "kda_recurrent_verify", "kda_layer_fwd", "kda_layer_step", "kda_layer_fwd_workspace_bytes",
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
     "kda_recurrent_step_supported", "kda_chunk_fwd_mode", "kda_recurrent_step_mode", "MODES",
     "kda_dplr_chunk_fwd", "kda_dplr_recurrent_step", "kda_dplr_chunk_fwd_workspace_bytes",
@@ -45,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_debug", "kda_chunk_fwd_timed", "kda_recurrent_step", "kda_recurrent_fold",
     "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step", "kda_chunk_fwd_mode",
     "kda_recurrent_step_mode", "kda_dplr_chunk_fwd_workspace_bytes", "kda_dplr_chunk_fwd",
-    "kda_dplr_chunk_fwd_timed", "kda_dplr_recurrent_step",
+    "kda_dplr_chunk_fwd_timed", "kda_dplr_recurrent_step", "kda_recurrent_verify",
 )
 # family modes of kda_chunk_fwd_mode / kda_recurrent_step_mode (kda_mode_t)
 MODES = {"kda": 0, "gla": 1, "deltanet": 2}
@@ -116,6 +117,8 @@ def lib() -> ctypes.CDLL:
     L.kda_dplr_chunk_fwd_timed.restype = i
     L.kda_dplr_chunk_fwd_timed.argtypes = ([vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 8
                                            + [vp, f, vp, sz, ctypes.POINTER(vp), i, vp])
+    L.kda_recurrent_verify.restype = i
+    L.kda_recurrent_verify.argtypes = [vp, vp, vp, f, f, f, f, vp] + [i] * 6 + [vp]
     L.kda_dplr_recurrent_step.restype = i
     L.kda_dplr_recurrent_step.argtypes = [vp, vp, vp, vp, vp, f, f, f, vp] + [i] * 5 + [vp]
     _lib = L
@@ -393,6 +396,37 @@ def _step(q, k, v, g, beta, A, state, mode):
         _check(lib().kda_recurrent_step(*args, _stream(dev)), "kda_recurrent_step")
     else:
         _check(lib().kda_recurrent_step_mode(*args, mode, _stream(dev)), "kda_recurrent_step_mode")
+    return o
+
+
+def kda_recurrent_verify(q, k, v, g, beta, A, state):
+    """Outputs of every token of each sequence's draft window from the
+    checkpoint state, which is only read: q, k [N, W, H, dk], v [N, W, H, dv]
+    (bf16 or fp32), g [N, W, H, dk] fp32, beta [N, W, H] fp32, A [H] fp32,
+    state [N, H, dk, dv] fp32.  Returns o [N, W, H, dv], bit-identical to W
+    kda_recurrent_step calls on a copy of the state."""
+    torch = _torch()
+    _req(q, "q")
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _req(k, "k", dt, dev)
+    _req(v, "v", dt, dev)
+    _req(g, "g", torch.float32, dev)
+    _req(beta, "beta", torch.float32, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(state, "state", torch.float32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [N, W, H, dk]")
+    N, W, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, W, H, dv):
+        raise ValueError("k, g must match q [N, W, H, dk] and v must be [N, W, H, dv]")
+    if beta.shape != (N, W, H) or A.shape != (H,) or state.shape != (N, H, dk, dv):
+        raise ValueError("beta [N, W, H], A [H] and state [N, H, dk, dv] expected")
+    o = torch.empty((N, W, H, dv), dtype=dt, device=dev)
+    _check(lib().kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                                      _ptr(state), _ptr(o), N, W, H, dk, dv, code, _stream(dev)),
+           "kda_recurrent_verify")
     return o
 
 

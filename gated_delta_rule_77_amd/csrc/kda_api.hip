@@ -373,6 +373,22 @@ kda_status_t kda_layer_step(const void* q_in, const void* k_in, const void* v_in
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v,
+                                  const float* g_logits, const float* beta_logits, const float* A,
+                                  const float* state, void* o, int N, int W, int H, int dk, int dv,
+                                  kda_dtype_t dtype, void* stream) {
+    if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || W < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H > 0x7fffffffLL || (long long)N * W * H > 0x7fffffffLL)
+        return KDA_ERR_INVALID_ARG;
+    if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || W == 0) return KDA_OK;
+    if (!q || !k || !v || !g_logits || !beta_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    hipError_t e = launch_verify(q, k, v, g_logits, beta_logits, A, state, o, N, W, H, dk, dv,
+                                 dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status_t kda_recurrent_fold(const void* k, const void* v, const float* g_logits,
                                 const float* beta_logits, const float* A, const int* n_accept,
                                 float* state, int N, int W, int H, int dk, int dv,

@@ -20,7 +20,7 @@ void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 {
     const int nh = blockIdx.x;          // sequence * H + head
     float* S = state + (size_t)nh * DK * DV;
-    __shared__ float s_al[DK], s_k[DK], s_q[DK];
+    __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
     // the state stream is the cost of this kernel: issue its loads first
     float4 Sv[16];
@@ -28,7 +28,7 @@ void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     const float ea = MODE == kModeDeltaNet ? 1.f : expf(A[nh % H]);
     kda_token_step<DK, DV, Tin, true, MODE>(Sv, k + (size_t)nh * DK, v + (size_t)nh * DV,
                                       MODE == kModeDeltaNet ? z : z + (size_t)nh * DK, bl[nh], ea, q + (size_t)nh * DK,
-                                      o + (size_t)nh * DV, s_al, s_k, s_q, s_red);
+                                      o + (size_t)nh * DV, s_al, s_k, s_q, s_red, s_qk);
     store_state<DK, DV>(Sv, S);
 }
 
@@ -63,6 +63,33 @@ void fold_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v, const flo
     store_state<DK, DV>(Sv, S);
 }
 
+// Verify pass of the same draft window ([K3-ATTN §6.2]): from the checkpoint
+// state, the outputs of every window token, with exactly the decode step
+// above, the state held in registers and never written back (the accepted
+// prefix is committed afterwards by the fold).  Window layout: q, k, z
+// [N, W, H, DK]; v, o [N, W, H, DV]; b [N, W, H].
+template <int DK, int DV, typename Tin>
+__global__ __launch_bounds__((DV / 4) * (DK / 16))
+void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                   const float* __restrict__ z, const float* __restrict__ bl,
+                   const float* __restrict__ A, const float* __restrict__ state,
+                   Tin* __restrict__ o, int W, int H)
+{
+    const int nh = blockIdx.x;          // sequence * H + head
+    const int n = nh / H, h = nh % H;
+    __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
+    __shared__ __align__(16) float s_red[2][DK / 16][DV];
+    float4 Sv[16];
+    load_state<DK, DV>(Sv, state + (size_t)nh * DK * DV);
+    const float ea = expf(A[h]);
+    for (int t = 0; t < W; t++) {
+        const size_t tok = ((size_t)n * W + t) * H + h;
+        if (t > 0) __syncthreads();     // the previous step's readers of the LDS vectors are done
+        kda_token_step<DK, DV, Tin, true>(Sv, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok], ea,
+                                          q + tok * DK, o + tok * DV, s_al, s_k, s_q, s_red, s_qk);
+    }
+}
+
 bool decode_supported(int dk, int dv) {
     return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
 }
@@ -92,6 +119,29 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
         : launch_decode_t<D, float>(q, k, v, z, b, A, state, o, N, H, s, mode);
     KDA_DEC(16) KDA_DEC(32) KDA_DEC(64) KDA_DEC(128)
 #undef KDA_DEC
+    return hipErrorInvalidValue;
+}
+
+template <int D, typename Tin>
+static hipError_t launch_verify_t(const void* q, const void* k, const void* v, const float* z,
+                                  const float* b, const float* A, const float* state, void* o,
+                                  int N, int W, int H, hipStream_t s) {
+    constexpr int NT = (D / 4) * (D / 16);
+    hipLaunchKernelGGL((verify_kernel<D, D, Tin>), dim3((unsigned)N * H), dim3(NT), 0, s,
+                       (const Tin*)q, (const Tin*)k, (const Tin*)v, z, b, A, state, (Tin*)o, W, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify(const void* q, const void* k, const void* v, const float* z,
+                         const float* b, const float* A, const float* state, void* o, int N,
+                         int W, int H, int dk, int dv, int dtype_bf16, hipStream_t s) {
+    (void)dv;
+#define KDA_VER(D)                                                                          \
+    if (dk == D) return dtype_bf16                                                          \
+        ? launch_verify_t<D, bf16>(q, k, v, z, b, A, state, o, N, W, H, s)                 \
+        : launch_verify_t<D, float>(q, k, v, z, b, A, state, o, N, W, H, s);
+    KDA_VER(16) KDA_VER(32) KDA_VER(64) KDA_VER(128)
+#undef KDA_VER
     return hipErrorInvalidValue;
 }
 

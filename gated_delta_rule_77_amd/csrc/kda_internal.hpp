@@ -185,6 +185,9 @@ hipError_t launch_dplr_intra(const ChunkArgs& a);   // MFMA path: the DPLR intra
 hipError_t launch_dplr_decode(const void* q, const void* k, const void* v, const void* la,
                               const void* lb, const float* z, const float* A, float* state,
                               void* o, int N, int H, int d, int dtype_bf16, hipStream_t s);
+hipError_t launch_verify(const void* q, const void* k, const void* v, const float* z,
+                         const float* b, const float* A, const float* state, void* o, int N,
+                         int W, int H, int dk, int dv, int dtype_bf16, hipStream_t s);
 hipError_t launch_fold(const void* k, const void* v, const float* z, const float* b,
                        const float* A, const int* n_accept, float* state, int N, int W, int H,
                        int dk, int dv, int dtype_bf16, hipStream_t s);

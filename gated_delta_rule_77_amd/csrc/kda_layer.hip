@@ -228,7 +228,7 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
     const int tid = threadIdx.x;
     float* S = state + (size_t)nh * D * D;
     __shared__ float s_in[3][D], s_o[D];
-    __shared__ float s_al[D], s_k[D], s_q[D];
+    __shared__ float s_al[D], s_k[D], s_q[D], s_qk[D / 16];
     __shared__ __align__(16) float s_red[2][D / 16][D];
     __shared__ float s_tmp[NT >= 64 ? NT / 64 : NT];
 
@@ -262,7 +262,7 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
     }
     __syncthreads();
     kda_token_step<D, D, float, true>(Sv, s_in[1], s_in[2], z + (size_t)nh * D, bl[nh],
-                                      expf(A[h]), s_in[0], s_o, s_al, s_k, s_q, s_red);
+                                      expf(A[h]), s_in[0], s_o, s_al, s_k, s_q, s_red, s_qk);
     __syncthreads();
     float so = 0.f;
     for (int i = tid; i < D; i += NT) so = __builtin_fmaf(s_o[i], s_o[i], so);

@@ -33,7 +33,8 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
                                                const Tin* __restrict__ vt, const float* __restrict__ zt,
                                                float b_logit, float ea, const Tin* __restrict__ qt,
                                                Tin* __restrict__ ot, float* s_al, float* s_k,
-                                               float* s_q, float (*s_red)[DK / 16][DV]) {
+                                               float* s_q, float (*s_red)[DK / 16][DV],
+                                               float* s_qk = nullptr) {
 #pragma clang fp contract(off)
     constexpr int CG = DV / 4, RG = DK / 16, NT = CG * RG;
     const int t = threadIdx.x;
@@ -49,8 +50,8 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
     for (int c = 0; c < 4; c++) vj[c] = to_f32(vt[cg * 4 + c]);
     __syncthreads();
 
-    // partial S'^T k (and S'^T q) over this thread's 16 rows
-    float p[4] = {0.f, 0.f, 0.f, 0.f}, r4[4] = {0.f, 0.f, 0.f, 0.f};
+    // partial S'^T k (and S'^T q, q . k) over this thread's 16 rows
+    float p[4] = {0.f, 0.f, 0.f, 0.f}, r4[4] = {0.f, 0.f, 0.f, 0.f}, qkp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         const int i = rg * 16 + r;
@@ -67,10 +68,14 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
             r4[1] = __builtin_fmaf(qa, Sv[r].y, r4[1]);
             r4[2] = __builtin_fmaf(qa, Sv[r].z, r4[2]);
             r4[3] = __builtin_fmaf(qa, Sv[r].w, r4[3]);
+            qkp = __builtin_fmaf(s_q[i], s_k[i], qkp);
         }
     }
     *reinterpret_cast<float4*>(&s_red[0][rg][cg * 4]) = make_float4(p[0], p[1], p[2], p[3]);
-    if (WITH_Q) *reinterpret_cast<float4*>(&s_red[1][rg][cg * 4]) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+    if (WITH_Q) {
+        *reinterpret_cast<float4*>(&s_red[1][rg][cg * 4]) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+        if (cg == 0) s_qk[rg] = qkp;
+    }
     __syncthreads();
 
     float P[4] = {0.f, 0.f, 0.f, 0.f}, R[4] = {0.f, 0.f, 0.f, 0.f};
@@ -87,9 +92,9 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const Tin* __re
 #pragma unroll
     for (int c = 0; c < 4; c++) u[c] = MODE == kModeGLA ? beta * vj[c] : beta * (vj[c] - P[c]);
     if (WITH_Q) {
-        float qk = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < DK; i++) qk = __builtin_fmaf(s_q[i], s_k[i], qk);
+        float qk = 0.f;       // row-group partials of q . k, summed in a fixed order
+#pragma unroll
+        for (int gidx = 0; gidx < RG; gidx++) qk += s_qk[gidx];
         if (rg == 0) {
 #pragma unroll
             for (int c = 0; c < 4; c++) ot[cg * 4 + c] = from_f32<Tin>(__builtin_fmaf(qk, u[c], R[c]));

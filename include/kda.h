@@ -364,6 +364,29 @@ KDA_API kda_status_t kda_layer_step(const void* q_in, const void* k_in, const vo
                             void* y, int N, int H, int d, kda_dtype_t dtype, void* stream);
 
 /*
+ * Verify pass over a stored draft window ([K3-ATTN §6.2], ReplaySSM): from the
+ * checkpoint `state`, the outputs of all W window tokens of every sequence,
+ * exactly as W successive kda_recurrent_step calls would produce them (same
+ * step, same operation order: the outputs are bit-identical), while `state`
+ * itself is only read.  Once the number of accepted tokens is known,
+ * kda_recurrent_fold commits that prefix from the same window.
+ *
+ *   q, k, g_logits  [N, W, H, dk]   dtype / dtype / fp32
+ *   v, o            [N, W, H, dv]   dtype
+ *   beta_logits     [N, W, H]       fp32
+ *   A               [H]             fp32
+ *   state           [N, H, dk, dv]  fp32, read only
+ *
+ * Each (sequence, head) state is read once for the whole window.  N = 0 or
+ * W = 0 is a no-op.  Supported shapes: as kda_recurrent_step.
+ */
+KDA_API kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v,
+                                          const float* g_logits, const float* beta_logits,
+                                          const float* A, const float* state, void* o, int N,
+                                          int W, int H, int dk, int dv, kda_dtype_t dtype,
+                                          void* stream);
+
+/*
  * Replay fold for speculative decoding ([K3-ATTN §6.2], ReplaySSM): instead
  * of a state snapshot per draft token, the caller keeps each window token's
  * inputs; once the number of accepted tokens is known, this call advances

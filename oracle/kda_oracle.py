@@ -40,6 +40,9 @@ Functions:
                                        extended with the decay (derivation in the
                                        design notes); exposes its intermediates
   packed                            -- loops `recurrence` over a cu_seqlens batch
+  decode_step, replay_fold,
+  verify_window                     -- the recurrent call, and the replay and verify
+                                       passes over a draft window
   recurrence_dplr_general           -- the diagonal-plus-low-rank update with its own
                                        low-rank pair (a, b) and write key
   chunkwise_dplr                    -- its chunked form with four C x C matrices
@@ -400,6 +403,20 @@ def replay_fold(k, v, z, b, A, state, n_accept):
         _, out[s] = recurrence(np.zeros_like(k[s, :n]), k[s, :n], v[s, :n], z[s, :n], b[s, :n], A,
                                state[s])
     return out
+
+
+def verify_window(q, k, v, z, b, A, state):
+    """The verify pass of [K3-ATTN §6.2] (ReplaySSM): from each sequence's
+    checkpoint state, the outputs of every token of its draft window
+    (q, k, z [N, W, H, d_k]; v [N, W, H, d_v]; b [N, W, H]), the state itself
+    left as it is (the accepted prefix is committed later by `replay_fold`).
+    Returns o [N, W, H, d_v]."""
+    q, k, v, z, b, A, state = map(_f64, (q, k, v, z, b, A, state))
+    N, W, H, dk = k.shape
+    o = np.zeros((N, W, H, v.shape[-1]))
+    for s in range(N):
+        o[s], _ = recurrence(q[s], k[s], v[s], z[s], b[s], A, state[s])
+    return o
 
 
 # ------------------------------------------------------------ around the core

@@ -233,3 +233,18 @@ def test_dplr_entry_points_reject_bad_arguments(L):
     assert st(*[FAKE] * 9, 4, 2, 96, 96, 1, None) == 2
     assert st(*([FAKE] * 3 + [None] + [FAKE] * 5), 4, 2, 128, 128, 1, None) == 1
     assert st(*[None] * 9, 0, 2, 128, 128, 1, None) == 0
+
+
+def test_recurrent_verify_rejects_bad_arguments(L):
+    fn = L.kda_recurrent_verify
+    fn.restype = ctypes.c_int
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    ok = [FAKE] * 8
+    assert fn(*ok, 4, 7, 2, 96, 96, 1, None) == 2
+    assert fn(*ok, -1, 7, 2, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, -1, 2, 128, 128, 1, None) == 1
+    assert fn(*ok, 4, 7, 2, 128, 128, 5, None) == 1
+    assert fn(*([FAKE] * 6 + [None, FAKE]), 4, 7, 2, 128, 128, 1, None) == 1   # state missing
+    assert fn(*([None] * 8), 0, 7, 2, 128, 128, 1, None) == 0
+    assert fn(*([None] * 8), 4, 0, 2, 128, 128, 1, None) == 0

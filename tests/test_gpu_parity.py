@@ -518,6 +518,58 @@ def test_fold_decode_workload_window(kda):
         assert rel_err(folded[n], r[0]) <= TOL_F32
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("fp32", 16), ("bf16", 64)])
+def test_verify_then_fold_bit_identical_to_recurrent_steps(kda, dtype, dk):
+    """[K3-ATTN §6.2] verify pass: every window token's output from the
+    checkpoint, bit-identical to the recurrent calls, with the checkpoint left
+    untouched; then the fold commits each sequence's accepted prefix, again
+    bit-identical.  Against the oracle's verify pass on the same inputs."""
+    N, H, W = 6, 3, 7
+    run, steps, win = _fold_window(dtype, dk, N, H, W, seed=24)
+    A = run["A"].cuda()
+    st0 = run["state"].cuda().contiguous()
+    ck = st0.clone()
+    dev = {key: win[key].cuda().contiguous() for key in win}
+    o = kda.kda_recurrent_verify(dev["q"], dev["k"], dev["v"], dev["z"], dev["b"], A, ck)
+    cur = st0.clone()
+    outs = []
+    for s in steps:
+        sd = to_dev(s)
+        outs.append(kda.kda_recurrent_step(sd["q"], sd["k"], sd["v"], sd["z"], sd["b"], A, cur))
+    ref = torch.stack(outs, 1)
+    n_acc = torch.tensor([7, 0, 3, 1, 6, 7], dtype=torch.int32)
+    kda.kda_recurrent_fold(dev["k"], dev["v"], dev["z"], dev["b"], A, n_acc.cuda(), ck)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref), float((o.float() - ref.float()).abs().max())
+    expect = st0.clone()
+    for n in range(N):
+        if int(n_acc[n]) == W:
+            expect[n] = cur[n]
+    full = [n for n in range(N) if int(n_acc[n]) == W]
+    none = [n for n in range(N) if int(n_acc[n]) == 0]
+    assert torch.equal(ck[full], expect[full]) and torch.equal(ck[none], st0[none])
+    ro = oracle.verify_window(win["q"], win["k"], win["v"], win["z"], win["b"], run["A"],
+                              run["state"])
+    e = rel_err(o, ro)
+    _report(f"verify vs oracle {dtype} d={dk}", o=e)
+    assert e <= (TOL_F32 if dtype == "fp32" else TOL_BF16)
+
+
+def test_verify_reads_state_only(kda):
+    """The checkpoint state is bit-for-bit unchanged by the verify pass, and
+    W = 0 is a no-op."""
+    run, _, win = _fold_window("bf16", 128, 4, 2, 5, seed=25)
+    st = run["state"].cuda().contiguous()
+    st0 = st.clone()
+    dev = {key: win[key].cuda().contiguous() for key in win}
+    kda.kda_recurrent_verify(dev["q"], dev["k"], dev["v"], dev["z"], dev["b"], run["A"].cuda(), st)
+    kda.kda_recurrent_verify(dev["q"][:, :0].contiguous(), dev["k"][:, :0].contiguous(),
+                             dev["v"][:, :0].contiguous(), dev["z"][:, :0].contiguous(),
+                             dev["b"][:, :0].contiguous(), run["A"].cuda(), st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st0)
+
+
 # ------------------------------------------------------ segment layouts
 
 @pytest.mark.parametrize("B,T,H,heads", [(1, 8192, 1, [0]), (3, 1500, 5, [0, 4]),

@@ -640,3 +640,20 @@ def test_dplr_decode_step_is_one_token_of_the_recurrence():
         r = lambda x: x[n:n + 1]
         o1, S1 = oracle.recurrence_dplr_general(r(q), r(k), r(v), r(a), r(bv), r(z), A, st[n])
         assert np.allclose(o[n], o1[0], atol=1e-14) and np.allclose(S[n], S1, atol=1e-14)
+
+
+def test_verify_window_matches_explicit_matrices_and_leaves_state():
+    """[K3-ATTN §6.2] verify pass: every draft token's output from the
+    checkpoint, checked against the explicit-matrix recurrence of
+    [LA-KDA §5.2]; the checkpoint passed in is not modified."""
+    rng = np.random.default_rng(60)
+    N, W, H, dk, dv = 3, 5, 2, 6, 4
+    q, k, v, z, b, A, _ = _rand_case(rng, N * W, H, dk, dv)
+    sh = lambda x: x.reshape(N, W, *x.shape[1:])   # noqa: E731
+    st = 0.3 * rng.standard_normal((N, H, dk, dv))
+    st0 = st.copy()
+    o = oracle.verify_window(sh(q), sh(k), sh(v), sh(z), sh(b), A, st)
+    assert np.array_equal(st, st0)
+    for n in range(N):
+        on, _ = oracle.recurrence_matrix(sh(q)[n], sh(k)[n], sh(v)[n], sh(z)[n], sh(b)[n], A, st[n])
+        assert np.allclose(o[n], on, atol=1e-13)
