@@ -9,14 +9,9 @@ namespace kda {
 
 // ---------------------------------------------------------------- workspace
 //
-// [0, 256)                 header: int32 total number of chunks
-// chunk table              cap x int4 (sequence, first token, length, position in sequence)
-// sequence table           N x int2  (first chunk id, number of chunks)
-// chunk records            cap x H records of rec_bytes each (MFMA path: head
-//                          major, so one head's chunks are contiguous)
-//
 // Chunks are numbered sequence by sequence in token order; `cap` bounds their
-// number for both layouts: B*ceil(T/C) + N.
+// number for both layouts: B*ceil(T/C) + N.  The full layout is given with
+// ws_layout below.
 struct WsLayout {
     int cap;                 // chunk capacity
     int seg_chunks;          // chunks per segment of the MFMA chain (0 on the fp32 path)
@@ -106,7 +101,7 @@ inline int pick_seg_chunks(int cap, int H) {
 // seqs       N x int2 (first chunk id, number of chunks)
 // seqsegs    N x int2 (first segment id, number of segments)      [MFMA path]
 // segs       seg_cap x int4 (sequence, first chunk id, chunks, index in sequence)
-// recs       H x cap chunk records (MFMA path), cap x H (fp32 path)
+// recs       cap x H chunk records of rec_bytes each, (chunk, head) order
 // sstart     seg_cap x H x 128 x 128 fp32: state entering each segment
 // rm         seg_cap x H x 128 x 256 fp32: [R | M] of each segment
 inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, bool fast,
