@@ -20,7 +20,9 @@ bool prefill_sizes_ok(int B, int T, int H, int dk, int dv, int N, int chunk) {
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || N < 0 || chunk < 1) return false;
     if ((long long)B * T > 0x7fffffffLL) return false;            // token index fits int32
     if ((long long)N * H > 0x7fffffffLL) return false;
-    return chunk_capacity(B, T, N, chunk) >= 0;
+    const int cap = chunk_capacity(B, T, N, chunk);
+    // one workgroup per (chunk, head) and per (segment, head): grids stay within int32
+    return cap >= 0 && (long long)cap * H <= 0x7fffffffLL;
 }
 
 kda_status_t run_prefill(const void* q, const void* k, const void* v, const float* z,

@@ -248,3 +248,12 @@ def test_recurrent_verify_rejects_bad_arguments(L):
     assert fn(*([FAKE] * 6 + [None, FAKE]), 4, 7, 2, 128, 128, 1, None) == 1   # state missing
     assert fn(*([None] * 8), 0, 7, 2, 128, 128, 1, None) == 0
     assert fn(*([None] * 8), 4, 0, 2, 128, 128, 1, None) == 0
+
+
+def test_grid_limits_are_validated(L):
+    """One workgroup per (chunk, head): chunk capacity x heads must stay within
+    int32, checked on the host (no launch with a wrapped grid)."""
+    L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    # B * T fits int32, but ceil(T / 16) * H does not
+    assert L.kda_chunk_fwd_workspace_bytes(1, 2000000000, 1024, 16, 16, 1, 16, 0) == 0
+    assert _chunk(L, q=FAKE, k=FAKE, v=FAKE, z=FAKE, b=FAKE, A=FAKE, o=FAKE, T=2000000000, H=1024) == 1
