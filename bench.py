@@ -49,7 +49,7 @@ DECODE_BYTES = 2 * 128 * 128 * 4 + PREFILL_BYTES
 DPLR_BYTES = 2048
 DPLR_INTRA_BYTES = 1792
 # chunk records the intra kernels write (bytes per chunk and head)
-KDA_RECORD_BYTES = 74240
+KDA_RECORD_BYTES = 72192
 DPLR_RECORD_BYTES = 98816
 
 

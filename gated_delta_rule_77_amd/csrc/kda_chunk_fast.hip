@@ -445,14 +445,16 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             const f32x4 t1 = {n1.x * b1.x, n1.y * b1.y, n1.z * b1.z, n1.w * b1.w};
             tf[tb][kb] = pack_frag(t0, t1);
         }
-    // A_qk rows of token block w, same k-slot order, to the record
+    // A_qk rows of token block w, same k-slot order, to the record (the
+    // all-zero fragments above the diagonal are not stored)
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
+        if (!rec_a_stored(w, kb)) continue;
         const int row = 16 * w + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
         const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j0);
         const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j1);
         const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
-        *reinterpret_cast<bf16x8*>(rec + REC_A + ((w * 2 + kb) * 64 + lane) * 16) = pack_frag(x0, x1);
+        *reinterpret_cast<bf16x8*>(rec + REC_A + (rec_a_frag(w, kb) * 64 + lane) * 16) = pack_frag(x0, x1);
     }
     // W^T = (K . Gamma)^T T^T: tiles [channel][token], stored negated as the
     // chain's A operand (token block tb, k-step w)
@@ -537,7 +539,9 @@ __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __res
     } else {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
-            f.a[kb] = *reinterpret_cast<const bf16x8*>(rec + RL::A + ((w * 2 + kb) * 64 + lane) * 16);
+            f.a[kb] = rec_a_stored(w, kb)
+                          ? *reinterpret_cast<const bf16x8*>(rec + RL::A + (rec_a_frag(w, kb) * 64 + lane) * 16)
+                          : bf16x8{};
     }
 #pragma unroll
     for (int sl = 0; sl < kOutNS; sl++)
@@ -633,7 +637,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
         for (int kb = 0; kb < 2; kb++) {
             s0 = mfma_bf16(f.k[kb], vfr[kb], s0);
             s1 = mfma_bf16(f.k[2 + kb], vfr[kb], s1);
-            if constexpr (!DPLR) acc = mfma_bf16(f.a[kb], vfr[kb], acc);
+            if (!DPLR && rec_a_stored(w, kb)) acc = mfma_bf16(f.a[kb], vfr[kb], acc);
         }
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(s0, s1);
 #pragma unroll

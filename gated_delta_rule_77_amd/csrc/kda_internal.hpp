@@ -48,9 +48,15 @@ constexpr int REC_W = 0;        // -W^T fragments [4 token block][4 kstep][64 la
 constexpr int REC_Q = 16384;    // (Q . Gamma)^T fragments, same layout
 constexpr int REC_K = 32768;    // Kbar^T fragments [4 row block][2 half][2 kstep][64 lane][8] bf16
 constexpr int REC_U = 49152;    // U tiles [8 slice][4 token block][64 lane][4] bf16
-constexpr int REC_A = 65536;    // A_qk row fragments [4 token block][2 kstep][64 lane][8] bf16
-constexpr int REC_G = 73728;    // gamma_C [128] fp32
-constexpr int REC_BYTES = 74240;
+constexpr int REC_A = 65536;    // A_qk row fragments [6 nonzero (token block, kstep)][64 lane][8] bf16
+constexpr int REC_G = 71680;    // gamma_C [128] fp32
+constexpr int REC_BYTES = 72192;
+// A_qk is causal: token blocks 0 and 1 (rows 0..31) have no entry in k-step 1
+// (columns 32..63), so only six of the eight row fragments are stored, in the
+// order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__host__ __device__ constexpr int rec_a_frag(int tb, int kb) { return tb < 2 ? tb : 2 * tb - 2 + kb; }
+__host__ __device__ constexpr bool rec_a_stored(int tb, int kb) { return tb >= 2 || kb == 0; }
+static_assert(rec_a_frag(3, 1) == 5 && REC_A + 6 * 1024 == REC_G, "A_qk fragments fill the gap");
 }  // namespace fast
 
 // record of the MFMA path of the general DPLR update: what the chain needs
