@@ -90,8 +90,9 @@ static_assert(3 * 64 * kLdA * 4 + 4 * 256 * 4 <= kOffFac, "A_kk, A_qk, N and P a
 // the carried state cs0 or zeros), Swish, and for q and k the L2Norm over the
 // head's 128 channels; the results are rounded to bf16 as the core's inputs.
 // MODE selects a row of the family table ([LA-KDA §4]): kModeDeltaNet skips
-// the gate (G = 0, every factor 1); kModeGLA drops A_kk (T = Diag(beta)) and
-// stores W = 0, so the chain kernels see V~ = U = Diag(beta) V.
+// the gate (G = 0, every factor 1); kModeGLA drops A_kk (T = Diag(beta)), so
+// W = 0: it is not stored, and the GLA chain kernels read none (V~ = U =
+// Diag(beta) V).
 template <bool DBG, bool CONV, int MODE>
 __global__ __launch_bounds__(256, 2)
 void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -460,15 +461,15 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // chain's A operand (token block tb, k-step w)
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) {
-        f32x4 wt0 = zero4(), wt1 = zero4();
         if constexpr (MODE != kModeGLA) {
+            f32x4 wt0 = zero4(), wt1 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
                 wt0 = mfma_bf16(kgf[kb][0], tf[tb][kb], wt0);
                 wt1 = mfma_bf16(kgf[kb][1], tf[tb][kb], wt1);
             }
+            *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
         }
-        *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
     }
     // U = T V: tiles (slice 2w + cb, token block tb)
 #pragma unroll
@@ -506,6 +507,11 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // [16w, 16w + 16) and owns state rows [32w, 32w + 32) as 8 pairs of fp32 C
 // tiles (one pair per 16-column slice).  The bf16 copy of wave w's tiles is
 // exactly the B fragment of k-step w.
+// Chain kinds: the KDA record; the GLA record, whose W is zero and neither
+// stored nor read (V~ = U, and the M columns of a transition only decay); the
+// general DPLR record (X~ = Wb S, the folded Uo and Cs terms).
+constexpr int kChainKDA = 0, kChainGLA = 1, kChainDPLR = 2;
+
 constexpr int kOutNS = 8;       // 16-column slices
 constexpr int kOutDepth = 3;    // record prefetch ring depth (chunks)
 constexpr int kLdO = 136;       // bf16 output staging rows [64][kLdO]
@@ -520,13 +526,15 @@ struct OutFrags {
     float4 g0, g1;              // gamma_C for the wave's two row tiles
 };
 
-template <bool DPLR>
+template <int CK>
 __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __restrict__ rec, int w,
                                                int lane, int g4) {
+    constexpr bool DPLR = CK == kChainDPLR;
     using RL = RecLayout<DPLR>;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-        f.w[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::W + ((w * 4 + ks) * 64 + lane) * 16);
+        f.w[ks] = CK == kChainGLA ? bf16x8{}
+                                  : *reinterpret_cast<const bf16x8*>(rec + RL::W + ((w * 4 + ks) * 64 + lane) * 16);
         f.k[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::K + ((w * 4 + ks) * 64 + lane) * 16);
         f.q[ks] = *reinterpret_cast<const bf16x8*>(rec + RL::Q + ((w * 4 + ks) * 64 + lane) * 16);
     }
@@ -563,12 +571,13 @@ struct OutGate {
 // One chunk for one wave over all slices.  KDA: V~ = U - W S,
 // O = (Q . Gamma) S + A_qk V~, S <- Diag(gamma_C) S + Kbar^T V~.  DPLR:
 // X~ = Wb S, O = Q' S + Uo, S <- Diag(gamma_C) S + Abar^T X~ + Cs.
-template <bool DBG, bool GATE, bool DPLR>
+template <bool DBG, bool GATE, int CK>
 __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, int len,
                                          f32x4 (&accS)[kOutNS][2], bf16* sS, bf16* sVt, bf16* sO,
                                          bf16* __restrict__ o, float* __restrict__ dbgS, int H,
                                          int h, int w, int lane, int n16, int g4, int tid,
                                          const OutGate& og) {
+    constexpr bool DPLR = CK == kChainDPLR;
     if (DBG) {
 #pragma unroll
         for (int sl = 0; sl < kOutNS; sl++)
@@ -609,7 +618,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
             f32x4 acc = DPLR ? unpack4(f.u[sl]) : zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
-                accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
+                if constexpr (CK != kChainGLA) accV = mfma_bf16(f.w[ks], sf[s4][ks], accV);
                 acc = mfma_bf16(f.q[ks], sf[s4][ks], acc);
             }
             *reinterpret_cast<bf16x4*>(sVt + ((sl * 4 + w) * 64 + lane) * 4) = pack4(accV);
@@ -676,7 +685,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
 
 // grid: seg_cap * H blocks, block = (segment, head).  With GATE the rows
 // stored are the layer's gated RMSNorm of O instead of O.
-template <bool DBG, bool GATE, bool DPLR>
+template <bool DBG, bool GATE, int CK>
 __global__ __launch_bounds__(256, 1)
 void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
                     const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
@@ -684,6 +693,7 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
                     bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS,
                     const bf16* __restrict__ gate, const float* __restrict__ norm_w, float rms_eps)
 {
+    constexpr bool DPLR = CK == kChainDPLR;
     const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
     if (seg_id >= hdr[1]) return;
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
@@ -727,7 +737,7 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
     OutFrags F[D];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < D - 1; u++) load_out_frags<DPLR>(F[u], rec(min(u, nch - 1)), w, lane, g4);
+        for (int u = 0; u < D - 1; u++) load_out_frags<CK>(F[u], rec(min(u, nch - 1)), w, lane, g4);
     }
     __syncthreads();
     const int nfull = nch / D * D;
@@ -735,9 +745,9 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 #pragma unroll
         for (int u = 0; u < D; u++) {
             // unconditional prefetch (index clamped) keeps the wait counts exact
-            load_out_frags<DPLR>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
+            load_out_frags<CK>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
             const int t0 = (ci + u) * C;
-            out_step<DBG, GATE, DPLR>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
+            out_step<DBG, GATE, CK>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
                                 dbgS, H, h, w, lane, n16, g4, tid, og);
         }
     }
@@ -745,7 +755,7 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            out_step<DBG, GATE, DPLR>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
+            out_step<DBG, GATE, CK>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
                                 o, dbgS, H, h, w, lane, n16, g4, tid, og);
         }
 
@@ -784,12 +794,15 @@ struct StageRegs {
     u32x4 w0, w1, k0, k1, x0, x1, x2, x3, g;      // x: U (two pieces) or Cs (four)
 };
 
-template <bool DPLR>
+template <int CK>
 __device__ __forceinline__ StageRegs stage_load(const uint8_t* __restrict__ rec, int t) {
+    constexpr bool DPLR = CK == kChainDPLR;
     using RL = RecLayout<DPLR>;
     auto ld = [&](int off) { return *reinterpret_cast<const u32x4*>(rec + off + t * 16); };
     StageRegs r;
-    r.w0 = ld(RL::W); r.w1 = ld(RL::W + 8192);
+    if constexpr (CK != kChainGLA) {
+        r.w0 = ld(RL::W); r.w1 = ld(RL::W + 8192);
+    }
     r.k0 = ld(RL::K); r.k1 = ld(RL::K + 8192);
     if constexpr (DPLR) {
         r.x0 = ld(RL::C); r.x1 = ld(RL::C + 8192); r.x2 = ld(RL::C + 16384); r.x3 = ld(RL::C + 24576);
@@ -800,11 +813,14 @@ __device__ __forceinline__ StageRegs stage_load(const uint8_t* __restrict__ rec,
     return r;
 }
 
-template <bool DPLR>
+template <int CK>
 __device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int t) {
+    constexpr bool DPLR = CK == kChainDPLR;
     using TS = TransStage<DPLR>;
     auto stv = [&](int off, u32x4 x) { *reinterpret_cast<u32x4*>(st + off + t * 16) = x; };
-    stv(TS::W, r.w0); stv(TS::W + 8192, r.w1);
+    if constexpr (CK != kChainGLA) {
+        stv(TS::W, r.w0); stv(TS::W + 8192, r.w1);
+    }
     stv(TS::K, r.k0); stv(TS::K + 8192, r.k1);
     if constexpr (DPLR) {
         stv(TS::C, r.x0); stv(TS::C + 8192, r.x1); stv(TS::C + 16384, r.x2); stv(TS::C + 24576, r.x3);
@@ -815,12 +831,27 @@ __device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int
 }
 
 // One chunk for wave w from the staged record.  KDA: V~ = U - W S (U = 0 for
-// M), S <- Diag(gamma_C) S + Kbar^T V~.  DPLR: X~ = Wb S,
-// S <- Diag(gamma_C) S + Abar^T X~ + Cs (Cs for R only).
-template <bool DPLR>
+// M), S <- Diag(gamma_C) S + Kbar^T V~.  GLA: V~ = U, so the M columns
+// (V~ = 0) only decay.  DPLR: X~ = Wb S, S <- Diag(gamma_C) S + Abar^T X~ + Cs
+// (Cs for R only).
+template <int CK>
 __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2], int w, int lane,
                                             int g4) {
+    constexpr bool DPLR = CK == kChainDPLR;
     using TS = TransStage<DPLR>;
+    const float* gC = reinterpret_cast<const float*>(st + TS::G);
+    if (CK == kChainGLA && w >= 4) {
+#pragma unroll
+        for (int rt = 0; rt < 8; rt++) {
+            const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                f32x4& a = acc[rt][j];
+                a[0] *= g.x; a[1] *= g.y; a[2] *= g.z; a[3] *= g.w;
+            }
+        }
+        return;
+    }
     // S fragments of k-step ks: row tiles 2ks, 2ks + 1 of each owned slice
     bf16x8 sf[4][2];
 #pragma unroll
@@ -838,11 +869,13 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
                 vt[tb][j] = unpack4(*reinterpret_cast<const bf16x4*>(
                     st + TS::U + (((2 * w + j) * 4 + tb) * 64 + lane) * 8));
         }
+        if constexpr (CK != kChainGLA) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + TS::W + ((tb * 4 + ks) * 64 + lane) * 16);
+            for (int ks = 0; ks < 4; ks++) {
+                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + TS::W + ((tb * 4 + ks) * 64 + lane) * 16);
 #pragma unroll
-            for (int j = 0; j < 2; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
+                for (int j = 0; j < 2; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
+            }
         }
     }
     // V~ fragments over tokens, then S <- Diag(gamma_C) S + Kbar^T V~
@@ -851,7 +884,6 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int j = 0; j < 2; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
-    const float* gC = reinterpret_cast<const float*>(st + TS::G);
 #pragma unroll
     for (int rt = 0; rt < 8; rt++) {
         const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
@@ -871,12 +903,13 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
 }
 
 // grid: seg_cap * H blocks, block = (segment, head)
-template <bool DPLR>
+template <int CK>
 __global__ __launch_bounds__(512, 1)
 void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
                       const int2* __restrict__ seqsegs, const int* __restrict__ hdr, int H,
                       float* __restrict__ rm)
 {
+    constexpr bool DPLR = CK == kChainDPLR;
     const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
     if (seg_id >= hdr[1]) return;
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
@@ -904,23 +937,23 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
             return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * RecLayout<DPLR>::BYTES;
         };
         // chunk c sits in stage c & 1; its copy passes through register set c & 1
-        StageRegs R0 = stage_load<DPLR>(rec(0), tid);
-        StageRegs R1 = stage_load<DPLR>(rec(1), tid);
-        stage_store<DPLR>(R0, stage[0], tid);
-        R0 = stage_load<DPLR>(rec(2), tid);
+        StageRegs R0 = stage_load<CK>(rec(0), tid);
+        StageRegs R1 = stage_load<CK>(rec(1), tid);
+        stage_store<CK>(R0, stage[0], tid);
+        R0 = stage_load<CK>(rec(2), tid);
         __syncthreads();
         int c = 0;
         for (; c + 2 <= nch; c += 2) {
-            trans_chunk<DPLR>(stage[0], acc, w, lane, g4);
-            stage_store<DPLR>(R1, stage[1], tid);    // chunk c + 1
-            R1 = stage_load<DPLR>(rec(c + 3), tid);
+            trans_chunk<CK>(stage[0], acc, w, lane, g4);
+            stage_store<CK>(R1, stage[1], tid);    // chunk c + 1
+            R1 = stage_load<CK>(rec(c + 3), tid);
             __syncthreads();
-            trans_chunk<DPLR>(stage[1], acc, w, lane, g4);
-            stage_store<DPLR>(R0, stage[0], tid);    // chunk c + 2
-            R0 = stage_load<DPLR>(rec(c + 4), tid);
+            trans_chunk<CK>(stage[1], acc, w, lane, g4);
+            stage_store<CK>(R0, stage[0], tid);    // chunk c + 2
+            R0 = stage_load<CK>(rec(c + 4), tid);
             __syncthreads();
         }
-        if (c < nch) trans_chunk<DPLR>(stage[0], acc, w, lane, g4);
+        if (c < nch) trans_chunk<CK>(stage[0], acc, w, lane, g4);
     }
 #pragma unroll
     for (int rt = 0; rt < 8; rt++)
@@ -1020,7 +1053,7 @@ void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ 
 
 }  // namespace
 
-template <bool DPLR>
+template <int CK>
 hipError_t launch_chain(const ChunkArgs& a) {
     const int* hdr = reinterpret_cast<const int*>(a.ws);
     const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
@@ -1031,7 +1064,7 @@ hipError_t launch_chain(const ChunkArgs& a) {
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
     hipError_t e;
     const dim3 gc((unsigned)((long long)a.L.seg_cap * a.H));
-    hipLaunchKernelGGL((seg_trans_kernel<DPLR>), gc, dim3(512), 0, a.stream, (const uint8_t*)recs,
+    hipLaunchKernelGGL((seg_trans_kernel<CK>), gc, dim3(512), 0, a.stream, (const uint8_t*)recs,
                        segs, seqsegs, hdr, a.H, rm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
@@ -1042,12 +1075,12 @@ hipError_t launch_chain(const ChunkArgs& a) {
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     const bf16* gate = static_cast<const bf16*>(a.gate);
 #define KDA_OUT(DBG, GATE)                                                                       \
-    hipLaunchKernelGGL((seg_out_kernel<DBG, GATE, DPLR>), gc, dim3(256), 0, a.stream,            \
+    hipLaunchKernelGGL((seg_out_kernel<DBG, GATE, CK>), gc, dim3(256), 0, a.stream,            \
                        (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, \
                        (bf16*)a.o, a.hT, DBG ? a.dbg_state : (float*)nullptr, gate, a.norm_w,    \
                        a.rms_eps)
     // the debug and gated variants exist for KDA only (the API enforces it)
-    if constexpr (DPLR) {
+    if constexpr (CK != kChainKDA) {
         KDA_OUT(false, false);
     } else {
         if (a.dbg_state) KDA_OUT(true, false);
@@ -1078,14 +1111,14 @@ hipError_t launch_fast(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
-    return launch_chain<false>(a);
+    return a.mode == kModeGLA ? launch_chain<kChainGLA>(a) : launch_chain<kChainKDA>(a);
 }
 
 hipError_t launch_fast_dplr(const ChunkArgs& a) {
     hipError_t e = launch_dplr_intra(a);
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
-    return launch_chain<true>(a);
+    return launch_chain<kChainDPLR>(a);
 }
 
 }  // namespace kda
