@@ -87,20 +87,59 @@ def code_sha1(path: str) -> str:
     return hashlib.sha1(" ".join(text.split()).encode()).hexdigest()
 
 
+# sources whose code the counter records in profiles/ were taken from
+PREFILL_SOURCES = ["gated_delta_rule_77_amd/csrc/kda_chunk_fast.hip",
+                   "gated_delta_rule_77_amd/csrc/kda_fast_common.hpp",
+                   "gated_delta_rule_77_amd/csrc/kda_internal.hpp",
+                   "gated_delta_rule_77_amd/csrc/kda_device.hpp"]
+DECODE_SOURCES = ["gated_delta_rule_77_amd/csrc/kda_decode.hip",
+                  "gated_delta_rule_77_amd/csrc/kda_step.hpp",
+                  "gated_delta_rule_77_amd/csrc/kda_internal.hpp",
+                  "gated_delta_rule_77_amd/csrc/kda_device.hpp"]
+
+
+def sources_sha1(paths) -> dict:
+    return {p: code_sha1(os.path.join(ROOT, p)) for p in paths}
+
+
+def _counter_record(name: str):
+    """A committed counter record (profiles/<name>.json), or None when any of
+    the sources it was taken from has changed since."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    try:
+        rec = json.load(open(path))
+        src = rec["sources"]
+        if sources_sha1(src.keys()) != src:
+            return None
+    except (OSError, ValueError, KeyError, AttributeError):
+        return None
+    return rec
+
+
 def _traffic_for(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/traffic_long_1m.json), or None when the kernel code changed
     since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_long_1m.json")
-    try:
-        rec = json.load(open(path))
-        sha = code_sha1(os.path.join(ROOT, rec["source"]))
-    except (OSError, ValueError, KeyError):
-        return None
-    if sha != rec.get("source_code_sha1"):
-        return None
-    k = rec.get("kernels", {}).get(kernel)
+    rec = _counter_record("traffic_long_1m")
+    k = None if rec is None else rec.get("kernels", {}).get(kernel)
     return None if k is None else int(k["hbm_bytes"])
+
+
+def _mfma_counters(call_ms: float):
+    """MFMA utilisation of the prefill kernels from the committed counter
+    record (profiles/mfma_long_1m.json): per kernel the busy fraction of the
+    matrix cores (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
+    the MFMA FLOPs the hardware executed (bf16 and f32 MOPS x 512), which
+    include the chain's re-runs; None when the kernel code changed."""
+    rec = _counter_record("mfma_long_1m")
+    if rec is None:
+        return None
+    ks = rec["kernels"]
+    hw = sum(k["bf16_flop"] + k["f32_flop"] for k in ks.values())
+    return {"busy_frac": {n: k["busy_frac"] for n, k in ks.items()},
+            "hw_mfma_TFLOP_per_call": round(hw / 1e12, 4),
+            "hw_mfma_TFLOPs": round(hw / (call_ms * 1e-3) / 1e12, 1),
+            "hw_mfma_frac": round(hw / (call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
 
 
 def bench_prefill(args, kda, torch, KI):
@@ -178,6 +217,7 @@ def bench_prefill(args, kda, torch, KI):
         "path_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
         "path_alg_TFLOPs": round(call_tfs, 2),
         "mfma_frac_algorithmic": round(call_tfs / MFMA_BF16_PEAK_TFS, 4),
+        "mfma_counters": _mfma_counters(avg["call"]),
     }
     cpu_inputs = {k: d[k][:, :args.cpu_tokens].cpu() for k in ("q", "k", "v", "z", "b")}
     cpu_inputs.update(A=d["A"].cpu(), h0=d["h0"].cpu())
@@ -222,8 +262,23 @@ def bench_decode(args, kda, torch, KI):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
                 "algorithmic bytes and may exceed the HBM rate",
+        "traffic": _decode_traffic(mean),
         "fold": fold,
     }
+
+
+def _decode_traffic(step_ms: float):
+    """Bytes the decode kernel moved between L2 and the memory fabric per step
+    (FETCH_SIZE and WRITE_SIZE, scaled as in the prefill record) from
+    profiles/traffic_decode_256.json, and their rate at the measured step
+    time; None when the kernel code changed since the counters were taken.
+    The counters cannot tell HBM from Infinity Cache hits."""
+    rec = _counter_record("traffic_decode_256")
+    if rec is None:
+        return None
+    b = rec["kernels"]["decode_kernel"]["bytes"]
+    return {"bytes_per_step": b, "GBps": round(b / (step_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(b / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 # Replay fold: a window of 7 draft tokens (the pages' num_speculative_tokens),
