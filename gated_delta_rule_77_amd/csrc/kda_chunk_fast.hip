@@ -568,6 +568,42 @@ struct OutGate {
     float eps;
 };
 
+// 64 rows x 256 bytes of O (or, with GATE, of Sigmoid(gate) * RMSNorm(O)),
+// 16 bytes per lane.  FULL: every row is inside the sequence (a uniform
+// test by the caller), so the stores need no per-row test.
+template <bool GATE, bool FULL>
+__device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[4],
+                                           bf16* __restrict__ o, int tok0, int len, int H, int h,
+                                           int tid, const OutGate& og) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
+        const size_t off = ((size_t)(tok0 + row) * H + h) * 128 + c8;
+        if constexpr (GATE) {
+            const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + row * kLdO + c8);
+            float ov[8], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                ov[e] = (float)ob[e];
+                ss = __builtin_fmaf(ov[e], ov[e], ss);
+            }
+#pragma unroll
+            for (int m = 8; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);   // the row's 16 lanes
+            const float r = 1.f / sqrtf(ss * (1.f / 128.f) + og.eps);
+            if (FULL || row < len) {
+                const bf16x8 gt = gpre[i];
+                bf16x8 yv;
+#pragma unroll
+                for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
+                *reinterpret_cast<bf16x8*>(o + off) = yv;
+            }
+        } else {
+            if (FULL || row < len)
+                *reinterpret_cast<uint4*>(o + off) = *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
+        }
+    }
+}
+
 // One chunk for one wave over all slices.  KDA: V~ = U - W S,
 // O = (Q . Gamma) S + A_qk V~, S <- Diag(gamma_C) S + Kbar^T V~.  DPLR:
 // X~ = Wb S, O = Q' S + Uo, S <- Diag(gamma_C) S + Abar^T X~ + Cs.
@@ -593,12 +629,19 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
     // chunk's products so that their latency hides under them
     bf16x8 gpre[4];
     if constexpr (GATE) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
+        auto gate_row = [&](int i) {
             const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-            gpre[i] = bf16x8{};
-            if (row < len)
-                gpre[i] = *reinterpret_cast<const bf16x8*>(og.gate + ((size_t)(tok0 + row) * H + h) * 128 + c8);
+            return *reinterpret_cast<const bf16x8*>(og.gate + ((size_t)(tok0 + row) * H + h) * 128 + c8);
+        };
+        if (len >= C) {            // a full chunk (uniform): no per-row test
+#pragma unroll
+            for (int i = 0; i < 4; i++) gpre[i] = gate_row(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                gpre[i] = bf16x8{};
+                if (i * 16 + (tid >> 4) < len) gpre[i] = gate_row(i);
+            }
         }
     }
     f32x4 accO[kOutNS];
@@ -653,34 +696,8 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
         for (int e = 0; e < 4; e++) sO[(16 * w + 4 * g4 + e) * kLdO + 16 * sl + n16] = (bf16)acc[e];
     }
     __syncthreads();
-    // 64 rows x 256 bytes of O, 16 bytes per lane
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-        const size_t off = ((size_t)(tok0 + row) * H + h) * 128 + c8;
-        if constexpr (GATE) {
-            const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + row * kLdO + c8);
-            float ov[8], ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                ov[e] = (float)ob[e];
-                ss = __builtin_fmaf(ov[e], ov[e], ss);
-            }
-#pragma unroll
-            for (int m = 8; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);   // the row's 16 lanes
-            const float r = 1.f / sqrtf(ss * (1.f / 128.f) + og.eps);
-            if (row < len) {
-                const bf16x8 gt = gpre[i];
-                bf16x8 yv;
-#pragma unroll
-                for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
-                *reinterpret_cast<bf16x8*>(o + off) = yv;
-            }
-        } else {
-            if (row < len)
-                *reinterpret_cast<uint4*>(o + off) = *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
-        }
-    }
+    if (len >= C) store_rows<GATE, true>(sO, gpre, o, tok0, len, H, h, tid, og);
+    else store_rows<GATE, false>(sO, gpre, o, tok0, len, H, h, tid, og);
 }
 
 // grid: seg_cap * H blocks, block = (segment, head).  With GATE the rows
