@@ -252,6 +252,7 @@ def bench_decode(args, kda, torch, KI):
     units = run["N"] * run["H"]
     gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
     fold = bench_fold(args, kda, torch, run, mean)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(run, 4)
     return {
         "workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v",
         "steps_timed": len(ms),
@@ -263,6 +264,7 @@ def bench_decode(args, kda, torch, KI):
         "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
                 "algorithmic bytes and may exceed the HBM rate",
         "traffic": _decode_traffic(mean),
+        "cpu_baseline": cpu,
         "fold": fold,
     }
 
@@ -501,16 +503,43 @@ def bench_family(args, kda, torch, KI, kda_stages):
     return out
 
 
+def _one_thread():
+    """BLAS pools held to one thread while the oracle is timed (its einsum
+    loops are single-threaded already), so `cores` is what it used."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
 def cpu_baseline(inp, torch):
     import oracle
     n = inp["q"].shape[1]
-    t0 = time.perf_counter()
-    oracle.recurrence(inp["q"][0], inp["k"][0], inp["v"][0], inp["z"][0], inp["b"][0], inp["A"],
-                      inp["h0"][0])
-    dt = time.perf_counter() - t0
+    with _one_thread():
+        t0 = time.perf_counter()
+        oracle.recurrence(inp["q"][0], inp["k"][0], inp["v"][0], inp["z"][0], inp["b"][0],
+                          inp["A"], inp["h0"][0])
+        dt = time.perf_counter() - t0
     return {"value": round(n / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens of long_1m, all 12 heads, fp64 numpy token "
                       f"recurrence, single thread, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(run, n_steps: int):
+    """The oracle's decode step timed on the decode workload: the first
+    n_steps of its 16 steps for all 256 x 12 states, one thread."""
+    import oracle
+    A = run["A"].cpu()
+    S = run["state"].cpu()
+    steps = [{k: run["steps"][i][k].cpu() for k in ("q", "k", "v", "z", "b")}
+             for i in range(n_steps)]
+    with _one_thread():
+        t0 = time.perf_counter()
+        for st in steps:
+            _, S = oracle.decode_step(st["q"], st["k"], st["v"], st["z"], st["b"], A, S)
+        dt = time.perf_counter() - t0
+    return {"value": round(run["N"] * n_steps / dt, 1), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {n_steps} of the 16 decode_256 steps, all {run['N']} x {run['H']} "
+                      f"states, fp64 numpy, single thread, {dt:.1f} s"}
 
 
 def main():
