@@ -252,7 +252,7 @@ def bench_decode(args, kda, torch, KI):
     units = run["N"] * run["H"]
     gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
     fold = bench_fold(args, kda, torch, run, mean)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(run, 4)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(run, len(run["steps"]))
     return {
         "workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v",
         "steps_timed": len(ms),
@@ -524,8 +524,8 @@ def cpu_baseline(inp, torch):
 
 
 def cpu_baseline_decode(run, n_steps: int):
-    """The oracle's decode step timed on the decode workload: the first
-    n_steps of its 16 steps for all 256 x 12 states, one thread."""
+    """The oracle's decode step timed on the decode workload: its first
+    n_steps steps for all 256 x 12 states, one thread."""
     import oracle
     A = run["A"].cpu()
     S = run["state"].cpu()
@@ -538,7 +538,7 @@ def cpu_baseline_decode(run, n_steps: int):
         dt = time.perf_counter() - t0
     return {"value": round(run["N"] * n_steps / dt, 1), "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"first {n_steps} of the 16 decode_256 steps, all {run['N']} x {run['H']} "
+            "sample": f"{n_steps} decode_256 steps, all {run['N']} x {run['H']} "
                       f"states, fp64 numpy, single thread, {dt:.1f} s"}
 
 
