@@ -14,7 +14,7 @@ namespace kda {
 // ws_layout below.
 struct WsLayout {
     int cap;                 // chunk capacity
-    int seg_chunks;          // chunks per segment of the MFMA chain (0 on the fp32 path)
+    int seg_chunks;          // smallest chunks per segment of the MFMA chain (0 on the fp32 path)
     int seg_cap;             // segment capacity
     size_t off_chunks, off_seqs, off_seqsegs, off_segs, off_recs, rec_bytes;
     size_t off_sstart, off_rm, total;
@@ -88,21 +88,26 @@ inline bool use_fast_path(int dk, int dv, int C, int dtype_bf16) {
     return dtype_bf16 && dk == 128 && dv == 128 && C == 64;
 }
 
-// Chunks per segment of the MFMA chain.  Both chain launches run one
-// workgroup per (segment, head) and one workgroup fills a CU, so a long
-// sequence is cut into about 256 / H segments: one full round of 256 CUs.
-// At least 16 chunks (1024 tokens) per segment.
+// Segments of the MFMA chain.  Both chain launches run one workgroup per
+// (segment, head) and one workgroup fills a CU, so the segments of all
+// sequences together should number about 256 / H: one full round of 256 CUs.
+inline int seg_target(int H) { return H >= 256 ? 1 : 256 / H; }
+
+// Smallest segment length (chunks) the device may pick: the target count on
+// the whole capacity, and at least 8 chunks (512 tokens), below which the
+// serial composition of segment starts costs more than the shorter chains
+// save.  The device picks the length from the actual sequence lengths
+// (prep_seq_kernel), never below this, so cap / min + N segments always fit.
 inline int pick_seg_chunks(int cap, int H) {
-    long long nseg = 256 / (long long)H;
-    if (nseg < 1) nseg = 1;
+    const long long nseg = seg_target(H);
     long long per = (cap + nseg - 1) / nseg;
-    if (per < 16) per = 16;
+    if (per < 8) per = 8;
     if (per > cap) per = cap > 0 ? cap : 1;
     return (int)per;
 }
 
 // Workspace layout (all offsets 256-byte aligned):
-// [0, 256)   header: int32 total chunks, int32 total segments
+// [0, 256)   header: int32 total chunks, int32 total segments, int32 chunks per segment
 // chunks     cap x int4 (sequence, first token, length, position in sequence)
 // seqs       N x int2 (first chunk id, number of chunks)
 // seqsegs    N x int2 (first segment id, number of segments)      [MFMA path]

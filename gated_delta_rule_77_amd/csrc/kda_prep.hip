@@ -21,31 +21,74 @@ __device__ __forceinline__ void seq_extent(const int* cu, int s, int Tfix, int T
     }
 }
 
-// Block-wide inclusive scan of one int per thread (1024 threads).
+// Block-wide inclusive scan of one int per thread (1024 threads): a scan
+// inside each wave, then the wave totals.  Every thread also finds the block
+// total in s_scan[1023] until the next call.
 __device__ __forceinline__ int block_scan_1024(int x, int* s_scan) {
-    const int t = threadIdx.x;
-    s_scan[t] = x;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int y = t >= off ? s_scan[t - off] : 0;
-        __syncthreads();
-        s_scan[t] += y;
-        __syncthreads();
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
     }
-    return s_scan[t];
+    if (lane == 63) s_scan[w] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int i = 0; i < 16; i++) {
+        const int v = s_scan[i];
+        if (i < w) before += v;
+        total += v;
+    }
+    __syncthreads();                            // every wave has read the totals
+    if (t == 1023) s_scan[1023] = total;
+    __syncthreads();
+    return before + x;
+}
+
+// Block-wide sum (or maximum) of one int per thread (1024 threads), returned
+// to every thread; s_red holds 16 ints.
+template <bool MAX>
+__device__ __forceinline__ int block_reduce_1024(int x, int* s_red) {
+    for (int m = 32; m > 0; m >>= 1) {
+        const int y = __shfl_xor(x, m, 64);
+        x = MAX ? max(x, y) : x + y;
+    }
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    int r = s_red[0];
+    for (int i = 1; i < 16; i++) r = MAX ? max(r, s_red[i]) : r + s_red[i];
+    __syncthreads();                            // s_red may be written again
+    return r;
+}
+
+// Sum over the N sequences of ceil(chunks / per): the segments that `per`
+// chunks per segment give (seqs[].y are the clamped chunk counts).
+__device__ long long count_segments(const int2* __restrict__ seqs, int N, int per, int* s_red) {
+    long long total = 0;
+    for (int base = 0; base < N; base += 1024) {
+        const int s = base + threadIdx.x;
+        const int nc = s < N ? seqs[s].y : 0;
+        total += block_reduce_1024<false>((nc + per - 1) / per, s_red);
+    }
+    return total;
 }
 
 // One workgroup: per-sequence chunk counts and their exclusive prefix sum
-// (clamped to the capacity), the total; with seg_chunks > 0 also the
-// per-sequence segment counts (seg_chunks chunks per segment) and their prefix.
+// (clamped to the capacity), the total; with min_seg > 0 also the segments of
+// the MFMA chain.  Both chain launches run one workgroup per (segment, head),
+// so the segment length `per` is the smallest value >= min_seg whose segments
+// (each sequence cut into ceil(chunks / per)) number at most seg_target (or
+// one per non-empty sequence when there are more of those): one round of
+// workgroups whose longest chain is as short as that round allows.  Any such
+// per gives at most cap / min_seg + N segments, the capacity the host sized.
+// hdr: [0] chunks, [1] segments, [2] per.
 __global__ __launch_bounds__(1024)
 void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
-                     int seg_chunks, int seg_cap, int* __restrict__ hdr,
+                     int min_seg, int seg_target, int seg_cap, int* __restrict__ hdr,
                      int2* __restrict__ seqs, int2* __restrict__ seqsegs)
 {
     __shared__ int s_scan[1024];
     const int t = threadIdx.x;
-    long long carry = 0, carry_seg = 0;
+    long long carry = 0;
     for (int base = 0; base < N; base += 1024) {
         const int s = base + t;
         int start = 0, len = 0;
@@ -53,16 +96,43 @@ void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int 
         const int nch = (len + C - 1) / C;
         const int incl = block_scan_1024(nch, s_scan);
         const int tile_total = s_scan[1023];
-        int nc = 0;
         if (s < N) {
             const long long first = carry + incl - nch;
             const int f = (int)min(first, (long long)cap);
-            nc = (int)max(0LL, min((long long)nch, (long long)cap - f));
+            const int nc = (int)max(0LL, min((long long)nch, (long long)cap - f));
             seqs[s] = make_int2(f, nc);
         }
         __syncthreads();
-        if (seg_chunks > 0) {
-            const int nseg = (nc + seg_chunks - 1) / seg_chunks;
+        carry += tile_total;
+    }
+    int per = 0;
+    long long carry_seg = 0;
+    if (min_seg > 0) {
+        __syncthreads();                        // seqs[] complete for the whole workgroup
+        int max_nc = 0;
+        for (int base = 0; base < N; base += 1024) {
+            const int s = base + t;
+            max_nc = max(max_nc, block_reduce_1024<true>(s < N ? seqs[s].y : 0, s_scan));
+        }
+        const long long total = min(carry, (long long)cap);
+        const long long nonempty = count_segments(seqs, N, max(max_nc, 1), s_scan);
+        const long long target = max((long long)seg_target, nonempty);
+        // count_segments(per) is non-increasing in per, at least total / per and
+        // at most total / per + nonempty: the answer lies in [lo, hi]
+        long long lo = max((long long)min_seg, (total + target - 1) / target);
+        long long hi = target > nonempty ? (total + (target - nonempty) - 1) / (target - nonempty)
+                                         : (long long)max_nc;
+        hi = max(hi, lo);
+        if (count_segments(seqs, N, (int)lo, s_scan) <= target) hi = lo;   // one sequence: always
+        while (lo < hi) {
+            const long long mid = lo + (hi - lo) / 2;
+            if (count_segments(seqs, N, (int)mid, s_scan) <= target) hi = mid; else lo = mid + 1;
+        }
+        per = (int)lo;
+        for (int base = 0; base < N; base += 1024) {
+            const int s = base + t;
+            const int nc = s < N ? seqs[s].y : 0;
+            const int nseg = (nc + per - 1) / per;
             const int sincl = block_scan_1024(nseg, s_scan);
             if (s < N) {
                 const long long first = carry_seg + sincl - nseg;
@@ -73,23 +143,24 @@ void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int 
             carry_seg += s_scan[1023];
             __syncthreads();
         }
-        carry += tile_total;
     }
     if (t == 0) {
         hdr[0] = (int)min(carry, (long long)cap);
         hdr[1] = (int)min(carry_seg, (long long)seg_cap);
+        hdr[2] = per;
     }
 }
 
 // One thread per segment slot: owning sequence (binary search over the
 // first-segment ids) and (sequence, first chunk, chunks, index in sequence).
 __global__ __launch_bounds__(256)
-void prep_seg_kernel(int N, int seg_chunks, int seg_cap, const int* __restrict__ hdr,
+void prep_seg_kernel(int N, int seg_cap, const int* __restrict__ hdr,
                      const int2* __restrict__ seqs, const int2* __restrict__ seqsegs,
                      int4* __restrict__ segs)
 {
     const int g = blockIdx.x * 256 + threadIdx.x;
     if (g >= seg_cap) return;
+    const int seg_chunks = hdr[2];
     if (g >= hdr[1]) { segs[g] = make_int4(-1, 0, 0, 0); return; }
     int lo = 0, hi = N - 1;
     while (lo < hi) {
@@ -135,8 +206,8 @@ hipError_t launch_prep(const ChunkArgs& a) {
     int4* segs = reinterpret_cast<int4*>(a.ws + a.L.off_segs);
     const int Ttot = a.cu ? a.T : a.B * a.T;
     hipLaunchKernelGGL(prep_seq_kernel, dim3(1), dim3(1024), 0, a.stream,
-                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, a.L.seg_cap, hdr, seqs,
-                       seqsegs);
+                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, seg_target(a.H),
+                       a.L.seg_cap, hdr, seqs, seqsegs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned nb = (unsigned)((a.L.cap + 255) / 256);
@@ -145,8 +216,8 @@ hipError_t launch_prep(const ChunkArgs& a) {
     e = hipGetLastError();
     if (e != hipSuccess || a.L.seg_chunks == 0) return e;
     const unsigned ns = (unsigned)((a.L.seg_cap + 255) / 256);
-    hipLaunchKernelGGL(prep_seg_kernel, dim3(ns), dim3(256), 0, a.stream, a.N, a.L.seg_chunks,
-                       a.L.seg_cap, (const int*)hdr, (const int2*)seqs, (const int2*)seqsegs, segs);
+    hipLaunchKernelGGL(prep_seg_kernel, dim3(ns), dim3(256), 0, a.stream, a.N, a.L.seg_cap,
+                       (const int*)hdr, (const int2*)seqs, (const int2*)seqsegs, segs);
     return hipGetLastError();
 }
 

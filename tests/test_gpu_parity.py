@@ -575,10 +575,10 @@ def test_verify_reads_state_only(kda):
 @pytest.mark.parametrize("B,T,H,heads", [(1, 8192, 1, [0]), (3, 1500, 5, [0, 4]),
                                          (1, 4096, 40, [7, 39])])
 def test_segment_layouts_vs_oracle(kda, B, T, H, heads):
-    """The MFMA path cuts every sequence into about 256 / H segments of at
-    least 16 chunks: one head with many segments, several sequences with two
-    segments each, and many heads with few.  Sampled heads of every sequence
-    against the oracle."""
+    """The MFMA path cuts the sequences into about 256 / H segments in all, of
+    at least 8 chunks: one head with many segments, several sequences with
+    three segments each, and many heads with few.  Sampled heads of every
+    sequence against the oracle."""
     case = KI.PrefillCase("seg", H=H, dk=128, dv=128, chunk=64, dtype="bf16", B=B, T=T,
                           zero_h0=False)
     d = KI.make_prefill(case, seed=17)
@@ -591,4 +591,28 @@ def test_segment_layouts_vs_oracle(kda, B, T, H, heads):
         e_o = rel_err(o[bi][:, heads], ro)
         e_s = rel_err(hT[bi][heads], rS)
         _report(f"segments B={B} T={T} H={H} seq {bi}", o=e_o, hT=e_s)
+        assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_packed_segment_lengths_vs_oracle(kda):
+    """Sequences of 11, 21, 32 and 6 chunks (and an empty and a one-chunk one)
+    at H = 32: the smallest segment length the capacity allows (10 chunks)
+    would give 11 segments per head where one round holds 8, so the device
+    lengthens the segments (11 chunks: 8 segments).  Sampled heads of every
+    sequence against the oracle."""
+    lens = [700, 1300, 2000, 333, 0, 64]
+    heads = [0, 31]
+    case = KI.PrefillCase("segpack", H=32, dk=128, dv=128, chunk=64, dtype="bf16", zero_h0=False)
+    d = KI.make_prefill(case, seed=19, lengths=lens)
+    o, hT = gpu_prefill(kda, to_dev(d))
+    torch.cuda.synchronize()
+    cu = [int(x) for x in d["cu_seqlens"].tolist()]
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s].cpu(), d["h0"][s])
+            continue
+        ro, rS = oracle_prefill(d, heads=heads, seq=s)
+        e_o = rel_err(o[0, cu[s]:cu[s + 1]][:, heads], ro)
+        e_s = rel_err(hT[s][heads], rS)
+        _report(f"packed segments seq {s} (len {n})", o=e_o, hT=e_s)
         assert e_o <= TOL_BF16 and e_s <= TOL_BF16
