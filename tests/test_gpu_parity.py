@@ -195,6 +195,49 @@ def test_slow_decay_long_memory(kda):
     assert eo <= TOL_BF16 and eS <= TOL_BF16
 
 
+@pytest.mark.parametrize("dtype,dk,chunk", [("bf16", 128, 64), ("fp32", 16, 16)])
+def test_extreme_gates(kda, dtype, dk, chunk):
+    """Saturated gates: on every other channel alpha = e^-5 (the lower bound,
+    g = -5 exactly) and on the rest alpha = 1, so decay exponents inside a
+    chunk span the whole range the 16-token sub-tiles are built for (a
+    reciprocal of up to e^80 on the diagonal tiles) next to channels that
+    never decay; a sequence with a ragged tail, from an initial state."""
+    case = KI.PrefillCase("extreme", H=2, dk=dk, dv=dk, chunk=chunk, dtype=dtype, B=1, T=300,
+                          zero_h0=False)
+    inp = KI.make_prefill(case, seed=21)
+    sign = torch.tensor([1.0 if c % 2 == 0 else -1.0 for c in range(dk)])
+    inp["z"] = (BIG * sign).expand_as(inp["z"]).contiguous()
+    inp["A"] = torch.zeros_like(inp["A"])
+    d = to_dev(inp)
+    o, hT = gpu_prefill(kda, d)
+    torch.cuda.synchronize()
+    ro, rS = oracle_prefill(inp)
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    eo, eS = rel_err(o[0], ro), rel_err(hT[0], rS)
+    _report(f"extreme gates {dtype}", o=eo, hT=eS)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+    assert eo <= tol and eS <= tol
+
+
+def test_extreme_gates_decode(kda):
+    """The decode step with the saturated gates above: alpha = e^-5 and 1 on
+    alternate channels, five steps against the oracle's step."""
+    case = KI.DecodeCase("extremedec", N=4, H=2, dk=128, dv=128, steps=5, dtype="bf16")
+    run = KI.make_decode(case, seed=22)
+    sign = torch.tensor([1.0 if c % 2 == 0 else -1.0 for c in range(128)])
+    A = torch.zeros_like(run["A"])
+    st = run["state"].cuda().contiguous()
+    S = run["state"]
+    for s in run["steps"]:
+        z = (BIG * sign).expand_as(s["z"]).contiguous()
+        o = kda.kda_recurrent_step(s["q"].cuda(), s["k"].cuda(), s["v"].cuda(), z.cuda(),
+                                   s["b"].cuda(), A.cuda(), st)
+        ro, S = oracle.decode_step(s["q"], s["k"], s["v"], z, s["b"], A, S)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and rel_err(o, ro) <= TOL_BF16
+    assert rel_err(st, S) <= TOL_BF16
+
+
 def test_stage_intermediates_match_chunked_oracle(kda):
     """Per-chunk G, A_kk, A_qk, T and the state entering each chunk match the
     oracle's chunked form (MFMA path, 3 chunks + tail, with h0)."""
