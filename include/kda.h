@@ -31,6 +31,9 @@
  *     allocates, frees or keeps them.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; nothing synchronises the host.
+ *     No entry point allocates memory, synchronises or clears memory with a
+ *     memset: each call is a fixed sequence of kernel launches, so it may be
+ *     captured into a HIP graph and replayed (with the same pointers).
  *   - Arguments are validated on the host before anything is enqueued; a
  *     non-OK status means nothing was enqueued, except KDA_ERR_HIP, which
  *     reports a failed launch.  No exception crosses the ABI.
