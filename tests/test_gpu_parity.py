@@ -659,3 +659,46 @@ def test_packed_segment_lengths_vs_oracle(kda):
         e_s = rel_err(hT[s][heads], rS)
         _report(f"packed segments seq {s} (len {n})", o=e_o, hT=e_s)
         assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+@pytest.mark.parametrize("case_id", range(12))
+def test_random_packed_layouts(kda, case_id):
+    """Seeded random packed batches: 1-9 sequences whose lengths mix empty,
+    one-token, short and multi-chunk ones, 1-40 heads, on the MFMA path and
+    on the fp32 path; the first and last head of every sequence against the
+    oracle (per-tensor metric), empty sequences return h0 exactly."""
+    import random
+    rng = random.Random(7000 + case_id)
+    mfma = case_id % 3 != 2
+    if mfma:
+        dk, chunk, dtype = 128, 64, "bf16"
+    else:
+        dk, chunk, dtype = rng.choice([16, 32, 64]), rng.choice([16, 64]), rng.choice(["fp32", "bf16"])
+    H = rng.choice([1, 2, 3, 5, 12, 16, 33, 40])
+    lens = [rng.choice([0, 1, rng.randint(1, 200), rng.randint(1, 2500)])
+            for _ in range(rng.randint(1, 9))]
+    budget = 8000 if dk == 128 else 3000
+    if sum(lens) > budget:
+        lens = [n * budget // sum(lens) for n in lens]
+    if sum(lens) == 0:
+        lens[-1] = 1
+    case = KI.PrefillCase("randlayout", H=H, dk=dk, dv=dk, chunk=chunk, dtype=dtype,
+                          zero_h0=False)
+    d = KI.make_prefill(case, seed=7100 + case_id, lengths=lens)
+    o, hT = gpu_prefill(kda, to_dev(d))
+    torch.cuda.synchronize()
+    heads = sorted({0, H - 1})
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    cu = [int(x) for x in d["cu_seqlens"].tolist()]
+    refs = {s: oracle_prefill(d, heads=heads, seq=s) for s, n in enumerate(lens) if n}
+    o_scale = max(float(abs(r[0]).max()) for r in refs.values())
+    s_scale = max(float(abs(r[1]).max()) for r in refs.values())
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s].cpu(), d["h0"][s])
+            continue
+        ro, rS = refs[s]
+        e_o = rel_err(o[0, cu[s]:cu[s + 1]][:, heads], ro, scale=o_scale)
+        e_s = rel_err(hT[s][heads], rS, scale=s_scale)
+        assert e_o <= tol and e_s <= tol, (case_id, dk, chunk, dtype, H, lens, s, e_o, e_s)
+    _report(f"random layout {case_id}: d={dk} C={chunk} {dtype} H={H} lens={lens}", ok=0.0)
