@@ -211,3 +211,25 @@ def test_layer_step_matches_layer_prefill(kda):
             assert y_within_bar(y_gpu, ry, ro, data["gate"][n], data["norm_w"], TOL_BF16) <= 1.0
         assert rel_err(st[n], rS) <= TOL_BF16 and rel_err(h_p[n], rS) <= TOL_BF16
     assert torch.equal(cs, c_p)
+
+
+@pytest.mark.parametrize("case_id", range(6))
+def test_layer_fwd_random_packed_layouts(kda, case_id):
+    """Seeded random packed batches through the layer: sequence lengths that
+    mix empty, shorter than the convolution, one chunk and several, with and
+    without incoming states, on the MFMA path (d = 128) and the fp32 path."""
+    import random
+    rng = random.Random(8000 + case_id)
+    d, chunk, dtype = ((128, 64, "bf16") if case_id % 2 == 0
+                       else (rng.choice([16, 32]), 16, rng.choice(["fp32", "bf16"])))
+    H = rng.choice([1, 2, 3])
+    lens = [rng.choice([0, 1, 2, 3, rng.randint(4, 100), rng.randint(100, 700)])
+            for _ in range(rng.randint(1, 6))]
+    if sum(lens) == 0:
+        lens[0] = 5
+    states = case_id % 3 != 1
+    case = KI.PrefillCase("layerrand", H=H, dk=d, dv=d, chunk=chunk, dtype=dtype,
+                          zero_h0=not states)
+    data = KI.make_layer(case, lengths=lens, seed=8100 + case_id, conv_state=states)
+    _check_layer(kda, data, TOL_BF16 if dtype == "bf16" else TOL_F32,
+                 f"random {case_id} d={d} {dtype} H={H} lens={lens}")
