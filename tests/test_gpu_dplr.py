@@ -171,3 +171,43 @@ def test_dplr_segment_layouts_vs_oracle(kda, B, T, H, heads):
         eo, eS = rel_err(o[bi][:, heads], ro), rel_err(hT[bi][heads], rS)
         _report(f"segments B={B} T={T} H={H} seq {bi} heads {heads}", o=eo, hT=eS)
         assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+@pytest.mark.parametrize("case_id", range(6))
+def test_dplr_random_packed_layouts(kda, case_id):
+    """Seeded random packed batches of the general update: length mixes with
+    empty, one-token and multi-chunk sequences, several head counts, on the
+    MFMA path and the fp32 path; the first and last head of every sequence
+    against the oracle (per-tensor metric)."""
+    import random
+    rng = random.Random(9000 + case_id)
+    dk, chunk, dtype = ((128, 64, "bf16") if case_id % 3 != 2
+                        else (rng.choice([16, 32]), rng.choice([16, 64]), rng.choice(["fp32", "bf16"])))
+    H = rng.choice([1, 2, 5, 12, 33])
+    lens = [rng.choice([0, 1, rng.randint(1, 200), rng.randint(1, 2000)])
+            for _ in range(rng.randint(1, 6))]
+    budget = 5000 if dk == 128 else 2000
+    if sum(lens) > budget:
+        lens = [n * budget // sum(lens) for n in lens]
+    if sum(lens) == 0:
+        lens[-1] = 1
+    case = KI.PrefillCase("dplrrand", H=H, dk=dk, dv=dk, chunk=chunk, dtype=dtype, zero_h0=False)
+    d = KI.make_dplr(case, seed=9100 + case_id, lengths=lens)
+    o, hT = _gpu(kda, _dev(d), chunk)
+    torch.cuda.synchronize()
+    heads = sorted({0, H - 1})
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    cu = [int(x) for x in d["cu_seqlens"].tolist()]
+    refs = {s: _oracle(d, 0, slice(cu[s], cu[s + 1]), d["h0"][s], heads=heads)
+            for s, n in enumerate(lens) if n}
+    o_scale = max(float(abs(r[0]).max()) for r in refs.values())
+    s_scale = max(float(abs(r[1]).max()) for r in refs.values())
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s].cpu(), d["h0"][s])
+            continue
+        ro, rS = refs[s]
+        eo = rel_err(o[0, cu[s]:cu[s + 1]][:, heads], ro, scale=o_scale)
+        eS = rel_err(hT[s][heads], rS, scale=s_scale)
+        assert eo <= tol and eS <= tol, (case_id, dk, chunk, dtype, H, lens, s, eo, eS)
+    _report(f"random layout {case_id}: d={dk} C={chunk} {dtype} H={H} lens={lens}", ok=0.0)
