@@ -72,7 +72,7 @@ constexpr int kOffRQ = kOffRK + 64 * kLdK * 2;
 constexpr int kOffFac = kOffRQ + 64 * kLdK * 2;
 constexpr int kOffBeta = kOffFac + kNFac * 128 * 4;
 constexpr int kSmemIntra = kOffBeta + 64 * 4;            // 80128 bytes: two workgroups per CU
-static_assert(3 * 64 * kLdA * 4 + 4 * 256 * 4 <= kOffFac, "A_kk, A_qk, N and P alias L/K.F and the row operands");
+static_assert(3 * 64 * kLdA * 4 + kInvScr * 4 <= kOffFac, "A_kk, A_qk, N and P alias L/K.F and the row operands");
 
 // One workgroup per (chunk, head), 4 waves.  Work on single elements is split
 // by channel: wave w owns channels [32w, 32w + 32) of all 64 tokens, lane
@@ -387,7 +387,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     float* sAkk = reinterpret_cast<float*>(smem);                     // [64][kLdA]
     float* sAqk = sAkk + 64 * kLdA;
     float* sN = sAqk + 64 * kLdA;
-    float* sP = sN + 64 * kLdA;                                       // [4][16][16]
+    float* sP = sN + 64 * kLdA;                                       // inverse scratch
     // causal masks and the beta row scale of A_kk; tiles above the diagonal are zero
 #pragma unroll
     for (int sl = 0; sl < 3; sl++) {

@@ -52,8 +52,8 @@ constexpr int kDB0 = 0;              // -A_ba, then R = A_qa T
 constexpr int kDB1 = kMat;           // A_bk, then P = R A_bk + A_qk
 constexpr int kDB2 = 2 * kMat;       // A_qa, then M = T A_bk
 constexpr int kDT = 3 * kMat;        // T
-constexpr int kDScr = 4 * kMat;      // 4 x 256 floats of inverse scratch
-static_assert(kDScr + 4096 <= kDSmem, "the matrices fit in the step 1-3 buffers");
+constexpr int kDScr = 4 * kMat;      // inverse scratch (kInvScr floats)
+static_assert(kDScr + kInvScr * 4 <= kDSmem, "the matrices fit in the step 1-3 buffers");
 // LDS at the end: Ub and V as token-contracting B fragments of all 8 slices
 constexpr int kDStU = 0;             // [8 slice][2 kstep][64 lane][8] bf16
 constexpr int kDStV = 16384;

@@ -7,12 +7,17 @@
 namespace kda {
 namespace fastc {
 
-// acc += A (16x16, row-major, lda) * B (16x16, row-major, ldb), fp32 MFMA
+// acc += A (16x16, row-major, lda) * B (16x16, row-major, ldb), fp32 MFMA.
+// Step ks gives lane group g the index k = 4g + ks: a lane reads its four A
+// values as one 16-byte piece of row n and its B values down column n, rows
+// 4g..4g+3.  With a B row stride of 4 (mod 16) words (68 and 20 here) the B
+// reads of one step fall on 64 distinct banks (bank = 16g + n + const).
 __device__ __forceinline__ f32x4 mm16_f32(f32x4 acc, const float* A, int lda, const float* B,
                                           int ldb, int n16, int g4) {
+    const float4 a = *reinterpret_cast<const float4*>(A + n16 * lda + 4 * g4);
+    const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-        acc = mfma_f32(A[n16 * lda + 4 * ks + g4], B[(4 * ks + g4) * ldb + n16], acc);
+    for (int ks = 0; ks < 4; ks++) acc = mfma_f32(av[ks], B[(4 * g4 + ks) * ldb + n16], acc);
     return acc;
 }
 
@@ -29,6 +34,8 @@ __device__ __forceinline__ void load8f(const float* p, float* out) {
 constexpr int kLdG = 132;   // fp32 [64][kLdG]: L, then K.F in place
 constexpr int kLdK = 136;   // bf16 row operands [64][kLdK]
 constexpr int kLdA = 68;    // fp32 64x64 matrices [64][kLdA]
+constexpr int kLdP = 20;    // the inverse's 16x16 fp32 partial products [16][kLdP]
+constexpr int kInvScr = 4 * 16 * kLdP;   // floats of inverse scratch: a [16][kLdP] tile per wave
 // per-channel factor rows (fp32 [128] each); L_s(r) = L at row 16r - 1
 // (0 for r = 0), L_e(r) = L at row 16r + 15, L_C = L at row 63:
 constexpr int kFX = 0;      // X(r,s) = 2^(L_s(r) - L_e(s)), row r(r+1)/2 + s, s <= r
@@ -50,7 +57,7 @@ __device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : p < 3 ? 1 : 
 // N = (I + A)^{-1} for a strictly lower-triangular 64 x 64 fp32 A in LDS
 // ([64][kLdA] rows), in fp32 by 16 x 16 blocks ([LA-KDA §8]: serial inside a
 // 16-token tile, matrix products between tiles).  N must hold zeros on entry
-// (its upper blocks stay zero); sP is 4 x 256 floats of scratch.  Every
+// (its upper blocks stay zero); sP is kInvScr floats of scratch.  Every
 // thread of the 256-thread workgroup calls it (it holds barriers).
 __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sN, float* sP, int w,
                                                    int n16, int g4) {
@@ -80,11 +87,11 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sN, f
                 P = mm16_f32(P, sA + 16 * r * kLdA + 16 * m, kLdA, sN + 16 * m * kLdA + 16 * s, kLdA,
                              n16, g4);
 #pragma unroll
-            for (int e = 0; e < 4; e++) sP[w * 256 + (4 * g4 + e) * 16 + n16] = P[e];
+            for (int e = 0; e < 4; e++) sP[w * 16 * kLdP + (4 * g4 + e) * kLdP + n16] = P[e];
         }
         __syncthreads();
         if (act) {
-            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * kLdA + 16 * r, kLdA, sP + w * 256, 16, n16, g4);
+            const f32x4 R = mm16_f32(zero4(), sN + 16 * r * kLdA + 16 * r, kLdA, sP + w * 16 * kLdP, kLdP, n16, g4);
 #pragma unroll
             for (int e = 0; e < 4; e++) sN[(16 * r + 4 * g4 + e) * kLdA + 16 * s + n16] = -R[e];
         }
