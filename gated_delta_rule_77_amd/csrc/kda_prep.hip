@@ -72,9 +72,45 @@ __device__ long long count_segments(const int2* __restrict__ seqs, int N, int pe
     return total;
 }
 
-// One workgroup: per-sequence chunk counts and their exclusive prefix sum
-// (clamped to the capacity), the total; with min_seg > 0 also the segments of
-// the MFMA chain.  Both chain launches run one workgroup per (segment, head),
+// Segment slot g: owning sequence (binary search over the first-segment ids)
+// and (sequence, first chunk, chunks, index in sequence); -1 past the total.
+__device__ __forceinline__ void fill_seg(int g, int N, int nseg_total, int per,
+                                         const int2* __restrict__ seqs,
+                                         const int2* __restrict__ seqsegs, int4* __restrict__ segs) {
+    if (g >= nseg_total) { segs[g] = make_int4(-1, 0, 0, 0); return; }
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seqsegs[mid].x <= g) lo = mid; else hi = mid - 1;
+    }
+    const int j = g - seqsegs[lo].x;
+    const int2 sq = seqs[lo];
+    segs[g] = make_int4(lo, sq.x + j * per, min(per, sq.y - j * per), j);
+}
+
+// Chunk slot c: the owning sequence by binary search over the first-chunk
+// ids (empty sequences share the next one's id, so the largest s with
+// seqs[s].x <= c is the non-empty owner) and (sequence, first token, length,
+// position of the first token within the sequence); -1 past the total.
+__device__ __forceinline__ void fill_chunk(int c, const int* __restrict__ cu, int N, int Tfix,
+                                           int Ttot, int C, int total,
+                                           const int2* __restrict__ seqs, int4* __restrict__ chunks) {
+    if (c >= total) { chunks[c] = make_int4(-1, 0, 0, 0); return; }
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seqs[mid].x <= c) lo = mid; else hi = mid - 1;
+    }
+    int start, len;
+    seq_extent(cu, lo, Tfix, Ttot, start, len);
+    const int j = c - seqs[lo].x;
+    chunks[c] = make_int4(lo, start + j * C, min(C, len - j * C), j * C);
+}
+
+// The chunk bookkeeping in one workgroup (one launch): per-sequence chunk
+// counts and their exclusive prefix sum (clamped to the capacity), the
+// total, the chunk table; with min_seg > 0 also the segments of the MFMA
+// chain and the segment table.  Both chain launches run one workgroup per (segment, head),
 // so the segment length `per` is the smallest value >= min_seg whose segments
 // (each sequence cut into ceil(chunks / per)) number at most seg_target (or
 // one per non-empty sequence when there are more of those): one round of
@@ -82,9 +118,10 @@ __device__ long long count_segments(const int2* __restrict__ seqs, int N, int pe
 // per gives at most cap / min_seg + N segments, the capacity the host sized.
 // hdr: [0] chunks, [1] segments, [2] per.
 __global__ __launch_bounds__(1024)
-void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
-                     int min_seg, int seg_target, int seg_cap, int* __restrict__ hdr,
-                     int2* __restrict__ seqs, int2* __restrict__ seqsegs)
+void prep_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
+                 int min_seg, int seg_target, int seg_cap, int* __restrict__ hdr,
+                 int2* __restrict__ seqs, int2* __restrict__ seqsegs, int4* __restrict__ chunks,
+                 int4* __restrict__ segs)
 {
     __shared__ int s_scan[1024];
     const int t = threadIdx.x;
@@ -144,58 +181,17 @@ void prep_seq_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int 
             __syncthreads();
         }
     }
+    const int total = (int)min(carry, (long long)cap);
+    const int nseg_total = (int)min(carry_seg, (long long)seg_cap);
     if (t == 0) {
-        hdr[0] = (int)min(carry, (long long)cap);
-        hdr[1] = (int)min(carry_seg, (long long)seg_cap);
+        hdr[0] = total;
+        hdr[1] = nseg_total;
         hdr[2] = per;
     }
-}
-
-// One thread per segment slot: owning sequence (binary search over the
-// first-segment ids) and (sequence, first chunk, chunks, index in sequence).
-__global__ __launch_bounds__(256)
-void prep_seg_kernel(int N, int seg_cap, const int* __restrict__ hdr,
-                     const int2* __restrict__ seqs, const int2* __restrict__ seqsegs,
-                     int4* __restrict__ segs)
-{
-    const int g = blockIdx.x * 256 + threadIdx.x;
-    if (g >= seg_cap) return;
-    const int seg_chunks = hdr[2];
-    if (g >= hdr[1]) { segs[g] = make_int4(-1, 0, 0, 0); return; }
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seqsegs[mid].x <= g) lo = mid; else hi = mid - 1;
-    }
-    const int j = g - seqsegs[lo].x;
-    const int2 sq = seqs[lo];
-    const int first = sq.x + j * seg_chunks;
-    segs[g] = make_int4(lo, first, min(seg_chunks, sq.y - j * seg_chunks), j);
-}
-
-// One thread per chunk slot: locate the owning sequence by binary search
-// over the first-chunk ids and record (sequence, first token, length,
-// position of the first token within the sequence).
-__global__ __launch_bounds__(256)
-void prep_chunk_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
-                       const int* __restrict__ hdr, const int2* __restrict__ seqs,
-                       int4* __restrict__ chunks)
-{
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= cap) return;
-    const int total = hdr[0];
-    if (c >= total) { chunks[c] = make_int4(-1, 0, 0, 0); return; }
-    // largest s with seqs[s].x <= c; empty sequences share the next one's id,
-    // so the largest such s is the non-empty owner
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seqs[mid].x <= c) lo = mid; else hi = mid - 1;
-    }
-    int start, len;
-    seq_extent(cu, lo, Tfix, Ttot, start, len);
-    const int j = c - seqs[lo].x;
-    chunks[c] = make_int4(lo, start + j * C, min(C, len - j * C), j * C);
+    __syncthreads();                            // seqs[] and seqsegs[] complete
+    for (int c = t; c < cap; c += 1024) fill_chunk(c, cu, N, Tfix, Ttot, C, total, seqs, chunks);
+    if (min_seg > 0)
+        for (int g = t; g < seg_cap; g += 1024) fill_seg(g, N, nseg_total, per, seqs, seqsegs, segs);
 }
 
 hipError_t launch_prep(const ChunkArgs& a) {
@@ -205,19 +201,9 @@ hipError_t launch_prep(const ChunkArgs& a) {
     int2* seqsegs = reinterpret_cast<int2*>(a.ws + a.L.off_seqsegs);
     int4* segs = reinterpret_cast<int4*>(a.ws + a.L.off_segs);
     const int Ttot = a.cu ? a.T : a.B * a.T;
-    hipLaunchKernelGGL(prep_seq_kernel, dim3(1), dim3(1024), 0, a.stream,
+    hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, a.stream,
                        a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, seg_target(a.H),
-                       a.L.seg_cap, hdr, seqs, seqsegs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned nb = (unsigned)((a.L.cap + 255) / 256);
-    hipLaunchKernelGGL(prep_chunk_kernel, dim3(nb), dim3(256), 0, a.stream,
-                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, (const int*)hdr, (const int2*)seqs, chunks);
-    e = hipGetLastError();
-    if (e != hipSuccess || a.L.seg_chunks == 0) return e;
-    const unsigned ns = (unsigned)((a.L.seg_cap + 255) / 256);
-    hipLaunchKernelGGL(prep_seg_kernel, dim3(ns), dim3(256), 0, a.stream, a.N, a.L.seg_cap,
-                       (const int*)hdr, (const int2*)seqs, (const int2*)seqsegs, segs);
+                       a.L.seg_cap, hdr, seqs, seqsegs, chunks, segs);
     return hipGetLastError();
 }
 
