@@ -99,7 +99,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const float* __restrict__ z,
                        const float* __restrict__ bl, const float* __restrict__ A,
                        const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
-                       int cap, uint8_t* __restrict__ recs, float* __restrict__ dbg,
+                       uint8_t* __restrict__ recs, float* __restrict__ dbg,
                        const float* __restrict__ conv_w, const bf16* __restrict__ cs0,
                        float l2_eps)
 {
@@ -797,7 +797,6 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 // operand fragment).  Only the chunk's W, Kbar, U and gamma_C are shared: the
 // workgroup copies them into a double-buffered LDS stage, two chunks ahead
 // through registers, with one barrier per chunk.
-constexpr int kTS = 16;                          // slices of [R | M]
 // stage of one chunk: W, Kbar, U (KDA) or Cs (DPLR) and gamma_C
 template <bool DPLR> struct TransStage {
     static constexpr int W = 0, K = 16384, U = 32768, C = 32768;
@@ -1117,7 +1116,7 @@ hipError_t launch_fast(const ChunkArgs& a) {
 #define KDA_INTRA(DBG, CONV, MODE, DBGP)                                                      \
     hipLaunchKernelGGL((fast_intra_kernel<DBG, CONV, MODE>), gi, dim3(256), 0, a.stream,         \
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A, hdr, \
-                       chunks, a.H, a.L.cap, recs, DBGP, a.conv_w, cs0, a.l2_eps)
+                       chunks, a.H, recs, DBGP, a.conv_w, cs0, a.l2_eps)
     // the debug and layer variants exist for KDA only (the API enforces it)
     if (a.dbg_intra) KDA_INTRA(true, false, kModeKDA, a.dbg_intra);
     else if (a.conv_w) KDA_INTRA(false, true, kModeKDA, (float*)nullptr);

@@ -122,7 +122,7 @@ template <typename T>
 __global__ __launch_bounds__(256)
 void layer_convstate_kernel(const T* __restrict__ q_in, const T* __restrict__ k_in,
                             const T* __restrict__ v_in, const T* cs0, const int* __restrict__ cu,
-                            int N, int Tfix, int Ttot, int H, int d, T* cs_out)
+                            int Tfix, int Ttot, int H, int d, T* cs_out)
 {
     const int n = blockIdx.x / H, h = blockIdx.x % H;
     int start, len;
@@ -297,7 +297,7 @@ hipError_t launch_layer_convstate(const void* q_in, const void* k_in, const void
     const dim3 grid((unsigned)((long long)N * H));
 #define KDA_CS(T)                                                                           \
     hipLaunchKernelGGL(layer_convstate_kernel<T>, grid, dim3(256), 0, s, (const T*)q_in,   \
-                       (const T*)k_in, (const T*)v_in, (const T*)cs0, cu, N, Tfix, Ttot, H,  \
+                       (const T*)k_in, (const T*)v_in, (const T*)cs0, cu, Tfix, Ttot, H,     \
                        d, (T*)cs_out)
     if (dtype_bf16) KDA_CS(bf16); else KDA_CS(float);
 #undef KDA_CS
