@@ -1,9 +1,11 @@
-"""The entry points under HIP graph capture.  libkda allocates nothing,
-synchronises nothing and clears no memory with memset: every call is a
-sequence of kernel launches on the caller's stream, so a caller can capture
-it once and replay it.  Each test replays a captured call several times, with
-eager work and synchronisations between the replays, and checks every replay
-bit for bit against the same call run eagerly (same kernels, same inputs).
+"""The entry points under HIP graph capture and on concurrent streams.
+libkda allocates nothing, synchronises nothing, clears no memory with memset
+and keeps no mutable global state: every call is a sequence of kernel
+launches on the caller's stream, so a caller can capture it once and replay
+it, or run independent calls side by side.  The graph tests replay a
+captured call several times, with eager work and synchronisations between
+the replays, and check every replay bit for bit against the same call run
+eagerly (same kernels, same inputs).
 """
 import pytest
 import torch
@@ -102,3 +104,41 @@ def test_decode_graph_replays_match_eager(kda):
         g.replay()                           # a second step from the replayed state
         torch.cuda.synchronize()
         assert torch.equal(o_g, o2) and torch.equal(st, s2), f"replay {r}, second step"
+
+
+def test_concurrent_streams_match_sequential(kda):
+    """The library holds no mutable global state: two prefill calls and two
+    decode calls on two streams at once, each with its own buffers, give the
+    bits of the same calls run one after the other."""
+    case = KI.PrefillCase("streams", H=3, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=900,
+                          zero_h0=False)
+    d1 = to_dev(KI.make_prefill(case, seed=44))
+    d2 = to_dev(KI.make_prefill(case, seed=45))
+    dec = KI.make_decode(KI.DecodeCase("streamsdec", N=16, H=3, dk=128, dv=128, steps=1,
+                                       dtype="bf16"), seed=46)
+    A = dec["A"].cuda()
+    tok = {k: dec["steps"][0][k].cuda().contiguous() for k in ("q", "k", "v", "z", "b")}
+
+    def prefill(d):
+        return kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["b"], d["A"],
+                                 initial_state=d["h0"])
+    ref1, ref2 = prefill(d1), prefill(d2)
+    s_ref = [dec["state"].cuda().clone() for _ in range(2)]
+    o_ref = [kda.kda_recurrent_step(tok["q"], tok["k"], tok["v"], tok["z"], tok["b"], A, s)
+             for s in s_ref]
+    st = [dec["state"].cuda().clone() for _ in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    out = [None, None]
+    for i, (s, d) in enumerate(zip(streams, (d1, d2))):
+        with torch.cuda.stream(s):
+            out[i] = (prefill(d),
+                      kda.kda_recurrent_step(tok["q"], tok["k"], tok["v"], tok["z"], tok["b"], A,
+                                             st[i]))
+    torch.cuda.synchronize()
+    for i, ref in enumerate((ref1, ref2)):
+        (o, hT), od = out[i]
+        assert torch.equal(o, ref[0]) and torch.equal(hT, ref[1])
+        assert torch.equal(od, o_ref[i]) and torch.equal(st[i], s_ref[i])
