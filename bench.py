@@ -116,13 +116,19 @@ def _counter_record(name: str):
     return rec
 
 
-def _traffic_for(kernel: str):
+def _traffic_for(kernel: str, split: bool = False):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/traffic_long_1m.json), or None when the kernel code changed
-    since the counters were taken."""
+    since the counters were taken.  With split, the (read, write) bytes."""
     rec = _counter_record("traffic_long_1m")
     k = None if rec is None else rec.get("kernels", {}).get(kernel)
-    return None if k is None else int(k["hbm_bytes"])
+    if k is None:
+        return None
+    if not split:
+        return int(k["hbm_bytes"])
+    cal = rec["calibration"]
+    return [int(round(k["FETCH_SIZE_KiB"] * cal["fetch_factor"] * 1024)),
+            int(round(k["WRITE_SIZE_KiB"] * cal["write_factor"] * 1024))]
 
 
 def _mfma_counters(call_ms: float):
@@ -207,7 +213,10 @@ def bench_prefill(args, kda, torch, KI):
     achieved = kd["alg_bytes"] / (kd["ms"] * 1e-3) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": _traffic_for(dom)}
+            "traffic": _traffic_for(dom),
+            # reads are the kernel's inputs once; writes are the chunk records
+            # the chain launches read back (the three-launch design)
+            "traffic_read_write": _traffic_for(dom, split=True)}
     call_gbs = PREFILL_BYTES * units / (avg["call"] * 1e-3) / 1e9
     call_tfs = PREFILL_FLOPS * units / (avg["call"] * 1e-3) / 1e12
     extra = {
