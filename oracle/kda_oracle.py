@@ -25,7 +25,7 @@ design notes):
   * no query scale: o_t = S_t^T q_t exactly; a caller wanting 1/sqrt(d_k)
     pre-scales q (no formula on any page carries a scale);
   * A_h is one scalar per head used as exp(A_h) * z inside the sigmoid; the
-    "per-head bias" of [LA-KDA §5.3] is folded into z upstream;
+    per-head bias that [LA-KDA §5.3] mentions is folded into z upstream;
   * the recurrent (decode) call applies the same gate to the same raw logits
     as the chunked call ([K3-NOTES]: both paths share state semantics);
   * a packed batch restarts the state at every sequence from that
@@ -45,7 +45,12 @@ Functions:
                                        passes over a draft window
   recurrence_dplr_general           -- the diagonal-plus-low-rank update with its own
                                        low-rank pair (a, b) and write key
-  chunkwise_dplr                    -- its chunked form with four C x C matrices
+  chunkwise_dplr, decode_step_dplr  -- its chunked form with four C x C matrices, and
+                                       its single-token step
+  short_conv, silu, l2norm,
+  rmsnorm_gated, fused_forward      -- the layer around the core ([LA-KDA §5.3, §5.5]):
+                                       causal short convolution, Swish, L2Norm before,
+                                       Sigmoid(gate) * RMSNorm after
 All arithmetic is float64.  Inputs are converted to float64 exactly as given
 (bf16 tensors are first widened, so the oracle sees the same rounded values
 the GPU sees); nothing is rounded internally.
