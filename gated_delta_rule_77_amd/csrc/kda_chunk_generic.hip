@@ -134,7 +134,15 @@ void gen_intra_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     }
 }
 
-// One workgroup per (sequence, head); the fp32 state lives in LDS.
+// The chain over a sequence's chunks.  Columns of the state evolve
+// independently (V~, O and the update of column j read only column j of S and
+// of U), so one workgroup per (sequence, head, 16-column slice) carries its
+// slice of S in LDS and reads the chunk's W, Q, Kbar, A and gamma rows whole
+// (shared through L2 by the slices of one head).  Each thread produces four
+// adjacent columns of a row; every sum runs in the same order as the plain
+// definition: U - sum_c W S, sum_c Q S + sum_m A V~, gamma S + sum_i Kbar V~.
+constexpr int kGenCS = 16;      // state columns per workgroup
+
 template <int DK, int DV, int C, typename Tin>
 __global__ __launch_bounds__(256)
 void gen_chain_kernel(const float* __restrict__ recs, const int2* __restrict__ seqs,
@@ -143,15 +151,18 @@ void gen_chain_kernel(const float* __restrict__ recs, const int2* __restrict__ s
                       float* __restrict__ dbgS)
 {
     using R = GenRec<DK, DV, C>;
-    const int p = blockIdx.x;           // sequence * H + head
+    constexpr int CS = DV < kGenCS ? DV : kGenCS, NSL = DV / CS, Q4 = CS / 4;
+    const int p = blockIdx.x / NSL, j0 = (blockIdx.x % NSL) * CS;   // (sequence * H + head, slice)
     const int n = p / H, h = p % H;
     const int tid = threadIdx.x;
 
-    __shared__ float sS[DK][DV];
-    __shared__ float sVt[C][DV];
+    __shared__ __align__(16) float sS[DK][CS];
+    __shared__ __align__(16) float sVt[C][CS];
 
-    for (int idx = tid; idx < DK * DV; idx += 256)
-        sS[idx / DV][idx % DV] = h0 ? h0[(size_t)p * DK * DV + idx] : 0.f;
+    for (int idx = tid; idx < DK * CS; idx += 256) {
+        const int c = idx / CS, j = idx % CS;
+        sS[c][j] = h0 ? h0[(size_t)p * DK * DV + (size_t)c * DV + j0 + j] : 0.f;
+    }
 
     const int2 sd = seqs[n];
     for (int ci = 0; ci < sd.y; ci++) {
@@ -161,34 +172,77 @@ void gen_chain_kernel(const float* __restrict__ recs, const int2* __restrict__ s
         const float* rec = recs + ((size_t)cid * H + h) * R::FLOATS;
         __syncthreads();
         if (dbgS)
-            for (int idx = tid; idx < DK * DV; idx += 256)
-                dbgS[((size_t)cid * H + h) * DK * DV + idx] = sS[idx / DV][idx % DV];
-        for (int idx = tid; idx < C * DV; idx += 256) {
-            const int i = idx / DV, j = idx % DV;
-            float acc = rec[R::U + idx];
-            for (int c = 0; c < DK; c++) acc -= rec[R::W + i * DK + c] * sS[c][j];
-            sVt[i][j] = acc;
+            for (int idx = tid; idx < DK * CS; idx += 256) {
+                const int c = idx / CS, j = idx % CS;
+                dbgS[((size_t)cid * H + h) * DK * DV + (size_t)c * DV + j0 + j] = sS[c][j];
+            }
+        // V~ = U - W S (rows i, columns 4q .. 4q + 3 of the slice)
+        for (int item = tid; item < C * Q4; item += 256) {
+            const int i = item / Q4, jq = 4 * (item % Q4);
+            const float* Ur = rec + R::U + (size_t)i * DV + j0 + jq;
+            float4 acc = make_float4(Ur[0], Ur[1], Ur[2], Ur[3]);
+            const float* Wr = rec + R::W + (size_t)i * DK;
+            for (int c4 = 0; c4 < DK; c4 += 4) {
+                const float4 w = *reinterpret_cast<const float4*>(Wr + c4);
+                const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float4 sv = *reinterpret_cast<const float4*>(&sS[c4 + e][jq]);
+                    acc.x -= wv[e] * sv.x; acc.y -= wv[e] * sv.y;
+                    acc.z -= wv[e] * sv.z; acc.w -= wv[e] * sv.w;
+                }
+            }
+            *reinterpret_cast<float4*>(&sVt[i][jq]) = acc;
         }
         __syncthreads();
-        for (int idx = tid; idx < C * DV; idx += 256) {
-            const int i = idx / DV, j = idx % DV;
-            float acc = 0.f;
-            for (int c = 0; c < DK; c++) acc += rec[R::Q + i * DK + c] * sS[c][j];
-            for (int m = 0; m <= i; m++) acc += rec[R::A + i * C + m] * sVt[m][j];
-            if (i < len) o[((size_t)(tok0 + i) * H + h) * DV + j] = from_f32<Tin>(acc);
+        // O = (Q . Gamma) S + A_qk V~
+        for (int item = tid; item < C * Q4; item += 256) {
+            const int i = item / Q4, jq = 4 * (item % Q4);
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float* Qr = rec + R::Q + (size_t)i * DK;
+            for (int c4 = 0; c4 < DK; c4 += 4) {
+                const float4 qv = *reinterpret_cast<const float4*>(Qr + c4);
+                const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float4 sv = *reinterpret_cast<const float4*>(&sS[c4 + e][jq]);
+                    acc.x += qa[e] * sv.x; acc.y += qa[e] * sv.y;
+                    acc.z += qa[e] * sv.z; acc.w += qa[e] * sv.w;
+                }
+            }
+            const float* Ar = rec + R::A + (size_t)i * C;
+            for (int m = 0; m <= i; m++) {
+                const float a = Ar[m];
+                const float4 vv = *reinterpret_cast<const float4*>(&sVt[m][jq]);
+                acc.x += a * vv.x; acc.y += a * vv.y; acc.z += a * vv.z; acc.w += a * vv.w;
+            }
+            if (i < len) {
+                Tin* orow = o + ((size_t)(tok0 + i) * H + h) * DV + j0 + jq;
+                orow[0] = from_f32<Tin>(acc.x); orow[1] = from_f32<Tin>(acc.y);
+                orow[2] = from_f32<Tin>(acc.z); orow[3] = from_f32<Tin>(acc.w);
+            }
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * DV; idx += 256) {
-            const int c = idx / DV, j = idx % DV;
-            float acc = rec[R::G + c] * sS[c][j];
-            for (int i = 0; i < C; i++) acc += rec[R::K + i * DK + c] * sVt[i][j];
-            sS[c][j] = acc;
+        // S <- Diag(gamma_C) S + Kbar^T V~
+        for (int item = tid; item < DK * Q4; item += 256) {
+            const int c = item / Q4, jq = 4 * (item % Q4);
+            const float g = rec[R::G + c];
+            const float4 s0 = *reinterpret_cast<const float4*>(&sS[c][jq]);
+            float4 acc = make_float4(g * s0.x, g * s0.y, g * s0.z, g * s0.w);
+            for (int i = 0; i < C; i++) {
+                const float kb = rec[R::K + (size_t)i * DK + c];
+                const float4 vv = *reinterpret_cast<const float4*>(&sVt[i][jq]);
+                acc.x += kb * vv.x; acc.y += kb * vv.y; acc.z += kb * vv.z; acc.w += kb * vv.w;
+            }
+            *reinterpret_cast<float4*>(&sS[c][jq]) = acc;
         }
     }
     __syncthreads();
     if (hT)
-        for (int idx = tid; idx < DK * DV; idx += 256)
-            hT[(size_t)p * DK * DV + idx] = sS[idx / DV][idx % DV];
+        for (int idx = tid; idx < DK * CS; idx += 256) {
+            const int c = idx / CS, j = idx % CS;
+            hT[(size_t)p * DK * DV + (size_t)c * DV + j0 + j] = sS[c][j];
+        }
 }
 
 template <int D, int C, typename Tin>
@@ -203,9 +257,11 @@ hipError_t launch_generic_t(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gen_chain_kernel<D, D, C, Tin>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
-                       a.stream, (const float*)recs, seqs, chunks, a.h0, a.H, (Tin*)a.o, a.hT,
-                       a.dbg_state);
+    constexpr int NSL = D < kGenCS ? 1 : D / kGenCS;          // column slices per (sequence, head)
+    if ((long long)a.N * a.H * NSL > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gen_chain_kernel<D, D, C, Tin>), dim3((unsigned)((long long)a.N * a.H * NSL)),
+                       dim3(256), 0, a.stream, (const float*)recs, seqs, chunks, a.h0, a.H,
+                       (Tin*)a.o, a.hT, a.dbg_state);
     return hipGetLastError();
 }
 
