@@ -450,24 +450,34 @@ def test_deterministic(kda):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
-def test_in_place_final_state(kda):
-    """hT may alias h0."""
-    case = KI.PrefillCase("alias", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=130,
+@pytest.mark.parametrize("dtype,dk,chunk", [
+    ("bf16", 128, 64),     # MFMA path
+    ("fp32", 128, 64),     # fp32 path: eight 16-column slices per (sequence, head)
+    ("fp32", 64, 16),      # fp32 path: four slices, 16-token chunks
+])
+def test_in_place_final_state(kda, dtype, dk, chunk):
+    """hT may alias h0: the in-place call equals the out-of-place one bit for bit."""
+    T, H = 130, 2
+    case = KI.PrefillCase("alias", H=H, dk=dk, dv=dk, chunk=chunk, dtype=dtype, B=1, T=T,
                           zero_h0=False)
     d = to_dev(KI.make_prefill(case, seed=13))
     o1, h1 = gpu_prefill(kda, d)
     st = d["h0"].clone()
     L = kda.lib()
-    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, 130, 2, 128, 128, 1, 64, torch.bfloat16),
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, T, H, dk, dk, 1, chunk, tdt),
                      dtype=torch.uint8, device="cuda")
     o2 = torch.empty_like(o1)
     rc = L.kda_chunk_fwd(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["z"].data_ptr(),
-                         d["b"].data_ptr(), d["A"].data_ptr(), st.data_ptr(), None, 1, 130, 2, 128,
-                         128, 1, 64, 1, o2.data_ptr(), st.data_ptr(), ws.data_ptr(), ws.numel(),
-                         torch.cuda.current_stream().cuda_stream)
+                         d["b"].data_ptr(), d["A"].data_ptr(), st.data_ptr(), None, 1, T, H, dk,
+                         dk, 1, chunk, 1 if dtype == "bf16" else 0, o2.data_ptr(), st.data_ptr(),
+                         ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(o1, o2) and torch.equal(h1, st)
+    ro, rS = oracle_prefill(KI.make_prefill(case, seed=13))
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    assert rel_err(o2[0], ro) <= tol and rel_err(st[0], rS) <= tol
 
 
 # ---------------------------------------------------------------- replay fold
