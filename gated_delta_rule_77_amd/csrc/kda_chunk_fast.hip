@@ -132,6 +132,20 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     //      one lane); gate [LA-KDA §5.4] and in-chunk cumulative sum in log2 units
     uint4 kr[4], qr[4], vr[4];
     float qkf[2][4][8];              // CONV: q, k after Swish, before the L2Norm
+    // the beta logits, issued with the first loads so that their latency hides
+    // under the gate scan (wave 0 turns them into beta before the barrier)
+    float blx = 0.f;
+    if (tid < 64) blx = bl[(size_t)(tok0 + min(tid, lastrow)) * H + h];
+    // the gate logits (thread = channel c, rows 32 half .. 32 half + 31),
+    // likewise issued first; with CONV after the convolution, whose registers
+    // leave no room for them before it
+    const int c = tid & 127, half = tid >> 7;
+    float lr[32];
+    auto load_gate_logits = [&]() {
+#pragma unroll
+        for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
+    };
+    if constexpr (MODE != kModeDeltaNet && !CONV) load_gate_logits();
     float* sL2 = reinterpret_cast<float*>(smem + kOffRK);   // CONV: [2][64 rows][4 waves], free in step 1
     if constexpr (!CONV) {
 #pragma unroll
@@ -204,14 +218,11 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             }
         }
     }
-    const int c = tid & 127, half = tid >> 7;
-    float lr[32];
     {
         float a2 = 0.f;                                 // e^{-e^A z} = 2^(a2 z)
         if constexpr (MODE != kModeDeltaNet) {
             a2 = -expf(A[h]) * kLog2e;
-#pragma unroll
-            for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
+            if constexpr (CONV) load_gate_logits();
         }
         float run = 0.f;
 #pragma unroll
@@ -225,10 +236,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             lr[i] = run;
             sG[row * kLdG + c] = run;
         }
-        if (tid < 64) {
-            const float x = bl[(size_t)(tok0 + min(tid, lastrow)) * H + h];
-            sBeta[tid] = tid < len ? __builtin_amdgcn_rcpf(1.f + ex2(-x * kLog2e)) : 0.f;
-        }
+        if (tid < 64) sBeta[tid] = tid < len ? __builtin_amdgcn_rcpf(1.f + ex2(-blx * kLog2e)) : 0.f;
     }
     __syncthreads();
     if constexpr (CONV) {
