@@ -557,7 +557,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-reps", type=int, default=4, help="passes over the 16 decode steps")
-    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-tokens", type=int, default=40960)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
