@@ -854,6 +854,38 @@ __device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int
     if (t < 32) *reinterpret_cast<u32x4*>(st + TS::G + t * 16) = r.g;
 }
 
+// gamma_C of the rows 16 RT + 4 g4 + e (e = 0..3) that lane (n16, g4) holds in
+// row tile RT.  Lane (n16, g4) has read gv0 = gamma_C[16 (n16 >> 2) + 4 g4 +
+// (n16 & 3)] and gv1 the same 64 rows on; the value of element e of tile RT
+// sits in lane 4 (RT & 3) + e of the lane's own 16-lane row, and a DPP row
+// broadcast hands it to the whole row (two 4-byte LDS reads per lane and
+// chunk instead of a 16-byte read per row tile).
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + L,
+                                                              0xF, 0xF, false));
+}
+
+template <int RT>
+__device__ __forceinline__ float4 gamma_rows(float gv0, float gv1) {
+    const float x = RT < 4 ? gv0 : gv1;
+    constexpr int L0 = 4 * (RT & 3);
+    return make_float4(row_bcast<L0>(x), row_bcast<L0 + 1>(x), row_bcast<L0 + 2>(x), row_bcast<L0 + 3>(x));
+}
+
+__device__ __forceinline__ float4 gamma_tile(int rt, float gv0, float gv1) {
+    switch (rt) {      // rt is a constant wherever the callers' loops are unrolled
+        case 0: return gamma_rows<0>(gv0, gv1);
+        case 1: return gamma_rows<1>(gv0, gv1);
+        case 2: return gamma_rows<2>(gv0, gv1);
+        case 3: return gamma_rows<3>(gv0, gv1);
+        case 4: return gamma_rows<4>(gv0, gv1);
+        case 5: return gamma_rows<5>(gv0, gv1);
+        case 6: return gamma_rows<6>(gv0, gv1);
+        default: return gamma_rows<7>(gv0, gv1);
+    }
+}
+
 // One chunk for wave w from the staged record.  KDA: V~ = U - W S (U = 0 for
 // M), S <- Diag(gamma_C) S + Kbar^T V~.  GLA: V~ = U, so the M columns
 // (V~ = 0) only decay.  DPLR: X~ = Wb S, S <- Diag(gamma_C) S + Abar^T X~ + Cs
@@ -864,10 +896,13 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
     constexpr bool DPLR = CK == kChainDPLR;
     using TS = TransStage<DPLR>;
     const float* gC = reinterpret_cast<const float*>(st + TS::G);
+    const int n16 = lane & 15;
+    const float gv0 = gC[16 * (n16 >> 2) + 4 * g4 + (n16 & 3)];
+    const float gv1 = gC[64 + 16 * (n16 >> 2) + 4 * g4 + (n16 & 3)];
     if (CK == kChainGLA && w >= 4) {
 #pragma unroll
         for (int rt = 0; rt < 8; rt++) {
-            const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
+            const float4 g = gamma_tile(rt, gv0, gv1);
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 f32x4& a = acc[rt][j];
@@ -910,7 +945,7 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
         for (int j = 0; j < 2; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
 #pragma unroll
     for (int rt = 0; rt < 8; rt++) {
-        const float4 g = *reinterpret_cast<const float4*>(gC + 16 * rt + 4 * g4);
+        const float4 g = gamma_tile(rt, gv0, gv1);
         const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 0) * 64 + lane) * 16);
         const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
