@@ -260,6 +260,7 @@ def bench_decode(args, kda, torch, KI):
     mean = sum(ms) / len(ms)
     units = run["N"] * run["H"]
     gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
+    graph = bench_decode_graph(args, kda, torch, run)
     fold = bench_fold(args, kda, torch, run, mean)
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(run, len(run["steps"]))
     return {
@@ -273,9 +274,54 @@ def bench_decode(args, kda, torch, KI):
         "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
                 "algorithmic bytes and may exceed the HBM rate",
         "traffic": _decode_traffic(mean),
+        "graph": graph,
         "cpu_baseline": cpu,
         "fold": fold,
     }
+
+
+def bench_decode_graph(args, kda, torch, run):
+    """The 16 decode steps captured once into a HIP graph (the launch-bound
+    serving loop) and replayed back to back: per-step time without the
+    per-launch host and event overhead of the eager loop.  The first replay's
+    state is compared bit for bit with 16 eager steps from the same state."""
+    A, steps = run["A"], run["steps"]
+    st0 = run["state"].clone()
+    st = st0.clone()
+
+    def loop(state):
+        for s in steps:
+            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, state)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop(st0.clone())                      # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop(st)
+    st.copy_(st0)
+    torch.cuda.synchronize()
+    g.replay()
+    ref = st0.clone()
+    loop(ref)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st, ref))
+    reps = max(4, 2 * args.decode_reps)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * len(steps))
+    gbs = DECODE_BYTES * run["N"] * run["H"] / (ms * 1e-3) / 1e9
+    return {"steps_timed": reps * len(steps), "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(run["N"] / (ms * 1e-3), 1), "alg_GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "replay_equals_eager": same}
 
 
 def _decode_traffic(step_ms: float):
@@ -592,6 +638,10 @@ def main():
 
     value, ms, roof, extra, cpu_inp = bench_prefill(args, kda, torch, KI)
     dec = None if args.no_decode else bench_decode(args, kda, torch, KI)
+    if dec:
+        print(f"[bench] decode: {dec['ms_per_step_mean']:.4f} ms/step eager, "
+              f"{dec['graph']['ms_per_step']:.4f} ms/step graph-replayed "
+              f"(replay equals eager: {dec['graph']['replay_equals_eager']})", flush=True)
     layer = None
     if not args.no_layer:
         layer = bench_layer(args, kda, torch, KI, extra["call_ms_events"],
