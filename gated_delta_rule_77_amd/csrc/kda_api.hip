@@ -15,15 +15,28 @@ static_assert(KDA_MODE_KDA == kModeKDA && KDA_MODE_GLA == kModeGLA &&
 
 bool chunk_shape_supported(int dk, int dv, int chunk) { return generic_supported(dk, dv, chunk); }
 
+// A dispatch's grid size (workgroups x threads) is a 32-bit work-item count.
+constexpr long long kMaxWorkItems = 0xFFFFFFFFLL;
+bool items_ok(long long blocks, long long threads) { return blocks * threads <= kMaxWorkItems; }
+
 // sizes shared by the prefill entry points; false on invalid arguments
 bool prefill_sizes_ok(int B, int T, int H, int dk, int dv, int N, int chunk) {
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || N < 0 || chunk < 1) return false;
     if ((long long)B * T > 0x7fffffffLL) return false;            // token index fits int32
     if ((long long)N * H > 0x7fffffffLL) return false;
     const int cap = chunk_capacity(B, T, N, chunk);
-    // one workgroup per (chunk, head) and per (segment, head): grids stay within int32
-    return cap >= 0 && (long long)cap * H <= 0x7fffffffLL;
+    if (cap < 0) return false;
+    // one workgroup per (chunk, head) (256 threads) and per (segment, head)
+    // (at most 512 threads; at most twice as many segments as chunks); per
+    // (sequence, head) the fp32 chain runs up to 8 column slices and the
+    // composition 8 of 256 threads
+    if (!items_ok((long long)cap * H, 1024) || !items_ok((long long)N * H, 2048)) return false;
+    // the intra kernels address a chunk's rows with 32-bit offsets
+    return (long long)H * (dk > dv ? dk : dv) * chunk <= kMaxWorkItems;
 }
+
+// decode-type launches: one workgroup of at most 256 threads per (sequence, head)
+bool nh_ok(int N, int H) { return items_ok((long long)N * H, 256); }
 
 kda_status_t run_prefill(const void* q, const void* k, const void* v, const float* z,
                          const float* b, const float* A, const float* h0, const int* cu,
@@ -88,6 +101,8 @@ LayerWs layer_ws(int B, int T, int H, int d, int N, int chunk, kda_dtype_t dtype
     if (!dtype_ok(dtype) || !prefill_sizes_ok(B, T, H, d, d, N, chunk)) return w;
     if (!chunk_shape_supported(d, d, chunk)) return w;
     const bool fast = use_fast_path(d, d, chunk, dtype == KDA_BF16);
+    // the fp32 path's convolution and output-gate passes: 64 threads per row
+    if (!fast && !items_ok(((long long)B * T * H + 3) / 4, 256)) return w;
     const WsLayout L = ws_layout(B, T, H, d, d, N, chunk, fast);
     if (L.total == 0) return w;
     w.core = align256(L.total);
@@ -183,7 +198,7 @@ kda_status_t kda_recurrent_step_mode(const void* q, const void* k, const void* v
                                      int dv, kda_dtype_t dtype, kda_mode_t mode, void* stream) {
     if (!dtype_ok(dtype) || !mode_ok(mode)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!nh_ok(N, H)) return KDA_ERR_INVALID_ARG;
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
     const bool gated = mode != KDA_MODE_DELTANET;
@@ -288,7 +303,7 @@ kda_status_t kda_dplr_recurrent_step(const void* q, const void* k, const void* v
                                      kda_dtype_t dtype, void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!nh_ok(N, H)) return KDA_ERR_INVALID_ARG;
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !a || !b || !g_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
@@ -362,7 +377,7 @@ kda_status_t kda_layer_step(const void* q_in, const void* k_in, const void* v_in
                             void* y, int N, int H, int d, kda_dtype_t dtype, void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || d < 1) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!nh_ok(N, H)) return KDA_ERR_INVALID_ARG;
     if (!eps_ok(l2_eps) || !eps_ok(rms_eps)) return KDA_ERR_INVALID_ARG;
     if (!decode_supported(d, d)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
@@ -381,7 +396,7 @@ kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v,
                                   kda_dtype_t dtype, void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || W < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H > 0x7fffffffLL || (long long)N * W * H > 0x7fffffffLL)
+    if (!nh_ok(N, H) || (long long)N * W * H > 0x7fffffffLL)
         return KDA_ERR_INVALID_ARG;
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0 || W == 0) return KDA_OK;
@@ -397,7 +412,7 @@ kda_status_t kda_recurrent_fold(const void* k, const void* v, const float* g_log
                                 kda_dtype_t dtype, void* stream) {
     if (!dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || W < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;
+    if (!nh_ok(N, H)) return KDA_ERR_INVALID_ARG;
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0 || W == 0) return KDA_OK;
     if (!k || !v || !g_logits || !beta_logits || !A || !n_accept || !state) return KDA_ERR_INVALID_ARG;

@@ -82,6 +82,17 @@ KDA_API const char* kda_status_string(kda_status_t s);
  *                       combination runs an fp32-arithmetic path.
  *   kda_recurrent_step: d_k == d_v in {16, 32, 64, 128}, fp32 or bf16.
  * Returns 1 when the combination is compiled in, 0 otherwise.
+ *
+ * Size limits (KDA_ERR_INVALID_ARG beyond them, checked on the host; a
+ * dispatch counts its work-items in 32 bits, and the intra-chunk kernels
+ * address a chunk's rows with 32-bit offsets):
+ *   prefill:  B * T < 2^31;  C_cap * H * 1024 < 2^32 with C_cap = B * ceil(T /
+ *             chunk) + N (about 4.2M chunk-heads);  N * H * 2048 < 2^32;
+ *             H * max(d_k, d_v) * chunk < 2^32 (H < 524,288 at d = 128,
+ *             chunk 64);  on the fp32 layer path also B * T * H * 64 < 2^32.
+ *   recurrent calls:  N * H * 256 < 2^32.
+ * At d = 128 each limit lies beyond what 288 GB of HBM can hold for the
+ * tensors involved, except the head count of very short batches.
  */
 KDA_API int kda_chunk_fwd_supported(int dk, int dv, int chunk, kda_dtype_t dtype);
 KDA_API int kda_recurrent_step_supported(int dk, int dv, kda_dtype_t dtype);

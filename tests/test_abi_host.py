@@ -257,3 +257,30 @@ def test_grid_limits_are_validated(L):
     # B * T fits int32, but ceil(T / 16) * H does not
     assert L.kda_chunk_fwd_workspace_bytes(1, 2000000000, 1024, 16, 16, 1, 16, 0) == 0
     assert _chunk(L, q=FAKE, k=FAKE, v=FAKE, z=FAKE, b=FAKE, A=FAKE, o=FAKE, T=2000000000, H=1024) == 1
+
+
+def test_work_item_and_offset_limits_are_validated(L):
+    """Each dispatch counts work-items in 32 bits and the intra-chunk kernels
+    address a chunk's rows with 32-bit offsets: shapes past either limit are
+    refused on the host, before any launch; shapes just inside are accepted."""
+    ws = L.kda_chunk_fwd_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    full = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, b=FAKE, A=FAKE, o=FAKE)
+    # H * 128 * 64 >= 2^32: one chunk of 600,000 heads on the MFMA path
+    assert ws(1, 64, 600000, 128, 128, 1, 64, 1) == 0
+    assert _chunk(L, **full, T=64, H=600000, dk=128, dv=128, chunk=64, dtype=1) == 1
+    # just inside: H * 128 * 64 = 2^32 - 65,536
+    assert ws(1, 64, 524287, 128, 128, 1, 64, 1) > 0
+    # N * H * 2048 >= 2^32: 300,000 packed sequences of 12 heads
+    assert ws(1, 3000000, 12, 16, 16, 300000, 16, 0) == 0
+    assert _chunk(L, **full, cu=FAKE, T=3000000, H=12, N=300000) == 1
+    # recurrent calls: N * H * 256 >= 2^32
+    fn = L.kda_recurrent_step
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    assert fn(*([FAKE] * 8), 1 << 20, 16, 128, 128, 1, None) == 1
+    # the fp32 layer path's per-row passes: B * T * H * 64 >= 2^32
+    lw = L.kda_layer_fwd_workspace_bytes
+    lw.restype = ctypes.c_size_t
+    assert lw(1, 100000000, 1, 16, 1, 16, 0) == 0
+    assert lw(1, 1000000, 1, 16, 1, 16, 0) > 0
