@@ -163,6 +163,18 @@ def _req(t, name, dtype=None, device=None):
     return t
 
 
+def _workspace(workspace, need: int, device):
+    """The caller's workspace (a contiguous uint8 tensor on `device`, at least
+    `need` bytes; the library also requires 256-byte alignment), or a fresh one
+    when none is given or it is too small."""
+    torch = _torch()
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8, device)
+        if workspace.numel() >= need:
+            return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def _stream(device) -> int:
     return _torch().cuda.current_stream(device).cuda_stream
 
@@ -257,8 +269,7 @@ def _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size, output_fi
     if need == 0:
         _check(2 if not L.kda_chunk_fwd_supported(dk, dv, chunk_size, code) else 1,
                "kda_chunk_fwd_workspace_bytes")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A), _ptr(initial_state),
@@ -315,8 +326,7 @@ def kda_dplr_chunk_fwd(q, k, v, a, b, g, A, initial_state=None, cu_seqlens=None,
     if need == 0:
         _check(2 if not L.kda_chunk_fwd_supported(dk, dv, chunk_size, code) else 1,
                "kda_dplr_chunk_fwd_workspace_bytes")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     _check(L.kda_dplr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(A),
@@ -494,8 +504,7 @@ def kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, initial_st
     if need == 0:
         _check(2 if not L.kda_chunk_fwd_supported(d, d, chunk_size, code) else 1,
                "kda_layer_fwd_workspace_bytes")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     y = torch.empty((B, T, H, d), dtype=dt, device=dev)
     hT = torch.empty((N, H, d, d), dtype=torch.float32, device=dev) if output_final_state else None
     csT = torch.empty((N, 3, 3, H, d), dtype=dt, device=dev) if output_final_state else None

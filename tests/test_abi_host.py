@@ -127,6 +127,15 @@ def test_binding_refuses_cpu_tensors():
                                torch.zeros(4, 1, 16, 16))
 
 
+def test_binding_refuses_a_host_workspace():
+    """A caller's workspace must be device memory: a host tensor raises before
+    its pointer could reach a kernel."""
+    import torch
+    import gated_delta_rule_77_amd as kda
+    with pytest.raises(ValueError):
+        kda._workspace(torch.zeros(1024, dtype=torch.uint8), 512, torch.device("cuda", 0))
+
+
 def test_recurrent_fold_rejects_bad_arguments(L):
     fn = L.kda_recurrent_fold
     fn.restype = ctypes.c_int
