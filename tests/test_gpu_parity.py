@@ -117,6 +117,35 @@ def test_long_1m_config_sampled(kda):
     assert eS <= TOL_BF16
 
 
+def test_long_1m_column_permutation_and_scaling(kda):
+    """Properties that hold at any size, checked on every output of the
+    1M-token workload: value columns evolve independently (permuting the d_v
+    columns of v and h0 permutes those of o and of the final state), and
+    (o, hT) is linear in (v, h0) (doubling both doubles both; a factor of two
+    is exact in floating point).  Both hold to rounding-free precision on this
+    path: the bar is 1e-6 of the largest value (denormals flushed to zero are
+    the only allowed difference)."""
+    case = KI.CONFIGS["long_1m"]
+    d = KI.make_prefill(case, device="cuda", seed=0)
+    o, hT = gpu_prefill(kda, d)
+    perm = torch.randperm(case.dv, generator=torch.Generator().manual_seed(5)).cuda()
+    dp = dict(d, v=d["v"][..., perm].contiguous(), h0=d["h0"][..., perm].contiguous())
+    op, hp = gpu_prefill(kda, dp)
+    torch.cuda.synchronize()
+    omax, smax = o.float().abs().max(), hT.abs().max()
+    e_o = float((op.float() - o[..., perm].float()).abs().max() / omax)
+    e_s = float((hp - hT[..., perm]).abs().max() / smax)
+    del dp, op, hp
+    d2 = dict(d, v=d["v"] * 2, h0=d["h0"] * 2)
+    o2, h2 = gpu_prefill(kda, d2)
+    torch.cuda.synchronize()
+    e2_o = float((o2.float() - 2 * o.float()).abs().max() / omax)
+    e2_s = float((h2 - 2 * hT).abs().max() / smax)
+    _report("long_1m permuted columns", o=e_o, hT=e_s)
+    _report("long_1m doubled v, h0", o=e2_o, hT=e2_s)
+    assert max(e_o, e_s, e2_o, e2_s) <= 1e-6
+
+
 def test_decode_config(kda):
     """N=256, H=12, 16 steps, state updated in place: equals a 16-token chunked
     prefill from the same state (all sequences and heads), and four sampled
