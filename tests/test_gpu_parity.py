@@ -117,15 +117,16 @@ def test_long_1m_config_sampled(kda):
     assert eS <= TOL_BF16
 
 
-def test_long_1m_column_permutation_and_scaling(kda):
+@pytest.mark.parametrize("name", ["long_1m", "varlen_8"])
+def test_column_permutation_and_scaling(kda, name):
     """Properties that hold at any size, checked on every output of the
-    1M-token workload: value columns evolve independently (permuting the d_v
+    1M-token and packed workloads: value columns evolve independently (permuting the d_v
     columns of v and h0 permutes those of o and of the final state), and
     (o, hT) is linear in (v, h0) (doubling both doubles both; a factor of two
     is exact in floating point).  Both hold to rounding-free precision on this
     path: the bar is 1e-6 of the largest value (denormals flushed to zero are
     the only allowed difference)."""
-    case = KI.CONFIGS["long_1m"]
+    case = KI.CONFIGS[name]
     d = KI.make_prefill(case, device="cuda", seed=0)
     o, hT = gpu_prefill(kda, d)
     perm = torch.randperm(case.dv, generator=torch.Generator().manual_seed(5)).cuda()
@@ -141,8 +142,8 @@ def test_long_1m_column_permutation_and_scaling(kda):
     torch.cuda.synchronize()
     e2_o = float((o2.float() - 2 * o.float()).abs().max() / omax)
     e2_s = float((h2 - 2 * hT).abs().max() / smax)
-    _report("long_1m permuted columns", o=e_o, hT=e_s)
-    _report("long_1m doubled v, h0", o=e2_o, hT=e2_s)
+    _report(f"{name} permuted columns", o=e_o, hT=e_s)
+    _report(f"{name} doubled v, h0", o=e2_o, hT=e2_s)
     assert max(e_o, e_s, e2_o, e2_s) <= 1e-6
 
 
