@@ -473,6 +473,55 @@ def _stage_ms(h, evs):
     return {k: sum(_elapsed(h, e[a], e[b]) for e in evs) / len(evs) for k, (a, b) in keys.items()}
 
 
+def bench_short_prefill(args, kda, torch, KI):
+    """The 4,096-token prefill (B=1, H=16, d=128, chunk 64): a latency-shaped
+    call of five launches, timed eagerly and as a replay of one captured HIP
+    graph (the serving form for short prompts); the replay's outputs are
+    compared bit for bit with the eager call's."""
+    dev = torch.device("cuda:0")
+    d = KI.make_prefill(KI.CONFIGS["prefill_4k"], device=dev, seed=0)
+    B, T, H, dk, dv, N, C = d["B"], d["T"], d["H"], d["dk"], d["dv"], d["N"], d["chunk"]
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, C, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        return kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["b"], d["A"],
+                                 initial_state=d["h0"], chunk_size=C, workspace=ws)
+
+    def timed(fn, reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    o_ref, h_ref = call()
+    torch.cuda.synchronize()
+    reps = max(20, 4 * args.steps)
+    eager = timed(call, reps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        o_g, h_g = call()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o_g, o_ref) and torch.equal(h_g, h_ref))
+    graph = timed(g.replay, reps)
+    tok = B * T
+    return {"workload": "prefill_4k: B=1, H=16, T=4096, d_k=d_v=128, chunk=64, bf16, seed 0",
+            "ms_per_call_eager": round(eager, 4), "tokens_per_s_eager": round(tok / (eager * 1e-3), 1),
+            "ms_per_call_graph": round(graph, 4), "tokens_per_s_graph": round(tok / (graph * 1e-3), 1),
+            "replay_equals_eager": same}
+
+
 def bench_family(args, kda, torch, KI, kda_stages):
     """The other rows of the family table (GLA with the erase step off,
     DeltaNet with alpha = 1) and the general DPLR update with the low-rank pair
@@ -650,6 +699,10 @@ def main():
     if not args.no_family:
         family = bench_family(args, kda, torch, KI, {"intra": extra["kernels_ms"]["intra"],
                                                      "call": extra["call_ms_events"]})
+    short = bench_short_prefill(args, kda, torch, KI)
+    print(f"[bench] prefill_4k: {short['ms_per_call_eager']:.4f} ms/call eager, "
+          f"{short['ms_per_call_graph']:.4f} ms/call graph-replayed "
+          f"(replay equals eager: {short['replay_equals_eager']})", flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_inp, torch)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -660,7 +713,7 @@ def main():
                                "q/k/v, fp32 logits and state, seed 0",
                    "B": 1, "T": 1 << 20, "H": 12, "dk": 128, "dv": 128, "chunk": 64},
         "roofline": roof, "cpu_baseline": cpu, "prefill": extra, "decode": dec, "layer": layer,
-        "family": family,
+        "family": family, "prefill_4k": short,
     }
     print(json.dumps(line), flush=True)
 
