@@ -211,3 +211,33 @@ def test_dplr_random_packed_layouts(kda, case_id):
         eS = rel_err(hT[s][heads], rS, scale=s_scale)
         assert eo <= tol and eS <= tol, (case_id, dk, chunk, dtype, H, lens, s, eo, eS)
     _report(f"random layout {case_id}: d={dk} C={chunk} {dtype} H={H} lens={lens}", ok=0.0)
+
+
+def test_dplr_long_1m_column_permutation_and_scaling(kda):
+    """Every output and final state of the general DPLR update on the
+    1M-token shapes, through two properties that hold at any size: value
+    columns evolve independently (permuting the d_v columns of v and h0
+    permutes those of o and the final state), and (o, hT) is linear in
+    (v, h0) (doubling both doubles both, exactly in floating point).  Bar:
+    1e-6 of the largest value (only flushed denormals may differ)."""
+    case = KI.CONFIGS["long_1m"]
+    d = KI.make_dplr(case, device="cuda", seed=0)
+    d["cu_seqlens"] = None
+    o, hT = _gpu(kda, d, 64)
+    perm = torch.randperm(case.dv, generator=torch.Generator().manual_seed(6)).cuda()
+    dp = dict(d, v=d["v"][..., perm].contiguous(), h0=d["h0"][..., perm].contiguous())
+    op, hp = _gpu(kda, dp, 64)
+    torch.cuda.synchronize()
+    omax, smax = o.float().abs().max(), hT.abs().max()
+    e_o = float((op.float() - o[..., perm].float()).abs().max() / omax)
+    e_s = float((hp - hT[..., perm]).abs().max() / smax)
+    del dp, op, hp
+    d2 = dict(d, v=d["v"] * 2, h0=d["h0"] * 2)
+    o2, h2 = _gpu(kda, d2, 64)
+    torch.cuda.synchronize()
+    e2_o = float((o2.float() - 2 * o.float()).abs().max() / omax)
+    e2_s = float((h2 - 2 * hT).abs().max() / smax)
+    _report("long_1m permuted columns", o=e_o, hT=e_s)
+    _report("long_1m doubled v, h0", o=e2_o, hT=e2_s)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+    assert max(e_o, e_s, e2_o, e2_s) <= 1e-6
