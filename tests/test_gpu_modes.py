@@ -148,3 +148,30 @@ def test_decode_mode_vs_oracle_and_prefill(kda, mode, dtype, dk):
     e1, e2 = rel_err(torch.stack(outs, 1), op), rel_err(st, hp)
     _report(f"{mode} decode {dtype} d={dk} vs prefill", o=e1, state=e2)
     assert e1 <= tol and e2 <= tol
+
+
+@pytest.mark.parametrize("mode", ["gla", "deltanet"])
+def test_mode_long_1m_column_permutation_and_scaling(kda, mode):
+    """Every output and final state of a family mode on the 1M-token
+    workload, through two properties that hold at any size: permuting the d_v
+    columns of v and h0 permutes those of o and the final state, and doubling
+    (v, h0) doubles (o, hT), exactly in floating point.  Bar: 1e-6 of the
+    largest value (only flushed denormals may differ)."""
+    d = KI.make_prefill(KI.CONFIGS["long_1m"], device="cuda", seed=0)
+    o, hT = _gpu(kda, d, mode, 64)
+    perm = torch.randperm(d["dv"], generator=torch.Generator().manual_seed(7)).cuda()
+    dp = dict(d, v=d["v"][..., perm].contiguous(), h0=d["h0"][..., perm].contiguous())
+    op, hp = _gpu(kda, dp, mode, 64)
+    torch.cuda.synchronize()
+    omax, smax = o.float().abs().max(), hT.abs().max()
+    e_o = float((op.float() - o[..., perm].float()).abs().max() / omax)
+    e_s = float((hp - hT[..., perm]).abs().max() / smax)
+    del dp, op, hp
+    o2, h2 = _gpu(kda, dict(d, v=d["v"] * 2, h0=d["h0"] * 2), mode, 64)
+    torch.cuda.synchronize()
+    e2_o = float((o2.float() - 2 * o.float()).abs().max() / omax)
+    e2_s = float((h2 - 2 * hT).abs().max() / smax)
+    _report(f"{mode} long_1m permuted columns", o=e_o, hT=e_s)
+    _report(f"{mode} long_1m doubled v, h0", o=e2_o, hT=e2_s)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+    assert max(e_o, e_s, e2_o, e2_s) <= 1e-6
