@@ -131,6 +131,15 @@ def _traffic_for(kernel: str, split: bool = False):
             int(round(k["WRITE_SIZE_KiB"] * cal["write_factor"] * 1024))]
 
 
+def _path_traffic():
+    """HBM bytes of one whole prefill call (every launch of the KDA core in
+    the counter record), or None when any kernel's code changed since."""
+    rec = _counter_record("traffic_long_1m")
+    if rec is None:
+        return None
+    return int(sum(k["hbm_bytes"] for k in rec.get("kernels", {}).values()))
+
+
 def _mfma_counters(call_ms: float):
     """MFMA utilisation of the prefill kernels from the committed counter
     record (profiles/mfma_long_1m.json): per kernel the busy fraction of the
@@ -219,6 +228,18 @@ def bench_prefill(args, kda, torch, KI):
             "traffic_read_write": _traffic_for(dom, split=True)}
     call_gbs = PREFILL_BYTES * units / (avg["call"] * 1e-3) / 1e9
     call_tfs = PREFILL_FLOPS * units / (avg["call"] * 1e-3) / 1e12
+    mc = _mfma_counters(avg["call"])
+    # the whole kda_chunk_fwd call beside the dominant kernel: the algorithmic
+    # FLOPs (the MFMA side of the metric) and bytes of the path over the
+    # call's event time, and the HBM bytes all its launches moved
+    roof["call"] = {"ms": round(avg["call"], 4),
+                    "mfma_frac": round(call_tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "achieved_TFLOPs": round(call_tfs, 2), "mfma_peak_TFLOPs": MFMA_BF16_PEAK_TFS,
+                    "hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
+                    "achieved_GBps": round(call_gbs, 1),
+                    "alg_bytes": PREFILL_BYTES * units, "alg_flops": PREFILL_FLOPS * units,
+                    "traffic": _path_traffic(),
+                    "hw_mfma_frac": None if mc is None else mc["hw_mfma_frac"]}
     extra = {
         "call_ms_events": round(avg["call"], 4),
         "kernels_ms": {k: round(v, 4) for k, v in avg.items() if k not in ("call", "chain")},
@@ -226,16 +247,53 @@ def bench_prefill(args, kda, torch, KI):
         "path_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
         "path_alg_TFLOPs": round(call_tfs, 2),
         "mfma_frac_algorithmic": round(call_tfs / MFMA_BF16_PEAK_TFS, 4),
-        "mfma_counters": _mfma_counters(avg["call"]),
+        "mfma_counters": mc,
     }
-    cpu_inputs = {k: d[k][:, :args.cpu_tokens].cpu() for k in ("q", "k", "v", "z", "b")}
-    cpu_inputs.update(A=d["A"].cpu(), h0=d["h0"].cpu())
     del ws, o, hT, d
     torch.cuda.empty_cache()
-    return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, cpu_inputs
+    return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra
 
 
-def bench_decode(args, kda, torch, KI):
+# decode states stepped in turn, standing in for as many layers of a model:
+# their 4 x 192 MiB exceed the 256 MB Infinity Cache, so each step reads and
+# writes its state in HBM (one layer's state is never cache-resident between
+# its own steps in serving: the other layers' states pass through in between)
+DECODE_STATE_SETS = 4
+
+
+def _decode_loop_times(kda, torch, run, states, reps):
+    """Per-step event times of reps passes over the 16 steps; step i updates
+    states[i % len(states)] in place."""
+    A, steps = run["A"], run["steps"]
+    times = []
+    for _ in range(reps):
+        for i, s in enumerate(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, states[i % len(states)])
+            b.record()
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    return ms
+
+
+def _decode_summary(run, ms):
+    mean = sum(ms) / len(ms)
+    gbs = DECODE_BYTES * run["N"] * run["H"] / (mean * 1e-3) / 1e9
+    return {"steps_timed": len(ms), "ms_per_step_mean": round(mean, 4),
+            "ms_per_step_median": round(ms[len(ms) // 2], 4),
+            "tokens_per_s": round(run["N"] / (mean * 1e-3), 1), "alg_GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_decode(args, kda, torch, KI, cpu=None):
+    """The decode workload (256 sequences x 12 heads, 16 single-token steps).
+    Headline: DECODE_STATE_SETS states stepped in turn (a working set of
+    768 MiB, beyond the Infinity Cache), eagerly and replayed from one
+    captured HIP graph.  Beside it, the same steps on one state in place
+    (cache-warm: its 192 MiB can stay in the Infinity Cache)."""
     case = KI.CONFIGS["decode_256"]
     dev = torch.device("cuda:0")
     run = KI.make_decode(case, device=dev, seed=0)
@@ -244,71 +302,58 @@ def bench_decode(args, kda, torch, KI):
     for s in steps[:2]:                       # warm-up on a scratch copy
         kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, st.clone())
     torch.cuda.synchronize()
-    times = []
-    for rep in range(args.decode_reps):
-        for s in steps:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, st)
-            b.record()
-            times.append((a, b))
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in times]
-    ms.sort()
-    med = ms[len(ms) // 2]
-    mean = sum(ms) / len(ms)
-    units = run["N"] * run["H"]
-    gbs = DECODE_BYTES * units / (mean * 1e-3) / 1e9
-    graph = bench_decode_graph(args, kda, torch, run)
-    fold = bench_fold(args, kda, torch, run, mean)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(run, len(run["steps"]))
-    return {
-        "workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v",
-        "steps_timed": len(ms),
-        "ms_per_step_mean": round(mean, 4),
-        "ms_per_step_median": round(med, 4),
-        "tokens_per_s": round(run["N"] / (mean * 1e-3), 1),
-        "alg_GBps": round(gbs, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "note": "the 192 MiB state can sit in the 256 MB Infinity Cache; alg_GBps counts "
-                "algorithmic bytes and may exceed the HBM rate",
-        "traffic": _decode_traffic(mean),
-        "graph": graph,
-        "cpu_baseline": cpu,
-        "fold": fold,
-    }
+    sets = [st.clone() for _ in range(DECODE_STATE_SETS)]
+    rot = _decode_summary(run, _decode_loop_times(kda, torch, run, sets, args.decode_reps))
+    rot_graph = bench_decode_graph(args, kda, torch, run, DECODE_STATE_SETS)
+    del sets
+    warm_ms = _decode_loop_times(kda, torch, run, [st], args.decode_reps)
+    warm = _decode_summary(run, warm_ms)
+    warm["graph"] = bench_decode_graph(args, kda, torch, run, 1)
+    warm["note"] = ("one 192 MiB state stepped in place: it can stay in the 256 MB Infinity "
+                    "Cache, so alg_GBps may exceed what HBM delivers")
+    fold = bench_fold(args, kda, torch, run, warm["ms_per_step_mean"])
+    out = {"workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v; "
+                       f"{DECODE_STATE_SETS} state sets stepped in turn "
+                       f"({DECODE_STATE_SETS * 192} MiB, beyond the Infinity Cache)"}
+    out.update(rot)
+    out.update({"graph": rot_graph, "cache_warm": warm,
+                "traffic": _decode_traffic(warm["ms_per_step_mean"]),
+                "cpu_baseline": cpu, "fold": fold})
+    return out
 
 
-def bench_decode_graph(args, kda, torch, run):
+def bench_decode_graph(args, kda, torch, run, n_sets):
     """The 16 decode steps captured once into a HIP graph (the launch-bound
     serving loop) and replayed back to back: per-step time without the
-    per-launch host and event overhead of the eager loop.  The first replay's
-    state is compared bit for bit with 16 eager steps from the same state."""
+    per-launch host and event overhead of the eager loop.  Step i updates
+    state set i % n_sets.  The first replay's states are compared bit for bit
+    with 16 eager steps from the same states."""
     A, steps = run["A"], run["steps"]
-    st0 = run["state"].clone()
-    st = st0.clone()
+    st0 = [run["state"].clone() for _ in range(n_sets)]
+    st = [x.clone() for x in st0]
 
-    def loop(state):
-        for s in steps:
-            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, state)
+    def loop(states):
+        for i, s in enumerate(steps):
+            kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], A, states[i % n_sets])
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        loop(st0.clone())                      # warm-up off the capture
+        loop([x.clone() for x in st0])         # warm-up off the capture
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         loop(st)
-    st.copy_(st0)
+    for a, b in zip(st, st0):
+        a.copy_(b)
     torch.cuda.synchronize()
     g.replay()
-    ref = st0.clone()
+    ref = [x.clone() for x in st0]
     loop(ref)
     torch.cuda.synchronize()
-    same = bool(torch.equal(st, ref))
+    same = all(bool(torch.equal(a, b)) for a, b in zip(st, ref))
+    del ref
     reps = max(4, 2 * args.decode_reps)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -607,43 +652,109 @@ def bench_family(args, kda, torch, KI, kda_stages):
     return out
 
 
-def _one_thread():
-    """BLAS pools held to one thread while the oracle is timed (its einsum
-    loops are single-threaded already), so `cores` is what it used."""
+def _cpu_unit(job):
+    """One work unit of the CPU baseline, run in a worker process: the oracle
+    on a slice of a workload.  `job` = (kind, arrays); prefill slices are one
+    head of one sequence, decode slices a block of sequences over all steps."""
+    import numpy as np   # noqa: F401  (the oracle's own dependency)
+    import oracle
     from threadpoolctl import threadpool_limits
-    return threadpool_limits(limits=1)
-
-
-def cpu_baseline(inp, torch):
-    import oracle
-    n = inp["q"].shape[1]
-    with _one_thread():
+    kind, a = job
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.recurrence(inp["q"][0], inp["k"][0], inp["v"][0], inp["z"][0], inp["b"][0],
-                          inp["A"], inp["h0"][0])
-        dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens of long_1m, all 12 heads, fp64 numpy token "
-                      f"recurrence, single thread, {dt:.1f} s"}
+        if kind == "prefill":
+            oracle.recurrence(a["q"], a["k"], a["v"], a["z"], a["b"], a["A"], a["h0"])
+        else:
+            S = a["state"]
+            for st in a["steps"]:
+                _, S = oracle.decode_step(st["q"], st["k"], st["v"], st["z"], st["b"], a["A"], S)
+        return time.perf_counter() - t0
 
 
-def cpu_baseline_decode(run, n_steps: int):
-    """The oracle's decode step timed on the decode workload: its first
-    n_steps steps for all 256 x 12 states, one thread."""
-    import oracle
-    A = run["A"].cpu()
-    S = run["state"].cpu()
-    steps = [{k: run["steps"][i][k].cpu() for k in ("q", "k", "v", "z", "b")}
-             for i in range(n_steps)]
-    with _one_thread():
-        t0 = time.perf_counter()
-        for st in steps:
-            _, S = oracle.decode_step(st["q"], st["k"], st["v"], st["z"], st["b"], A, S)
-        dt = time.perf_counter() - t0
-    return {"value": round(run["N"] * n_steps / dt, 1), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_steps} decode_256 steps, all {run['N']} x {run['H']} "
-                      f"states, fp64 numpy, single thread, {dt:.1f} s"}
+def _warm_unit(_):
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def _under_profiler() -> bool:
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def cpu_baselines(args):
+    """The fp64 oracle timed on the host's cores, before anything touches the
+    GPU: a process pool (spawned workers, one BLAS thread each) over the
+    independent (sequence, head) recurrences of three samples drawn on the
+    host with the workloads' recipe (seed 0): the 1M-token workload's first
+    `cpu_tokens` tokens (all 12 heads), the 4,096-token workload in full (16
+    heads) and the decode workload's 16 steps (256 x 12 states, in blocks of
+    16 sequences).  Returns (prefill baseline, {"prefill_4k": ..., "decode": ...})."""
+    import multiprocessing as mp
+    import torch
+    import kda_inputs as KI
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    host = len(os.sched_getaffinity(0))
+    # at most 16 workers: the host share of one GPU on the boxes this runs on
+    procs = max(1, min(host, 16))
+
+    def f32(x):
+        return x.float().numpy()
+
+    def prefill_jobs(case, T):
+        d = KI.make_prefill(case, T=T, seed=0)
+        return [("prefill", {"q": f32(d["q"][0, :, [h]]), "k": f32(d["k"][0, :, [h]]),
+                             "v": f32(d["v"][0, :, [h]]), "z": f32(d["z"][0, :, [h]]),
+                             "b": f32(d["b"][0, :, [h]]), "A": f32(d["A"][[h]]),
+                             "h0": None if d["h0"] is None else f32(d["h0"][0, [h]])})
+                for h in range(d["H"])]
+
+    long_jobs = prefill_jobs(KI.CONFIGS["long_1m"], args.cpu_tokens)
+    short_jobs = prefill_jobs(KI.CONFIGS["prefill_4k"], None)
+    run = KI.make_decode(KI.CONFIGS["decode_256"], seed=0)
+    blk = 16
+    dec_jobs = []
+    for n0 in range(0, run["N"], blk):
+        sl = slice(n0, n0 + blk)
+        dec_jobs.append(("decode", {"A": f32(run["A"]), "state": f32(run["state"][sl]),
+                                    "steps": [{k: f32(st[k][sl]) for k in ("q", "k", "v", "z", "b")}
+                                              for st in run["steps"]]}))
+    out = {}
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(procs) as pool:
+        pool.map(_warm_unit, range(procs))
+        for name, jobs in (("long", long_jobs), ("short", short_jobs), ("decode", dec_jobs)):
+            t0 = time.perf_counter()
+            busy = sum(pool.map(_cpu_unit, jobs, chunksize=1))
+            out[name] = (time.perf_counter() - t0, busy, min(procs, len(jobs)))
+    wall, busy, used = out["long"]
+    T = args.cpu_tokens
+    full = KI.CONFIGS["long_1m"].T
+    prefill = {"value": round(T / wall, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+               "sample": f"first {T} tokens of the 1M-token recipe (drawn on the host, seed 0), "
+                         f"all 12 heads: fp64 numpy token recurrence, {used} worker processes "
+                         f"(one head each, one BLAS thread each; {host} host CPUs visible), "
+                         f"{wall:.1f} s wall, {busy:.1f} s of worker time; the recurrence is "
+                         f"linear in T, so 2^20 tokens would take about {wall * full / T:.0f} s "
+                         f"(extrapolated, not run)",
+               "blas_threads": 1, "host_cpus": host}
+    sw, sb, su = out["short"]
+    dw, db, du = out["decode"]
+    dc = KI.CONFIGS["decode_256"]
+    extra = {
+        "prefill_4k": {"value": round(4096 / sw, 1), "unit": "tokens/s", "cores": su,
+                       "kind": "oracle", "wall_s": round(sw, 2),
+                       "sample": "the 4,096-token workload in full (16 heads, drawn on the "
+                                 "host), one head per worker"},
+        "decode": {"value": round(dc.N * dc.steps / dw, 1), "unit": "tokens/s", "cores": du,
+                   "kind": "oracle", "wall_s": round(dw, 2),
+                   "sample": f"all {dc.steps} steps of the decode workload (256 x 12 states, "
+                             f"drawn on the host), blocks of {blk} sequences per worker"},
+    }
+    print(f"[bench] CPU oracle on {used} workers: long_1m prefix {T} tokens in {wall:.1f} s; "
+          f"prefill_4k {sw:.1f} s; decode {dw:.1f} s", flush=True)
+    del torch
+    return prefill, extra
 
 
 def main():
@@ -652,7 +763,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-reps", type=int, default=4, help="passes over the 16 decode steps")
-    ap.add_argument("--cpu-tokens", type=int, default=40960)
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens of the 1M-token recipe the CPU oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
@@ -668,6 +780,16 @@ def main():
               "(heads shard across GPUs with no communication, one call per GPU). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baselines spawn their worker processes before anything here
+    # touches the GPU (and never under a profiler, whose preloaded library
+    # may initialise it in every process)
+    cpu, cpu_extra = None, {}
+    if not args.no_cpu_baseline:
+        if _under_profiler():
+            print("[bench] under a profiler: CPU baseline skipped", flush=True)
+        else:
+            cpu, cpu_extra = cpu_baselines(args)
 
     import torch
     import gated_delta_rule_77_amd as kda
@@ -685,16 +807,23 @@ def main():
         print(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written", flush=True)
         del src, dst
 
-    value, ms, roof, extra, cpu_inp = bench_prefill(args, kda, torch, KI)
-    dec = None if args.no_decode else bench_decode(args, kda, torch, KI)
+    value, ms, roof, extra = bench_prefill(args, kda, torch, KI)
+    if cpu_extra:
+        extra["cpu_baseline_prefill_4k"] = cpu_extra["prefill_4k"]
+    dec = None if args.no_decode else bench_decode(args, kda, torch, KI, cpu_extra.get("decode"))
     if dec:
-        print(f"[bench] decode: {dec['ms_per_step_mean']:.4f} ms/step eager, "
+        w = dec["cache_warm"]
+        print(f"[bench] decode, {DECODE_STATE_SETS} state sets in turn: "
+              f"{dec['ms_per_step_mean']:.4f} ms/step eager, "
               f"{dec['graph']['ms_per_step']:.4f} ms/step graph-replayed "
-              f"(replay equals eager: {dec['graph']['replay_equals_eager']})", flush=True)
+              f"({dec['hbm_frac']:.3f} / {dec['graph']['hbm_frac']:.3f} of HBM peak; replay equals "
+              f"eager: {dec['graph']['replay_equals_eager']}); one state, cache-warm: "
+              f"{w['ms_per_step_mean']:.4f} eager, {w['graph']['ms_per_step']:.4f} replayed",
+              flush=True)
     layer = None
     if not args.no_layer:
         layer = bench_layer(args, kda, torch, KI, extra["call_ms_events"],
-                            dec["ms_per_step_mean"] if dec else float("nan"))
+                            dec["cache_warm"]["ms_per_step_mean"] if dec else float("nan"))
     family = None
     if not args.no_family:
         family = bench_family(args, kda, torch, KI, {"intra": extra["kernels_ms"]["intra"],
@@ -703,7 +832,6 @@ def main():
     print(f"[bench] prefill_4k: {short['ms_per_call_eager']:.4f} ms/call eager, "
           f"{short['ms_per_call_graph']:.4f} ms/call graph-replayed "
           f"(replay equals eager: {short['replay_equals_eager']})", flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_inp, torch)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

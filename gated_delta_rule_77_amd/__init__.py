@@ -164,15 +164,21 @@ def _req(t, name, dtype=None, device=None):
 
 
 def _workspace(workspace, need: int, device):
-    """The caller's workspace (a contiguous uint8 tensor on `device`, at least
-    `need` bytes; the library also requires 256-byte alignment), or a fresh one
-    when none is given or it is too small."""
+    """The caller's workspace, or a fresh one when the caller passes none.
+
+    A caller who passes a workspace owns the call's scratch memory and gets no
+    allocation: it must be a contiguous uint8 tensor on `device`, at least
+    `need` bytes long and 256-byte aligned, or the call raises KdaError before
+    anything is enqueued."""
     torch = _torch()
-    if workspace is not None:
-        _req(workspace, "workspace", torch.uint8, device)
-        if workspace.numel() >= need:
-            return workspace
-    return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    _req(workspace, "workspace", torch.uint8, device)
+    if workspace.numel() < need:
+        raise KdaError(f"workspace holds {workspace.numel()} bytes; this call needs {need}")
+    if workspace.data_ptr() % 256:
+        raise KdaError("workspace must be 256-byte aligned")
+    return workspace
 
 
 def _stream(device) -> int:

@@ -12,6 +12,9 @@ q, k of the input recipe, and the MFMA operands round q and k (scaled by
 their decay factors) to bf16, which alone moves that small dot product by
 about 1% of itself (reproduced by a CPU emulation of the rounding points).
 """
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -19,6 +22,20 @@ import oracle
 
 TOL_F32 = 1e-4
 TOL_BF16 = 1e-2
+
+
+def report(suite: str, tag: str, **errs) -> None:
+    """Print a case's measured errors; with KDA_PARITY_LOG set, also append
+    them as one JSON line to that file, so that a GPU run keeps the margin of
+    every case against its bar (tests/golden/parity_margins.py summarises the
+    log)."""
+    print(f"[{suite}] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    path = os.environ.get("KDA_PARITY_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a") as f:
+            f.write(json.dumps({"suite": suite, "test": test, "case": tag,
+                                "errors": {k: float(v) for k, v in errs.items()}}) + "\n")
 
 
 def rel_err(got, ref, scale=None) -> float:

@@ -136,6 +136,30 @@ def test_binding_refuses_a_host_workspace():
         kda._workspace(torch.zeros(1024, dtype=torch.uint8), 512, torch.device("cuda", 0))
 
 
+def test_binding_raises_on_a_short_or_misaligned_workspace(monkeypatch):
+    """A caller who passes a workspace gets no allocation: one that is too
+    small or not 256-byte aligned raises KdaError, and nothing is allocated in
+    its place (the device checks of _req are bypassed so that a host tensor
+    can stand in on a machine without a GPU)."""
+    import torch
+    import gated_delta_rule_77_amd as kda
+    monkeypatch.setattr(kda, "_req", lambda t, *a, **k: t)
+
+    def no_alloc(*a, **k):
+        raise AssertionError("the binding allocated a workspace")
+
+    buf = torch.zeros(4096 + 256, dtype=torch.uint8)
+    off = (-buf.data_ptr()) % 256
+    aligned = buf[off:off + 4096]
+    monkeypatch.setattr(torch, "empty", no_alloc)
+    dev = torch.device("cuda", 0)
+    with pytest.raises(kda.KdaError, match="needs 8192"):
+        kda._workspace(aligned, 8192, dev)
+    with pytest.raises(kda.KdaError, match="aligned"):
+        kda._workspace(buf[off + 16:off + 16 + 1024], 512, dev)
+    assert kda._workspace(aligned, 4096, dev) is aligned
+
+
 def test_recurrent_fold_rejects_bad_arguments(L):
     fn = L.kda_recurrent_fold
     fn.restype = ctypes.c_int

@@ -13,7 +13,7 @@ import torch
 
 import kda_inputs as KI
 import oracle
-from kda_testutil import TOL_BF16, TOL_F32, rel_err
+from kda_testutil import report, TOL_BF16, TOL_F32, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def kda():
 
 
 def _report(tag, **errs):
-    print(f"[dplr] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    report("dplr", tag, **errs)
 
 
 def _dev(d):

@@ -13,7 +13,7 @@ import torch
 
 import kda_inputs as KI
 import oracle
-from kda_testutil import TOL_BF16, TOL_F32, rel_err
+from kda_testutil import TOL_BF16, TOL_F32, rel_err, report
 
 pytestmark = pytest.mark.gpu
 
@@ -94,8 +94,7 @@ def _check_layer(kda, d, tol, tag):
     for (n, s, L), (ry, rS, rcs, ro) in zip(_seqs(d), ref):
         ey = y_within_bar(yf[s:s + L], ry, ro, gf[s:s + L], d["norm_w"], tol) if L > 0 else 0.0
         eS = rel_err(hT[n], rS)
-        print(f"[parity] layer {tag} seq {n} len {L}: y error / bar = {ey:.3f}, hT={eS:.3e}",
-              flush=True)
+        report("layer", f"{tag} seq {n} len {L}", y_err_over_bar=ey, hT=eS)
         assert ey <= 1.0 and eS <= tol
         # the carried convolution state is a copy of inputs: exact
         assert np.array_equal(csT[n].double().cpu().numpy(), rcs)
@@ -180,8 +179,7 @@ def test_layer_step_vs_oracle(kda, dtype, d):
                                                with_o=True)
         ey = y_within_bar(y[n], ry, ro, data["gate"][n], data["norm_w"], tol)
         eS = rel_err(st[n], rS)
-        print(f"[parity] layer step {dtype} d={d} seq {n}: y error / bar = {ey:.3f}, S={eS:.3e}",
-              flush=True)
+        report("layer", f"step {dtype} d={d} seq {n}", y_err_over_bar=ey, S=eS)
         assert ey <= 1.0 and eS <= tol
         assert np.array_equal(cs[n].double().cpu().numpy(), rcs)
 

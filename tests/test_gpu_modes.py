@@ -14,7 +14,7 @@ import torch
 
 import kda_inputs as KI
 import oracle
-from kda_testutil import TOL_BF16, TOL_F32, rel_err, to_dev
+from kda_testutil import report, TOL_BF16, TOL_F32, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def kda():
 
 
 def _report(tag, **errs):
-    print(f"[modes] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    report("modes", tag, **errs)
 
 
 def _gpu(kda, d, mode, chunk):

@@ -11,7 +11,7 @@ import torch
 
 import kda_inputs as KI
 import oracle
-from kda_testutil import TOL_BF16, TOL_F32, gpu_prefill, oracle_prefill, rel_err, to_dev
+from kda_testutil import report, TOL_BF16, TOL_F32, gpu_prefill, oracle_prefill, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def _case(name, **over):
 
 
 def _report(tag, **errs):
-    print(f"[parity] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    report("parity", tag, **errs)
 
 
 # --------------------------------------------------------------- named configs
