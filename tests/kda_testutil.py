@@ -27,7 +27,7 @@ TOL_BF16 = 1e-2
 def report(suite: str, tag: str, **errs) -> None:
     """Print a case's measured errors; with KDA_PARITY_LOG set, also append
     them as one JSON line to that file, so that a GPU run keeps the margin of
-    every case against its bar (tests/golden/parity_margins.py summarises the
+    every case against its bar (tests/parity_margins.py summarises the
     log)."""
     print(f"[{suite}] {tag}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
     path = os.environ.get("KDA_PARITY_LOG")
