@@ -22,14 +22,17 @@ void decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     float* S = state + (size_t)nh * DK * DV;
     __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
-    // the state stream is the cost of this kernel: issue its loads first
+    // the token's few inputs first, then the state stream that is the cost
+    // of this kernel; the gate arithmetic waits on the former alone
+    TokenIn<DK, DV> in;
+    load_token<DK, DV, Tin, true, MODE>(in, k + (size_t)nh * DK, v + (size_t)nh * DV,
+                                        MODE == kModeDeltaNet ? z : z + (size_t)nh * DK, bl[nh],
+                                        q + (size_t)nh * DK);
+    const float ea = MODE == kModeDeltaNet ? 1.f : expf(A[nh % H]);
     float4 Sv[16];
     load_state<DK, DV>(Sv, S);
-    const float ea = MODE == kModeDeltaNet ? 1.f : expf(A[nh % H]);
-    kda_token_step<DK, DV, Tin, true, MODE>(Sv, k + (size_t)nh * DK, v + (size_t)nh * DV,
-                                      MODE == kModeDeltaNet ? z : z + (size_t)nh * DK, bl[nh], ea, q + (size_t)nh * DK,
-                                      o + (size_t)nh * DV, s_al, s_k, s_q, s_red, s_qk);
-    store_state<DK, DV>(Sv, S);
+    kda_token_step<DK, DV, Tin, true, MODE, true>(Sv, in, ea, o + (size_t)nh * DV, s_al, s_k, s_q,
+                                                  s_red, s_qk, S);
 }
 
 // Replay fold ([K3-ATTN §6.2], ReplaySSM): advance each (sequence, head)
@@ -56,9 +59,11 @@ void fold_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v, const flo
     for (int t = 0; t < cnt; t++) {
         const size_t tok = ((size_t)n * W + t) * H + h;
         if (t > 0) __syncthreads();     // the previous step's readers of s_al, s_k, s_red are done
-        kda_token_step<DK, DV, Tin, false>(Sv, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
-                                           ea, (const Tin*)nullptr, (Tin*)nullptr, s_al, s_k,
-                                           (float*)nullptr, s_red);
+        TokenIn<DK, DV> in;
+        load_token<DK, DV, Tin, false>(in, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
+                                       (const Tin*)nullptr);
+        kda_token_step<DK, DV, Tin, false>(Sv, in, ea, (Tin*)nullptr, s_al, s_k, (float*)nullptr,
+                                           s_red);
     }
     store_state<DK, DV>(Sv, S);
 }
@@ -85,8 +90,10 @@ void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     for (int t = 0; t < W; t++) {
         const size_t tok = ((size_t)n * W + t) * H + h;
         if (t > 0) __syncthreads();     // the previous step's readers of the LDS vectors are done
-        kda_token_step<DK, DV, Tin, true>(Sv, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok], ea,
-                                          q + tok * DK, o + tok * DV, s_al, s_k, s_q, s_red, s_qk);
+        TokenIn<DK, DV> in;
+        load_token<DK, DV, Tin, true>(in, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
+                                      q + tok * DK);
+        kda_token_step<DK, DV, Tin, true>(Sv, in, ea, o + tok * DV, s_al, s_k, s_q, s_red, s_qk);
     }
 }
 

@@ -261,8 +261,9 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
         s_in[1][i] *= inv_k;
     }
     __syncthreads();
-    kda_token_step<D, D, float, true>(Sv, s_in[1], s_in[2], z + (size_t)nh * D, bl[nh],
-                                      expf(A[h]), s_in[0], s_o, s_al, s_k, s_q, s_red, s_qk);
+    TokenIn<D, D> in;
+    load_token<D, D, float, true>(in, s_in[1], s_in[2], z + (size_t)nh * D, bl[nh], s_in[0]);
+    kda_token_step<D, D, float, true>(Sv, in, expf(A[h]), s_o, s_al, s_k, s_q, s_red, s_qk);
     __syncthreads();
     float so = 0.f;
     for (int i = tid; i < D; i += NT) so = __builtin_fmaf(s_o[i], s_o[i], so);
