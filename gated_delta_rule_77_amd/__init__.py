@@ -13,6 +13,7 @@ Names follow the C ABI in include/kda.h:
     kda_recurrent_fold(k, v, g, beta, A, n_accept, state)    (state updated in place)
     kda_layer_fwd(q_in, k_in, v_in, conv_w, g, beta, A, gate, norm_w, ...) -> (y, hT, conv_state)
     kda_layer_step(q_in, k_in, v_in, conv_w, conv_state, g, beta, A, state, gate, norm_w) -> y
+    kda_chunk_fwd_noalloc(q, k, v, g, beta, A, o, final_state=None, ...) -> (o, hT)
     kda_chunk_fwd_debug(...) -> (o, hT, intermediates)
     kda_chunk_fwd_mode(q, k, v, g, beta, A, mode, ...) -> (o, hT)  ("kda", "gla", "deltanet")
     kda_recurrent_step_mode(q, k, v, g, beta, A, state, mode) -> o
@@ -33,7 +34,7 @@ __all__ = [
     "kda_chunk_fwd_debug", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_supported",
     "kda_recurrent_step_supported", "kda_chunk_fwd_mode", "kda_recurrent_step_mode", "MODES",
     "kda_dplr_chunk_fwd", "kda_dplr_recurrent_step", "kda_dplr_chunk_fwd_workspace_bytes",
-    "EXPORTED_SYMBOLS",
+    "kda_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,7 +48,10 @@ EXPORTED_SYMBOLS = (
     "kda_layer_fwd_workspace_bytes", "kda_layer_fwd", "kda_layer_step", "kda_chunk_fwd_mode",
     "kda_recurrent_step_mode", "kda_dplr_chunk_fwd_workspace_bytes", "kda_dplr_chunk_fwd",
     "kda_dplr_chunk_fwd_timed", "kda_dplr_recurrent_step", "kda_recurrent_verify",
+    "kda_chunk_fwd_noalloc",
 )
+# bytes of the per-GPU scratch array behind kda_chunk_fwd_noalloc (include/kda.h)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 # family modes of kda_chunk_fwd_mode / kda_recurrent_step_mode (kda_mode_t)
 MODES = {"kda": 0, "gla": 1, "deltanet": 2}
 
@@ -92,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd.argtypes = chunk_args + [vp]
     L.kda_chunk_fwd_debug.restype = i
     L.kda_chunk_fwd_debug.argtypes = chunk_args + [f, f, vp]
+    L.kda_chunk_fwd_noalloc.restype = i
+    L.kda_chunk_fwd_noalloc.argtypes = chunk_args[:18] + [vp]
     L.kda_chunk_fwd_timed.restype = i
     L.kda_chunk_fwd_timed.argtypes = chunk_args + [ctypes.POINTER(vp), i, vp]
     L.kda_recurrent_step.restype = i
@@ -244,6 +250,29 @@ def kda_chunk_fwd(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,
     Returns (o [B, T, H, dv], final_state [N, H, dk, dv] fp32 or None)."""
     return _chunk(q, k, v, g, beta, A, initial_state, cu_seqlens, chunk_size,
                   output_final_state, workspace, debug=False)
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, A, o, final_state=None, initial_state=None,
+                          cu_seqlens=None, chunk_size: int = 64):
+    """kda_chunk_fwd without a workspace and without allocating: the caller
+    passes the output o [B, T, H, dv] (dtype of q) and, if wanted, the final
+    state [N, H, dk, dv] fp32; the library's per-GPU scratch array serves as
+    the workspace (calls beyond its size raise KdaError: KDA_ERR_SCRATCH).
+    Calls that overlap on one GPU race on that array.  Returns (o, final_state)."""
+    torch = _torch()
+    B, T, H, dk, dv, N, dev, dt = _prefill_args(q, k, v, g, beta, A, initial_state, cu_seqlens)
+    _req(o, "o", dt, dev)
+    if o.shape != (B, T, H, dv):
+        raise ValueError(f"o must be [{B}, {T}, {H}, {dv}]")
+    if final_state is not None:
+        _req(final_state, "final_state", torch.float32, dev)
+        if final_state.shape != (N, H, dk, dv):
+            raise ValueError(f"final_state must be [{N}, {H}, {dk}, {dv}]")
+    _check(lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                                       _ptr(initial_state), _ptr(cu_seqlens), B, T, H, dk, dv, N,
+                                       chunk_size, _dtype_code(q), _ptr(o), _ptr(final_state),
+                                       _stream(dev)), "kda_chunk_fwd_noalloc")
+    return o, final_state
 
 
 def kda_chunk_fwd_debug(q, k, v, g, beta, A, initial_state=None, cu_seqlens=None,

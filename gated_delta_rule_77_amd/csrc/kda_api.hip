@@ -3,9 +3,42 @@
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
 
+#include <mutex>
+
 using namespace kda;
 
+// Scratch memory of kda_chunk_fwd_noalloc, for callers that cannot allocate:
+// a file-scope device array, so that every GPU the library runs on holds its
+// own copy from the module's load until the process ends.  In host code the
+// name `scratch` is a host-side stand-in, never a device address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress (noalloc_scratch
+// below) and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// per device: the address of that device's `scratch`, looked up once with
+// the device current (guarded by a mutex; later calls only read the table)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
@@ -124,6 +157,9 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: shape or dtype not supported";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+        case KDA_ERR_SCRATCH:
+            return "KDA_ERR_SCRATCH: the call needs more scratch than kda_chunk_fwd_noalloc holds "
+                   "(KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -161,6 +197,23 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
                        chunk, dtype, o, hT, workspace, workspace_bytes, nullptr, nullptr, nullptr, 0,
                        stream);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* g_logits, const float* beta_logits, const float* A,
+                                   const float* h0, const int* cu_seqlens, int B, int T, int H,
+                                   int dk, int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                   float* hT, void* stream) {
+    // the workspace the same call of kda_chunk_fwd would need (0: the sizes
+    // are invalid or unsupported, which run_prefill reports before it looks
+    // at the scratch)
+    const size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, chunk, dtype);
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && N > 0 && noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+    return run_prefill(q, k, v, g_logits, beta_logits, A, h0, cu_seqlens, B, T, H, dk, dv, N,
+                       chunk, dtype, o, hT, ws, ws ? (size_t)KDA_NOALLOC_SCRATCH_BYTES : 0,
+                       nullptr, nullptr, nullptr, 0, stream);
 }
 
 kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const void* v,

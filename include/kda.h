@@ -38,7 +38,9 @@
  *     non-OK status means nothing was enqueued, except KDA_ERR_HIP, which
  *     reports a failed launch.  No exception crosses the ABI.
  *   - The library holds no mutable global state: calls on different streams
- *     may run concurrently if their buffers do not overlap.
+ *     may run concurrently if their buffers do not overlap.  The one
+ *     exception is kda_chunk_fwd_noalloc, whose scratch is a per-GPU array
+ *     inside the library (see its declaration).
  *   - No query scale is applied: o = S^T q exactly (no formula on the pages
  *     carries one); a caller wanting 1/sqrt(d_k) scales q first.  q and k are
  *     used as given (the pages normalise them upstream, [LA-KDA §5.3]).
@@ -64,7 +66,9 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative or inconsistent size   */
     KDA_ERR_UNSUPPORTED = 2,   /* (d_k, d_v, chunk, dtype) not compiled in      */
     KDA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required     */
-    KDA_ERR_HIP = 4            /* a kernel launch failed                         */
+    KDA_ERR_HIP = 4,           /* a kernel launch failed                         */
+    KDA_ERR_SCRATCH = 5        /* kda_chunk_fwd_noalloc: the call needs more     */
+                               /* scratch than KDA_NOALLOC_SCRATCH_BYTES        */
 } kda_status_t;
 
 /* Element type of q, k, v and o.  Gate logits, beta logits, A and states are
@@ -142,6 +146,34 @@ KDA_API kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
                            int B, int T, int H, int dk, int dv, int N, int chunk,
                            kda_dtype_t dtype, void* o, float* hT,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, layouts, supported shapes, results and errors, without the
+ * workspace.  Its scratch memory is a device array inside the library,
+ * KDA_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held from the
+ * library's first use on that GPU until the process ends; the call allocates
+ * and frees nothing.
+ * Limit: a call whose kda_chunk_fwd_workspace_bytes exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_SCRATCH and enqueues nothing
+ * (on the MFMA path about 70,000 token-heads fit: e.g. 4,096 tokens x 16
+ * heads; use kda_chunk_fwd with a workspace beyond that).
+ * Sharing: every call on one GPU uses that GPU's one array.  Calls that can
+ * overlap on one GPU (on different streams, or from different host threads)
+ * race on it and give undefined results: serialise them.  Nothing in the
+ * array needs to start at zero; each call overwrites what it reads.
+ * `stream` must belong to the current device (hipGetDevice) of the calling
+ * thread; the first call on a device looks up that device's array once
+ * (KDA_ERR_HIP if the lookup fails).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+KDA_API kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                           const float* g_logits, const float* beta_logits,
+                                           const float* A, const float* h0,
+                                           const int* cu_seqlens, int B, int T, int H, int dk,
+                                           int dv, int N, int chunk, kda_dtype_t dtype, void* o,
+                                           float* hT, void* stream);
 
 /*
  * Diagnostic variant of kda_chunk_fwd: identical results, plus per-chunk

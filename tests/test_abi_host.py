@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code, word in [(0, "KDA_OK"), (1, "INVALID"), (2, "UNSUPPORTED"), (3, "WORKSPACE"), (4, "HIP")]:
+    for code, word in [(0, "KDA_OK"), (1, "INVALID"), (2, "UNSUPPORTED"), (3, "WORKSPACE"), (4, "HIP"),
+                       (5, "SCRATCH")]:
         assert word in L.kda_status_string(code).decode()
     assert L.kda_status_string(99)
 
@@ -80,6 +81,25 @@ def _chunk(L, **kw):
 
 
 FAKE = 1 << 20   # never dereferenced: validation fails before any launch
+
+
+def test_noalloc_rejects_before_any_device_call(L):
+    """kda_chunk_fwd_noalloc checks the call's workspace need against its
+    scratch array (and the arguments) on the host: a call beyond the array
+    returns KDA_ERR_SCRATCH and an invalid one KDA_ERR_INVALID_ARG, both
+    before any HIP call (so this runs without a GPU)."""
+    import gated_delta_rule_77_amd as kda
+    fn = L.kda_chunk_fwd_noalloc
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn.restype = i
+    fn.argtypes = [vp] * 8 + [i] * 8 + [vp, vp, vp]
+    big = L.kda_chunk_fwd_workspace_bytes(1, 8192, 12, 128, 128, 1, 64, 1)
+    assert big > kda.NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 6 + [None, None]
+    assert fn(*args, 1, 8192, 12, 128, 128, 1, 64, 1, FAKE, FAKE, None) == 5
+    assert fn(*args, 1, 64, 0, 16, 16, 1, 16, 0, FAKE, FAKE, None) == 1      # H = 0
+    assert fn(*args, 1, 64, 2, 96, 96, 1, 64, 1, FAKE, FAKE, None) == 2      # unsupported shape
+    assert fn(*args, 1, 64, 2, 16, 16, 0, 16, 0, FAKE, FAKE, None) == 1      # N != B
 
 
 def test_chunk_fwd_rejects_bad_arguments(L):
