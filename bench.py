@@ -560,11 +560,34 @@ def bench_short_prefill(args, kda, torch, KI):
     torch.cuda.synchronize()
     same = bool(torch.equal(o_g, o_ref) and torch.equal(h_g, h_ref))
     graph = timed(g.replay, reps)
+    # the stages of the same call, from events the library records between
+    # its launches (the events themselves add a little to the call)
+    L = kda.lib()
+    h = _hip()
+    evs = [[_event(h) for _ in range(6)] for _ in range(reps)]
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    h0 = d["h0"].data_ptr() if d["h0"] is not None else None
+    for row in evs:
+        arr = (ctypes.c_void_p * 6)(*[e.value for e in row])
+        rc = L.kda_chunk_fwd_timed(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                                   d["z"].data_ptr(), d["b"].data_ptr(), d["A"].data_ptr(), h0, None,
+                                   B, T, H, dk, dv, N, C, 1, o.data_ptr(), hT.data_ptr(),
+                                   ws.data_ptr(), ws.numel(), arr, 6, stream)
+        if rc != 0:
+            raise RuntimeError(L.kda_status_string(rc).decode())
+    torch.cuda.synchronize()
+    stages = _stage_ms(h, evs)
+    for row in evs:
+        for e in row:
+            h.hipEventDestroy(e)
     tok = B * T
     return {"workload": "prefill_4k: B=1, H=16, T=4096, d_k=d_v=128, chunk=64, bf16, seed 0",
             "ms_per_call_eager": round(eager, 4), "tokens_per_s_eager": round(tok / (eager * 1e-3), 1),
             "ms_per_call_graph": round(graph, 4), "tokens_per_s_graph": round(tok / (graph * 1e-3), 1),
-            "replay_equals_eager": same}
+            "replay_equals_eager": same,
+            "stages_ms_with_events": {k: round(v, 4) for k, v in stages.items()}}
 
 
 def bench_family(args, kda, torch, KI, kda_stages):
@@ -831,7 +854,8 @@ def main():
     short = bench_short_prefill(args, kda, torch, KI)
     print(f"[bench] prefill_4k: {short['ms_per_call_eager']:.4f} ms/call eager, "
           f"{short['ms_per_call_graph']:.4f} ms/call graph-replayed "
-          f"(replay equals eager: {short['replay_equals_eager']})", flush=True)
+          f"(replay equals eager: {short['replay_equals_eager']}); stages with events (ms): "
+          + ", ".join(f"{k} {v:.4f}" for k, v in short["stages_ms_with_events"].items()), flush=True)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -1093,6 +1093,22 @@ void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ 
 #pragma unroll
             for (int e = 0; e < 4; e++) sSt[(32 * w + 16 * b + 4 * g4 + e) * 17 + n16] = x[b][e];
         __syncthreads();
+        // the contraction over 128 rows in four independent quarters (four
+        // short accumulation chains per tile instead of one of 32), summed
+        // in a fixed order
+        f32x4 part[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            const float* Ab = sM + (32 * w + 16 * b + n16) * 132;
+#pragma unroll
+            for (int qk = 0; qk < 4; qk++) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 8 * qk; ks < 8 * qk + 8; ks++)
+                    acc = mfma_f32(Ab[4 * ks + g4], sSt[(4 * ks + g4) * 17 + n16], acc);
+                part[b][qk] = acc;
+            }
+        }
 #pragma unroll
         for (int b = 0; b < 2; b++) {
             f32x4 acc;
@@ -1101,11 +1117,7 @@ void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ 
                 const int row = 32 * w + 16 * b + 4 * g4 + e;
                 acc[e] = RM[(size_t)row * 256 + col];
             }
-            const float* Ab = sM + (32 * w + 16 * b + n16) * 132;
-#pragma unroll 8
-            for (int ks = 0; ks < 32; ks++)
-                acc = mfma_f32(Ab[4 * ks + g4], sSt[(4 * ks + g4) * 17 + n16], acc);
-            x[b] = acc;
+            x[b] = acc + ((part[b][0] + part[b][1]) + (part[b][2] + part[b][3]));
         }
     }
 }

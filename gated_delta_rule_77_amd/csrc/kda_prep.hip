@@ -194,6 +194,95 @@ void prep_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, i
         for (int g = t; g < seg_cap; g += 1024) fill_seg(g, N, nseg_total, per, seqs, seqsegs, segs);
 }
 
+// Sum and maximum over the 64 lanes of a wave, returned to every lane.
+__device__ __forceinline__ long long wave_sum64(long long x) {
+    for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+    for (int m = 32; m > 0; m >>= 1) x = max(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
+// The same bookkeeping for batches of at most 64 sequences: wave 0 (lane s =
+// sequence s) does every scan, reduction and the search for the segment
+// length with cross-lane operations, and leaves the per-sequence tables in
+// LDS; after one barrier the whole workgroup fills the chunk and segment
+// tables.  Same results as prep_kernel.
+__global__ __launch_bounds__(1024)
+void prep_small_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, int C, int cap,
+                       int min_seg, int seg_target, int seg_cap, int* __restrict__ hdr,
+                       int2* __restrict__ seqs, int2* __restrict__ seqsegs,
+                       int4* __restrict__ chunks, int4* __restrict__ segs)
+{
+    __shared__ int2 s_seqs[64], s_seqsegs[64];
+    __shared__ int s_hdr[3];
+    const int t = threadIdx.x;
+    if (t < 64) {
+        const int s = t;
+        int start = 0, len = 0;
+        if (s < N) seq_extent(cu, s, Tfix, Ttot, start, len);
+        const long long nch = (len + C - 1) / C;
+        long long incl = nch;
+        for (int d = 1; d < 64; d <<= 1) {
+            const long long y = __shfl_up(incl, d, 64);
+            if (s >= d) incl += y;
+        }
+        const long long carry = __shfl(incl, 63, 64);
+        const int f = (int)min(incl - nch, (long long)cap);
+        const int nc = (int)max(0LL, min(nch, (long long)cap - f));
+        if (s < N) {
+            s_seqs[s] = make_int2(f, nc);
+            seqs[s] = make_int2(f, nc);
+        }
+        auto count = [&](long long per) { return wave_sum64(s < N ? (nc + per - 1) / per : 0); };
+        int per = 0;
+        long long carry_seg = 0;
+        if (min_seg > 0) {
+            const int max_nc = wave_max(s < N ? nc : 0);
+            const long long total = min(carry, (long long)cap);
+            const long long nonempty = count(max(max_nc, 1));
+            const long long target = max((long long)seg_target, nonempty);
+            long long lo = max((long long)min_seg, (total + target - 1) / target);
+            long long hi = target > nonempty ? (total + (target - nonempty) - 1) / (target - nonempty)
+                                             : (long long)max_nc;
+            hi = max(hi, lo);
+            if (count(lo) <= target) hi = lo;
+            while (lo < hi) {
+                const long long mid = lo + (hi - lo) / 2;
+                if (count(mid) <= target) hi = mid; else lo = mid + 1;
+            }
+            per = (int)lo;
+            const long long nseg = s < N ? (nc + per - 1) / per : 0;
+            long long sincl = nseg;
+            for (int d = 1; d < 64; d <<= 1) {
+                const long long y = __shfl_up(sincl, d, 64);
+                if (s >= d) sincl += y;
+            }
+            carry_seg = __shfl(sincl, 63, 64);
+            const int fs = (int)min(sincl - nseg, (long long)seg_cap);
+            const int ns = (int)max(0LL, min(nseg, (long long)seg_cap - fs));
+            if (s < N) {
+                s_seqsegs[s] = make_int2(fs, ns);
+                seqsegs[s] = make_int2(fs, ns);
+            }
+        }
+        if (s == 0) {
+            s_hdr[0] = (int)min(carry, (long long)cap);
+            s_hdr[1] = (int)min(carry_seg, (long long)seg_cap);
+            s_hdr[2] = per;
+            hdr[0] = s_hdr[0];
+            hdr[1] = s_hdr[1];
+            hdr[2] = per;
+        }
+    }
+    __syncthreads();
+    const int total = s_hdr[0], nseg_total = s_hdr[1], per = s_hdr[2];
+    for (int c = t; c < cap; c += 1024) fill_chunk(c, cu, N, Tfix, Ttot, C, total, s_seqs, chunks);
+    if (min_seg > 0)
+        for (int g = t; g < seg_cap; g += 1024) fill_seg(g, N, nseg_total, per, s_seqs, s_seqsegs, segs);
+}
+
 hipError_t launch_prep(const ChunkArgs& a) {
     int* hdr = reinterpret_cast<int*>(a.ws);
     int4* chunks = reinterpret_cast<int4*>(a.ws + a.L.off_chunks);
@@ -201,9 +290,14 @@ hipError_t launch_prep(const ChunkArgs& a) {
     int2* seqsegs = reinterpret_cast<int2*>(a.ws + a.L.off_seqsegs);
     int4* segs = reinterpret_cast<int4*>(a.ws + a.L.off_segs);
     const int Ttot = a.cu ? a.T : a.B * a.T;
-    hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, a.stream,
-                       a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, seg_target(a.H),
-                       a.L.seg_cap, hdr, seqs, seqsegs, chunks, segs);
+    if (a.N <= 64)
+        hipLaunchKernelGGL(prep_small_kernel, dim3(1), dim3(1024), 0, a.stream,
+                           a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, seg_target(a.H),
+                           a.L.seg_cap, hdr, seqs, seqsegs, chunks, segs);
+    else
+        hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, a.stream,
+                           a.cu, a.N, a.T, Ttot, a.C, a.L.cap, a.L.seg_chunks, seg_target(a.H),
+                           a.L.seg_cap, hdr, seqs, seqsegs, chunks, segs);
     return hipGetLastError();
 }
 
