@@ -311,7 +311,7 @@ def bench_decode(args, kda, torch, KI, cpu=None):
     warm["graph"] = bench_decode_graph(args, kda, torch, run, 1)
     warm["note"] = ("one 192 MiB state stepped in place: it can stay in the 256 MB Infinity "
                     "Cache, so alg_GBps may exceed what HBM delivers")
-    fold = bench_fold(args, kda, torch, run, warm["ms_per_step_mean"])
+    fold = bench_fold(args, kda, torch, run, rot["ms_per_step_mean"])
     out = {"workload": "decode_256: N=256 sequences, H=12, d=128, fp32 state, bf16 q/k/v; "
                        f"{DECODE_STATE_SETS} state sets stepped in turn "
                        f"({DECODE_STATE_SETS * 192} MiB, beyond the Infinity Cache)"}
@@ -396,17 +396,18 @@ def bench_fold(args, kda, torch, run, step_ms):
     win = {key: torch.stack([s[key] for s in steps], dim=1).contiguous() for key in ("k", "v", "z", "b")}
     N, H = run["N"], run["H"]
     n_acc = torch.full((N,), W, dtype=torch.int32, device=win["k"].device)
-    st = run["state"].clone()
+    # the state sets of the decode headline, one per call in turn
+    sts = [run["state"].clone() for _ in range(DECODE_STATE_SETS)]
     A = run["A"]
-    for _ in range(2):
-        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, st)
+    for i in range(2):
+        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, sts[i % len(sts)])
     torch.cuda.synchronize()
     times = []
-    for _ in range(max(4, args.decode_reps * 4)):
+    for i in range(max(4, args.decode_reps * 4)):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, st)
+        kda.kda_recurrent_fold(win["k"], win["v"], win["z"], win["b"], A, n_acc, sts[i % len(sts)])
         b.record()
         times.append((a, b))
     torch.cuda.synchronize()
@@ -417,22 +418,23 @@ def bench_fold(args, kda, torch, run, step_ms):
     # the verify pass over the same window: outputs of every draft token from
     # the checkpoint (read once, not written)
     qw = torch.stack([s["q"] for s in steps], dim=1).contiguous()
-    for _ in range(2):
-        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, st)
+    for i in range(2):
+        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, sts[i % len(sts)])
     torch.cuda.synchronize()
     vt = []
-    for _ in range(max(4, args.decode_reps * 4)):
+    for i in range(max(4, args.decode_reps * 4)):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, st)
+        kda.kda_recurrent_verify(qw, win["k"], win["v"], win["z"], win["b"], A, sts[i % len(sts)])
         b.record()
         vt.append((a, b))
     torch.cuda.synchronize()
     vms = sum(a.elapsed_time(b) for a, b in vt) / len(vt)
     v_unit = 128 * 128 * 4 + W * (FOLD_TOKEN_BYTES + 2 * 128 + 2 * 128)   # state read + window in (+q) + o out
     return {
-        "workload": f"decode_256 states, window of {W} draft tokens per sequence, all accepted",
+        "workload": f"decode_256 states ({DECODE_STATE_SETS} sets, one per call in turn), window of "
+                    f"{W} draft tokens per sequence, all accepted",
         "calls_timed": len(ms),
         "ms_per_call_mean": round(mean, 4),
         "tokens_per_s": round(N * W / (mean * 1e-3), 1),

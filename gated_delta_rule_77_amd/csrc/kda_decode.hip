@@ -54,18 +54,18 @@ void fold_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v, const flo
     __shared__ float s_al[DK], s_k[DK];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
     float4 Sv[16];
-    load_state<DK, DV>(Sv, S);
+    load_state<DK, DV, false>(Sv, S);
     const float ea = expf(A[h]);
     for (int t = 0; t < cnt; t++) {
         const size_t tok = ((size_t)n * W + t) * H + h;
         if (t > 0) __syncthreads();     // the previous step's readers of s_al, s_k, s_red are done
         TokenIn<DK, DV> in;
-        load_token<DK, DV, Tin, false>(in, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
-                                       (const Tin*)nullptr);
-        kda_token_step<DK, DV, Tin, false>(Sv, in, ea, (Tin*)nullptr, s_al, s_k, (float*)nullptr,
-                                           s_red);
+        load_token<DK, DV, Tin, false, kModeKDA, false>(in, k + tok * DK, v + tok * DV, z + tok * DK,
+                                                        bl[tok], (const Tin*)nullptr);
+        kda_token_step<DK, DV, Tin, false, kModeKDA, false, false>(Sv, in, ea, (Tin*)nullptr, s_al,
+                                                                   s_k, (float*)nullptr, s_red);
     }
-    store_state<DK, DV>(Sv, S);
+    store_state<DK, DV, false>(Sv, S);
 }
 
 // Verify pass of the same draft window ([K3-ATTN §6.2]): from the checkpoint
@@ -85,15 +85,16 @@ void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
     float4 Sv[16];
-    load_state<DK, DV>(Sv, state + (size_t)nh * DK * DV);
+    load_state<DK, DV, false>(Sv, state + (size_t)nh * DK * DV);
     const float ea = expf(A[h]);
     for (int t = 0; t < W; t++) {
         const size_t tok = ((size_t)n * W + t) * H + h;
         if (t > 0) __syncthreads();     // the previous step's readers of the LDS vectors are done
         TokenIn<DK, DV> in;
-        load_token<DK, DV, Tin, true>(in, k + tok * DK, v + tok * DV, z + tok * DK, bl[tok],
-                                      q + tok * DK);
-        kda_token_step<DK, DV, Tin, true>(Sv, in, ea, o + tok * DV, s_al, s_k, s_q, s_red, s_qk);
+        load_token<DK, DV, Tin, true, kModeKDA, false>(in, k + tok * DK, v + tok * DV, z + tok * DK,
+                                                       bl[tok], q + tok * DK);
+        kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, in, ea, o + tok * DV, s_al, s_k,
+                                                                  s_q, s_red, s_qk);
     }
 }
 

@@ -28,10 +28,11 @@ namespace kda {
 //   d = 128 (kWave): wave w = t / 64 owns columns [32w, 32w + 32); lane l of
 //     it holds columns 32w + 4 (l % 8) .. + 3 and rows 16 (l / 8) .. + 15, so
 //     the 8 lanes that share a column group (l % 8) cover all 128 rows.
-//   other sizes: thread t holds columns 4 (t % CG) .. + 3 and rows
-//     16 (t / CG) .. + 15 (CG = DV / 4 column groups, DK / 16 row groups).
-template <int DK, int DV> struct StateLayout {
-    static constexpr bool kWave = DK == 128 && DV == 128;
+//   other sizes, and d = 128 with WAVE false: thread t holds columns
+//     4 (t % CG) .. + 3 and rows 16 (t / CG) .. + 15 (CG = DV / 4 column
+//     groups, DK / 16 row groups); a wave spans 2 row groups at d = 128.
+template <int DK, int DV, bool WAVE = true> struct StateLayout {
+    static constexpr bool kWave = WAVE && DK == 128 && DV == 128;
     static constexpr int CG = DV / 4, RG = DK / 16, NT = CG * RG;
     __device__ static int col0(int t) { return kWave ? 32 * (t >> 6) + 4 * (t & 7) : 4 * (t % CG); }
     __device__ static int row0(int t) { return kWave ? 16 * ((t & 63) >> 3) : 16 * (t / CG); }
@@ -59,11 +60,11 @@ template <int DK, int DV> struct TokenIn {
     float z[KPT], k[KPT], q[KPT], v[4], b;
 };
 
-template <int DK, int DV, typename Tin, bool WITH_Q, int MODE = kModeKDA>
+template <int DK, int DV, typename Tin, bool WITH_Q, int MODE = kModeKDA, bool WAVE = true>
 __device__ __forceinline__ void load_token(TokenIn<DK, DV>& in, const Tin* __restrict__ kt,
                                            const Tin* __restrict__ vt, const float* __restrict__ zt,
                                            float b_logit, const Tin* __restrict__ qt) {
-    using SL = StateLayout<DK, DV>;
+    using SL = StateLayout<DK, DV, WAVE>;
     const int t = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < TokenIn<DK, DV>::KPT; j++) {
@@ -90,8 +91,16 @@ __device__ __forceinline__ void load_token(TokenIn<DK, DV>& in, const Tin* __res
 // MODE picks a row of the family table ([LA-KDA §4]): kModeGLA writes
 // u = beta v without the erase (no p), kModeDeltaNet takes alpha = 1 without
 // a gate logit.  With STORE each updated row is also written to S_out (the
-// thread's block of a row-major state) as soon as it is formed.
-template <int DK, int DV, typename Tin, bool WITH_Q, int MODE = kModeKDA, bool STORE = false>
+// thread's block of a row-major state) as soon as it is formed.  WAVE picks
+// the state layout (StateLayout): at d = 128 the one-token kernels sum over
+// row groups inside each wave with an xor butterfly (no barrier), while the
+// multi-token loops of the fold and verify pass keep the row-group layout and
+// sum through LDS.  Both add the 8 row groups' partial sums in the same
+// pairwise order, ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)), and
+// every thread forms its partial over its 16 rows in row order, so both give
+// the same bits.
+template <int DK, int DV, typename Tin, bool WITH_Q, int MODE = kModeKDA, bool STORE = false,
+          bool WAVE = true>
 __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const TokenIn<DK, DV>& in,
                                                float ea, Tin* __restrict__ ot, float* s_al,
                                                float* s_k, float* s_q,
@@ -99,7 +108,7 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const TokenIn<D
                                                float* s_qk = nullptr,
                                                float* __restrict__ S_out = nullptr) {
 #pragma clang fp contract(off)
-    using SL = StateLayout<DK, DV>;
+    using SL = StateLayout<DK, DV, WAVE>;
     constexpr int CG = SL::CG, RG = SL::RG, NT = SL::NT;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;           // the row-group layout (not kWave)
@@ -164,20 +173,36 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const TokenIn<D
             if (cg == 0) s_qk[rg] = qkp;
         }
         __syncthreads();
+        // the RG row-group partials summed as a pairwise tree (the order of
+        // the butterfly above when RG = 8)
+        float a[4][RG], c[4][RG], qq[RG];
 #pragma unroll
         for (int gidx = 0; gidx < RG; gidx++) {
-            const float4 a = *reinterpret_cast<const float4*>(&s_red[0][gidx][cg * 4]);
-            P[0] += a.x; P[1] += a.y; P[2] += a.z; P[3] += a.w;
+            const float4 x = *reinterpret_cast<const float4*>(&s_red[0][gidx][cg * 4]);
+            a[0][gidx] = x.x; a[1][gidx] = x.y; a[2][gidx] = x.z; a[3][gidx] = x.w;
             if (WITH_Q) {
-                const float4 c = *reinterpret_cast<const float4*>(&s_red[1][gidx][cg * 4]);
-                R[0] += c.x; R[1] += c.y; R[2] += c.z; R[3] += c.w;
+                const float4 y = *reinterpret_cast<const float4*>(&s_red[1][gidx][cg * 4]);
+                c[0][gidx] = y.x; c[1][gidx] = y.y; c[2][gidx] = y.z; c[3][gidx] = y.w;
+                qq[gidx] = s_qk[gidx];
             }
         }
-        if (WITH_Q) {
-            // row-group partials of q . k, summed in a fixed order
 #pragma unroll
-            for (int gidx = 0; gidx < RG; gidx++) qk += s_qk[gidx];
+        for (int m = 1; m < RG; m <<= 1)
+#pragma unroll
+            for (int gidx = 0; gidx < RG; gidx += 2 * m) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    a[e][gidx] += a[e][gidx + m];
+                    if (WITH_Q) c[e][gidx] += c[e][gidx + m];
+                }
+                if (WITH_Q) qq[gidx] += qq[gidx + m];
+            }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            P[e] = a[e][0];
+            R[e] = c[e][0];
         }
+        if (WITH_Q) qk = qq[0];
     }
     float u[4];
 #pragma unroll
@@ -198,20 +223,29 @@ __device__ __forceinline__ void kda_token_step(float4 (&Sv)[16], const TokenIn<D
     }
 }
 
-template <int DK, int DV>
+// NT: nontemporal loads and stores (the one-token kernels, bound by the state
+// stream); plain ones for the multi-token loops, bound by their steps.
+template <int DK, int DV, bool WAVE = true, bool NT = true>
 __device__ __forceinline__ void load_state(float4 (&Sv)[16], const float* __restrict__ S) {
-    using SL = StateLayout<DK, DV>;
+    using SL = StateLayout<DK, DV, WAVE>;
     const int c0 = SL::col0(threadIdx.x), r0 = SL::row0(threadIdx.x);
 #pragma unroll
-    for (int r = 0; r < 16; r++) Sv[r] = load_nt(S + (size_t)(r0 + r) * DV + c0);
+    for (int r = 0; r < 16; r++) {
+        const float* p = S + (size_t)(r0 + r) * DV + c0;
+        Sv[r] = NT ? load_nt(p) : *reinterpret_cast<const float4*>(p);
+    }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool WAVE = true, bool NT = true>
 __device__ __forceinline__ void store_state(const float4 (&Sv)[16], float* __restrict__ S) {
-    using SL = StateLayout<DK, DV>;
+    using SL = StateLayout<DK, DV, WAVE>;
     const int c0 = SL::col0(threadIdx.x), r0 = SL::row0(threadIdx.x);
 #pragma unroll
-    for (int r = 0; r < 16; r++) store_nt(S + (size_t)(r0 + r) * DV + c0, Sv[r]);
+    for (int r = 0; r < 16; r++) {
+        float* p = S + (size_t)(r0 + r) * DV + c0;
+        if (NT) store_nt(p, Sv[r]);
+        else *reinterpret_cast<float4*>(p) = Sv[r];
+    }
 }
 
 }  // namespace kda
