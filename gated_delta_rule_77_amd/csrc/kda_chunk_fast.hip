@@ -520,23 +520,37 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // general DPLR record (X~ = Wb S, the folded Uo and Cs terms).
 constexpr int kChainKDA = 0, kChainGLA = 1, kChainDPLR = 2;
 
+// With fewer (segment, head) chains than kSplitMaxChains (half the CUs of
+// the part) both chain launches split each chain across two workgroups by
+// columns, halving the matrix work of every serial step; the grid is sized
+// for it whenever the capacity allows it, and each workgroup checks the
+// actual segment count (uniform) before it takes its half.
+constexpr int kSplitMaxChains = 128;
+
+__device__ __forceinline__ bool chains_split(const int* __restrict__ hdr, int H, int split_grid) {
+    return split_grid && (long long)hdr[1] * H <= kSplitMaxChains;
+}
+
 constexpr int kOutNS = 8;       // 16-column slices
 constexpr int kOutDepth = 3;    // record prefetch ring depth (chunks)
 constexpr int kLdO = 136;       // bf16 output staging rows [64][kLdO]
 
-// per wave and chunk; KDA uses a (A_qk), DPLR c (Cs), the rest is common
+// per wave and chunk; KDA uses a (A_qk), DPLR c (Cs), the rest is common.
+// NS: the 16-column slices of state and output the workgroup owns (8: all
+// 128 columns; 4: one half of a split chain), starting at slice sb.
+template <int NS>
 struct OutFrags {
     bf16x8 w[4], q[4];          // -W^T (Wb^T), (Q . Gamma)^T (Q'^T) of token block w, k-steps 0..3
     bf16x8 k[4];                // Kbar^T (Abar^T) rows [32w, 32w + 32): [16-row half][token kstep]
     bf16x8 a[2];                // A_qk rows of token block w, token k-steps 0..1
-    bf16x4 u[kOutNS];           // U (Uo) tiles of token block w
-    bf16x4 c[2][kOutNS];        // Cs tiles of the wave's two row tiles
+    bf16x4 u[NS];               // U (Uo) tiles of token block w
+    bf16x4 c[2][NS];            // Cs tiles of the wave's two row tiles
     float4 g0, g1;              // gamma_C for the wave's two row tiles
 };
 
-template <int CK>
-__device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __restrict__ rec, int w,
-                                               int lane, int g4) {
+template <int CK, int NS>
+__device__ __forceinline__ void load_out_frags(OutFrags<NS>& f, const uint8_t* __restrict__ rec, int w,
+                                               int lane, int g4, int sb) {
     constexpr bool DPLR = CK == kChainDPLR;
     using RL = RecLayout<DPLR>;
 #pragma unroll
@@ -550,8 +564,8 @@ __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __res
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
-            for (int sl = 0; sl < kOutNS; sl++)
-                f.c[b][sl] = *reinterpret_cast<const bf16x4*>(rec + RL::C + (((2 * w + b) * 8 + sl) * 64 + lane) * 8);
+            for (int sl = 0; sl < NS; sl++)
+                f.c[b][sl] = *reinterpret_cast<const bf16x4*>(rec + RL::C + (((2 * w + b) * 8 + sb + sl) * 64 + lane) * 8);
     } else {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -560,8 +574,8 @@ __device__ __forceinline__ void load_out_frags(OutFrags& f, const uint8_t* __res
                           : bf16x8{};
     }
 #pragma unroll
-    for (int sl = 0; sl < kOutNS; sl++)
-        f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + RL::U + ((sl * 4 + w) * 64 + lane) * 8);
+    for (int sl = 0; sl < NS; sl++)
+        f.u[sl] = *reinterpret_cast<const bf16x4*>(rec + RL::U + (((sb + sl) * 4 + w) * 64 + lane) * 8);
     const float* gC = reinterpret_cast<const float*>(rec + RL::G);
     f.g0 = *reinterpret_cast<const float4*>(gC + 32 * w + 4 * g4);
     f.g1 = *reinterpret_cast<const float4*>(gC + 32 * w + 16 + 4 * g4);
@@ -577,16 +591,20 @@ struct OutGate {
 };
 
 // 64 rows x 256 bytes of O (or, with GATE, of Sigmoid(gate) * RMSNorm(O)),
-// 16 bytes per lane.  FULL: every row is inside the sequence (a uniform
-// test by the caller), so the stores need no per-row test.
-template <bool GATE, bool FULL>
+// 16 bytes per lane; with NS = 4 the 128 bytes of the workgroup's column half
+// (columns 16 sb ..), staged in sO's first 64 columns.  FULL: every row is
+// inside the sequence (a uniform test by the caller), so the stores need no
+// per-row test.
+template <bool GATE, bool FULL, int NS>
 __device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[4],
                                            bf16* __restrict__ o, int tok0, int len, int H, int h,
-                                           int tid, const OutGate& og) {
+                                           int tid, const OutGate& og, int sb) {
+    constexpr int LPR = 2 * NS;                 // 16-byte pieces per row
+    static_assert(!GATE || NS == 8, "the gated output needs whole rows");
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-        const size_t off = ((size_t)(tok0 + row) * H + h) * 128 + c8;
+    for (int i = 0; i < LPR / 4; i++) {
+        const int idx = i * 256 + tid, row = idx / LPR, c8 = (idx % LPR) * 8;
+        const size_t off = ((size_t)(tok0 + row) * H + h) * 128 + 16 * sb + c8;
         if constexpr (GATE) {
             const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + row * kLdO + c8);
             float ov[8], ss = 0.f;
@@ -615,22 +633,22 @@ __device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[
 // One chunk for one wave over all slices.  KDA: V~ = U - W S,
 // O = (Q . Gamma) S + A_qk V~, S <- Diag(gamma_C) S + Kbar^T V~.  DPLR:
 // X~ = Wb S, O = Q' S + Uo, S <- Diag(gamma_C) S + Abar^T X~ + Cs.
-template <bool DBG, bool GATE, int CK>
-__device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, int len,
-                                         f32x4 (&accS)[kOutNS][2], bf16* sS, bf16* sVt, bf16* sO,
+template <bool DBG, bool GATE, int CK, int NS>
+__device__ __forceinline__ void out_step(const OutFrags<NS>& f, int cid, int tok0, int len,
+                                         f32x4 (&accS)[NS][2], bf16* sS, bf16* sVt, bf16* sO,
                                          bf16* __restrict__ o, float* __restrict__ dbgS, int H,
                                          int h, int w, int lane, int n16, int g4, int tid,
-                                         const OutGate& og) {
+                                         const OutGate& og, int sb) {
     constexpr bool DPLR = CK == kChainDPLR;
     if (DBG) {
 #pragma unroll
-        for (int sl = 0; sl < kOutNS; sl++)
+        for (int sl = 0; sl < NS; sl++)
 #pragma unroll
             for (int b = 0; b < 2; b++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int row = 32 * w + 16 * b + 4 * g4 + e;
-                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * sl + n16] = accS[sl][b][e];
+                    dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * (sb + sl) + n16] = accS[sl][b][e];
                 }
     }
     // the gate logits of the rows this thread stores, issued before the
@@ -652,10 +670,10 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
             }
         }
     }
-    f32x4 accO[kOutNS];
+    f32x4 accO[NS];
     // V~ and the (Q . Gamma) S part of O, four slices at a time
 #pragma unroll
-    for (int bb = 0; bb < kOutNS / 4; bb++) {
+    for (int bb = 0; bb < NS / 4; bb++) {
         bf16x8 sf[4][4];
 #pragma unroll
         for (int s4 = 0; s4 < 4; s4++)
@@ -678,7 +696,7 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
     }
     __syncthreads();
 #pragma unroll
-    for (int sl = 0; sl < kOutNS; sl++) {
+    for (int sl = 0; sl < NS; sl++) {
         bf16x8 vfr[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -704,44 +722,32 @@ __device__ __forceinline__ void out_step(const OutFrags& f, int cid, int tok0, i
         for (int e = 0; e < 4; e++) sO[(16 * w + 4 * g4 + e) * kLdO + 16 * sl + n16] = (bf16)acc[e];
     }
     __syncthreads();
-    if (len >= C) store_rows<GATE, true>(sO, gpre, o, tok0, len, H, h, tid, og);
-    else store_rows<GATE, false>(sO, gpre, o, tok0, len, H, h, tid, og);
+    if (len >= C) store_rows<GATE, true, NS>(sO, gpre, o, tok0, len, H, h, tid, og, sb);
+    else store_rows<GATE, false, NS>(sO, gpre, o, tok0, len, H, h, tid, og, sb);
 }
 
-// grid: seg_cap * H blocks, block = (segment, head).  With GATE the rows
-// stored are the layer's gated RMSNorm of O instead of O.
-template <bool DBG, bool GATE, int CK>
-__global__ __launch_bounds__(256, 1)
-void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
-                    const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
-                    const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
-                    bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS,
-                    const bf16* __restrict__ gate, const float* __restrict__ norm_w, float rms_eps)
-{
+// The output chain of one (segment, head) over NS slices starting at sb.
+template <bool DBG, bool GATE, int CK, int NS>
+__device__ __forceinline__ void out_body(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
+                                         int seg_id, int h, int n, int c0, int nch, bool last, int H,
+                                         int sb, const float* __restrict__ sstart, bf16* __restrict__ o,
+                                         float* __restrict__ hT, float* __restrict__ dbgS,
+                                         const bf16* __restrict__ gate, const float* __restrict__ norm_w,
+                                         float rms_eps, bf16* sS, bf16* sVt, bf16* sO) {
     constexpr bool DPLR = CK == kChainDPLR;
-    const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
-    if (seg_id >= hdr[1]) return;
-    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
-    const int n = sg.x, c0 = sg.y, nch = sg.z;
-    const bool last = sg.w == seqsegs[n].y - 1;
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
 
-    __shared__ __align__(16) bf16 sS[kOutNS * 4 * 64 * 8];
-    __shared__ __align__(16) bf16 sVt[kOutNS * 4 * 64 * 4];
-    __shared__ __align__(16) bf16 sO[64 * kLdO];
-
-    f32x4 accS[kOutNS][2];
+    f32x4 accS[NS][2];
     const float* st = sstart + ((size_t)seg_id * H + h) * 128 * 128;
 #pragma unroll
-    for (int sl = 0; sl < kOutNS; sl++) {
+    for (int sl = 0; sl < NS; sl++) {
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                accS[sl][b][e] = st[(32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * sl + n16];
+                accS[sl][b][e] = st[(32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * (sb + sl) + n16];
         *reinterpret_cast<bf16x8*>(sS + ((sl * 4 + w) * 64 + lane) * 8) = pack_frag(accS[sl][0], accS[sl][1]);
     }
     int seg_tok0 = 0, seg_len = 0;
@@ -759,10 +765,10 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 
     constexpr int D = kOutDepth;
     auto rec = [&](int c) { return recs + ((size_t)(c0 + c) * H + h) * RecLayout<DPLR>::BYTES; };
-    OutFrags F[D];
+    OutFrags<NS> F[D];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < D - 1; u++) load_out_frags<CK>(F[u], rec(min(u, nch - 1)), w, lane, g4);
+        for (int u = 0; u < D - 1; u++) load_out_frags<CK, NS>(F[u], rec(min(u, nch - 1)), w, lane, g4, sb);
     }
     __syncthreads();
     const int nfull = nch / D * D;
@@ -770,30 +776,67 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 #pragma unroll
         for (int u = 0; u < D; u++) {
             // unconditional prefetch (index clamped) keeps the wait counts exact
-            load_out_frags<CK>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4);
+            load_out_frags<CK, NS>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4, sb);
             const int t0 = (ci + u) * C;
-            out_step<DBG, GATE, CK>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
-                                dbgS, H, h, w, lane, n16, g4, tid, og);
+            out_step<DBG, GATE, CK, NS>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
+                                        dbgS, H, h, w, lane, n16, g4, tid, og, sb);
         }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
-            out_step<DBG, GATE, CK>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO,
-                                o, dbgS, H, h, w, lane, n16, g4, tid, og);
+            out_step<DBG, GATE, CK, NS>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt,
+                                        sO, o, dbgS, H, h, w, lane, n16, g4, tid, og, sb);
         }
 
     if (last && hT) {
 #pragma unroll
-        for (int sl = 0; sl < kOutNS; sl++)
+        for (int sl = 0; sl < NS; sl++)
 #pragma unroll
             for (int b = 0; b < 2; b++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    hT[(((size_t)n * H + h) * 128 + 32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * sl + n16] =
+                    hT[(((size_t)n * H + h) * 128 + 32 * w + 16 * b + 4 * g4 + e) * 128 + 16 * (sb + sl) + n16] =
                         accS[sl][b][e];
     }
+}
+
+// grid: seg_cap * H blocks, block = (segment, head), times 2 (the column
+// halves) when split_grid.  With GATE the rows stored are the layer's gated
+// RMSNorm of O instead of O; the gated, debug and DPLR outputs never split.
+template <bool DBG, bool GATE, int CK>
+__global__ __launch_bounds__(256, 1)
+void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ chunks,
+                    const int4* __restrict__ segs, const int2* __restrict__ seqsegs,
+                    const int* __restrict__ hdr, int H, const float* __restrict__ sstart,
+                    bf16* __restrict__ o, float* __restrict__ hT, float* __restrict__ dbgS,
+                    const bf16* __restrict__ gate, const float* __restrict__ norm_w, float rms_eps,
+                    int split_grid)
+{
+    constexpr bool CAN_SPLIT = !DBG && !GATE && CK != kChainDPLR;
+    const int ways = CAN_SPLIT && split_grid ? 2 : 1;
+    const int half = blockIdx.x % ways, chain = blockIdx.x / ways;
+    const int seg_id = chain / H, h = chain % H;
+    if (seg_id >= hdr[1]) return;
+    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
+    const int n = sg.x;
+    const bool last = sg.w == seqsegs[n].y - 1;
+
+    __shared__ __align__(16) bf16 sS[kOutNS * 4 * 64 * 8];
+    __shared__ __align__(16) bf16 sVt[kOutNS * 4 * 64 * 4];
+    __shared__ __align__(16) bf16 sO[64 * kLdO];
+    if constexpr (CAN_SPLIT) {
+        if (chains_split(hdr, H, split_grid)) {
+            out_body<DBG, GATE, CK, kOutNS / 2>(recs, chunks, seg_id, h, n, sg.y, sg.z, last, H,
+                                                half * kOutNS / 2, sstart, o, hT, dbgS, gate, norm_w,
+                                                rms_eps, sS, sVt, sO);
+            return;
+        }
+        if (half != 0) return;
+    }
+    out_body<DBG, GATE, CK, kOutNS>(recs, chunks, seg_id, h, n, sg.y, sg.z, last, H, 0, sstart, o, hT,
+                                    dbgS, gate, norm_w, rms_eps, sS, sVt, sO);
 }
 
 // Transition launch: one workgroup of 8 waves per (segment, head) carries the
@@ -886,25 +929,27 @@ __device__ __forceinline__ float4 gamma_tile(int rt, float gv0, float gv1) {
     }
 }
 
-// One chunk for wave w from the staged record.  KDA: V~ = U - W S (U = 0 for
-// M), S <- Diag(gamma_C) S + Kbar^T V~.  GLA: V~ = U, so the M columns
-// (V~ = 0) only decay.  DPLR: X~ = Wb S, S <- Diag(gamma_C) S + Abar^T X~ + Cs
-// (Cs for R only).
-template <int CK>
-__device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2], int w, int lane,
-                                            int g4) {
+// One chunk for one wave from the staged record: NJ slices of 16 columns of
+// [R | M], the first at slice index s0 (slices 0..7 are R, 8..15 M; is_m: the
+// wave's slices are M columns).  KDA: V~ = U - W S (U = 0 for M),
+// S <- Diag(gamma_C) S + Kbar^T V~.  GLA: V~ = U, so the M columns (V~ = 0)
+// only decay.  DPLR: X~ = Wb S, S <- Diag(gamma_C) S + Abar^T X~ + Cs (Cs for
+// R only).
+template <int CK, int NJ>
+__device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][NJ], int s0, bool is_m,
+                                            int lane, int g4) {
     constexpr bool DPLR = CK == kChainDPLR;
     using TS = TransStage<DPLR>;
     const float* gC = reinterpret_cast<const float*>(st + TS::G);
     const int n16 = lane & 15;
     const float gv0 = gC[16 * (n16 >> 2) + 4 * g4 + (n16 & 3)];
     const float gv1 = gC[64 + 16 * (n16 >> 2) + 4 * g4 + (n16 & 3)];
-    if (CK == kChainGLA && w >= 4) {
+    if (CK == kChainGLA && is_m) {
 #pragma unroll
         for (int rt = 0; rt < 8; rt++) {
             const float4 g = gamma_tile(rt, gv0, gv1);
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
+            for (int j = 0; j < NJ; j++) {
                 f32x4& a = acc[rt][j];
                 a[0] *= g.x; a[1] *= g.y; a[2] *= g.z; a[3] *= g.w;
             }
@@ -912,83 +957,77 @@ __device__ __forceinline__ void trans_chunk(const uint8_t* st, f32x4 (&acc)[8][2
         return;
     }
     // S fragments of k-step ks: row tiles 2ks, 2ks + 1 of each owned slice
-    bf16x8 sf[4][2];
+    bf16x8 sf[4][NJ];
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) sf[ks][j] = pack_frag(acc[2 * ks][j], acc[2 * ks + 1][j]);
+        for (int j = 0; j < NJ; j++) sf[ks][j] = pack_frag(acc[2 * ks][j], acc[2 * ks + 1][j]);
     // V~ = U - W S for the 4 token blocks of the owned slices (U = 0 for M)
-    f32x4 vt[4][2];
+    f32x4 vt[4][NJ];
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) {
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < NJ; j++) {
             vt[tb][j] = zero4();
-            if (!DPLR && w < 4)
+            if (!DPLR && !is_m)
                 vt[tb][j] = unpack4(*reinterpret_cast<const bf16x4*>(
-                    st + TS::U + (((2 * w + j) * 4 + tb) * 64 + lane) * 8));
+                    st + TS::U + (((s0 + j) * 4 + tb) * 64 + lane) * 8));
         }
         if constexpr (CK != kChainGLA) {
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
                 const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + TS::W + ((tb * 4 + ks) * 64 + lane) * 16);
 #pragma unroll
-                for (int j = 0; j < 2; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
+                for (int j = 0; j < NJ; j++) vt[tb][j] = mfma_bf16(wf, sf[ks][j], vt[tb][j]);
             }
         }
     }
     // V~ fragments over tokens, then S <- Diag(gamma_C) S + Kbar^T V~
-    bf16x8 vf[2][2];
+    bf16x8 vf[2][NJ];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
+        for (int j = 0; j < NJ; j++) vf[kb][j] = pack_frag(vt[2 * kb][j], vt[2 * kb + 1][j]);
 #pragma unroll
     for (int rt = 0; rt < 8; rt++) {
         const float4 g = gamma_tile(rt, gv0, gv1);
         const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 0) * 64 + lane) * 16);
         const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(st + TS::K + ((rt * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < NJ; j++) {
             f32x4& a = acc[rt][j];
             a[0] *= g.x; a[1] *= g.y; a[2] *= g.z; a[3] *= g.w;
-            if (DPLR && w < 4)
+            if (DPLR && !is_m)
                 a += unpack4(*reinterpret_cast<const bf16x4*>(
-                    st + TS::C + ((rt * 8 + 2 * w + j) * 64 + lane) * 8));
+                    st + TS::C + ((rt * 8 + s0 + j) * 64 + lane) * 8));
             a = mfma_bf16(k0, vf[0][j], a);
             a = mfma_bf16(k1, vf[1][j], a);
         }
     }
 }
 
-// grid: seg_cap * H blocks, block = (segment, head)
-template <int CK>
-__global__ __launch_bounds__(512, 1)
-void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
-                      const int2* __restrict__ seqsegs, const int* __restrict__ hdr, int H,
-                      float* __restrict__ rm)
-{
+// The transition of one (segment, head): NJ = 2, wave w owns slices 2w and
+// 2w + 1 (all 256 columns in one workgroup); NJ = 1, wave w of half `half`
+// owns slice 8 half + w (R in half 0, M in half 1).
+template <int CK, int NJ>
+__device__ __forceinline__ void trans_body(const uint8_t* __restrict__ recs, int c0, int nch, int H,
+                                           int h, int seg_id, int half, float* __restrict__ rm,
+                                           uint8_t (*stage)[TransStage<CK == kChainDPLR>::BYTES]) {
     constexpr bool DPLR = CK == kChainDPLR;
-    const int seg_id = blockIdx.x / H, h = blockIdx.x % H;
-    if (seg_id >= hdr[1]) return;
-    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
-    const int2 ss = seqsegs[sg.x];
-    if (sg.w == ss.y - 1) return;          // the last segment's transition is never needed
-    const int c0 = sg.y, nch = sg.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
+    const int s0 = NJ == 2 ? 2 * w : 8 * half + w;
+    const bool is_m = s0 >= 8;
 
-    __shared__ __align__(16) uint8_t stage[2][TransStage<DPLR>::BYTES];
-
-    f32x4 acc[8][2];        // R from 0, M from the identity
+    f32x4 acc[8][NJ];       // R from 0, M from the identity
 #pragma unroll
     for (int rt = 0; rt < 8; rt++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < NJ; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int row = 16 * rt + 4 * g4 + e, col = 16 * (2 * w + j) + n16;
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * (s0 + j) + n16;
                 acc[rt][j][e] = (row == col - 128) ? 1.f : 0.f;
             }
     if (nch > 0) {
@@ -1003,26 +1042,49 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
         __syncthreads();
         int c = 0;
         for (; c + 2 <= nch; c += 2) {
-            trans_chunk<CK>(stage[0], acc, w, lane, g4);
+            trans_chunk<CK, NJ>(stage[0], acc, s0, is_m, lane, g4);
             stage_store<CK>(R1, stage[1], tid);    // chunk c + 1
             R1 = stage_load<CK>(rec(c + 3), tid);
             __syncthreads();
-            trans_chunk<CK>(stage[1], acc, w, lane, g4);
+            trans_chunk<CK, NJ>(stage[1], acc, s0, is_m, lane, g4);
             stage_store<CK>(R0, stage[0], tid);    // chunk c + 2
             R0 = stage_load<CK>(rec(c + 4), tid);
             __syncthreads();
         }
-        if (c < nch) trans_chunk<CK>(stage[0], acc, w, lane, g4);
+        if (c < nch) trans_chunk<CK, NJ>(stage[0], acc, s0, is_m, lane, g4);
     }
 #pragma unroll
     for (int rt = 0; rt < 8; rt++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < NJ; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int row = 16 * rt + 4 * g4 + e, col = 16 * (2 * w + j) + n16;
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * (s0 + j) + n16;
                 rm[(((size_t)seg_id * H + h) * 128 + row) * 256 + col] = acc[rt][j][e];
             }
+}
+
+// grid: seg_cap * H blocks, block = (segment, head), times 2 (the halves)
+// when split_grid
+template <int CK>
+__global__ __launch_bounds__(512, 1)
+void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
+                      const int2* __restrict__ seqsegs, const int* __restrict__ hdr, int H,
+                      float* __restrict__ rm, int split_grid)
+{
+    constexpr bool DPLR = CK == kChainDPLR;
+    const int ways = split_grid ? 2 : 1;
+    const int half = blockIdx.x % ways, chain = blockIdx.x / ways;
+    const int seg_id = chain / H, h = chain % H;
+    if (seg_id >= hdr[1]) return;
+    const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
+    const int2 ss = seqsegs[sg.x];
+    if (sg.w == ss.y - 1) return;          // the last segment's transition is never needed
+    __shared__ __align__(16) uint8_t stage[2][TransStage<DPLR>::BYTES];
+    if (chains_split(hdr, H, split_grid))
+        trans_body<CK, 1>(recs, sg.y, sg.z, H, h, seg_id, half, rm, stage);
+    else if (half == 0)
+        trans_body<CK, 2>(recs, sg.y, sg.z, H, h, seg_id, 0, rm, stage);
 }
 
 // Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and
@@ -1134,9 +1196,13 @@ hipError_t launch_chain(const ChunkArgs& a) {
     float* sstart = reinterpret_cast<float*>(a.ws + a.L.off_sstart);
     float* rm = reinterpret_cast<float*>(a.ws + a.L.off_rm);
     hipError_t e;
-    const dim3 gc((unsigned)((long long)a.L.seg_cap * a.H));
-    hipLaunchKernelGGL((seg_trans_kernel<CK>), gc, dim3(512), 0, a.stream, (const uint8_t*)recs,
-                       segs, seqsegs, hdr, a.H, rm);
+    // the split of each chain across two workgroups can only apply when the
+    // segment capacity is small; otherwise the grids keep one per chain
+    const long long chains = (long long)a.L.seg_cap * a.H;
+    const int split_grid = chains <= 2 * kSplitMaxChains ? 1 : 0;
+    const dim3 gc((unsigned)chains), gc2((unsigned)(chains * (split_grid ? 2 : 1)));
+    hipLaunchKernelGGL((seg_trans_kernel<CK>), gc2, dim3(512), 0, a.stream, (const uint8_t*)recs,
+                       segs, seqsegs, hdr, a.H, rm, split_grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
     const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
@@ -1146,10 +1212,14 @@ hipError_t launch_chain(const ChunkArgs& a) {
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
     const bf16* gate = static_cast<const bf16*>(a.gate);
 #define KDA_OUT(DBG, GATE)                                                                       \
-    hipLaunchKernelGGL((seg_out_kernel<DBG, GATE, CK>), gc, dim3(256), 0, a.stream,            \
-                       (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H, (const float*)sstart, \
-                       (bf16*)a.o, a.hT, DBG ? a.dbg_state : (float*)nullptr, gate, a.norm_w,    \
-                       a.rms_eps)
+    do {                                                                                         \
+        constexpr bool can_split = !DBG && !GATE && CK != kChainDPLR;                             \
+        hipLaunchKernelGGL((seg_out_kernel<DBG, GATE, CK>), can_split ? gc2 : gc, dim3(256), 0,    \
+                           a.stream, (const uint8_t*)recs, chunks, segs, seqsegs, hdr, a.H,       \
+                           (const float*)sstart, (bf16*)a.o, a.hT,                                 \
+                           DBG ? a.dbg_state : (float*)nullptr, gate, a.norm_w, a.rms_eps,         \
+                           can_split ? split_grid : 0);                                            \
+    } while (0)
     // the debug and gated variants exist for KDA only (the API enforces it)
     if constexpr (CK != kChainKDA) {
         KDA_OUT(false, false);
