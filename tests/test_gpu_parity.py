@@ -742,3 +742,43 @@ def test_random_packed_layouts(kda, case_id):
         e_s = rel_err(hT[s][heads], rS, scale=s_scale)
         assert e_o <= tol and e_s <= tol, (case_id, dk, chunk, dtype, H, lens, s, e_o, e_s)
     _report(f"random layout {case_id}: d={dk} C={chunk} {dtype} H={H} lens={lens}", ok=0.0)
+
+
+@pytest.mark.parametrize("dtype,dk,chunk", [("bf16", 128, 64), ("fp32", 16, 16)])
+def test_packed_batch_beyond_64_sequences(kda, dtype, dk, chunk):
+    """A packed batch of 100 sequences (empty, one-token, ragged and
+    multi-chunk lengths): the chunk bookkeeping's block-wide path (more than
+    64 sequences) instead of its single-wave one.  Seven sequences against
+    the oracle on both heads (per-tensor metric over the checked ones), every
+    empty sequence's state equal to its h0, and the packed call equal bit for
+    bit to separate calls of the same sequences."""
+    import random
+    rng = random.Random(9100 + dk)
+    lens = [rng.choice([0, 1, rng.randint(2, 63), rng.randint(64, 300)]) for _ in range(100)]
+    lens[0], lens[50], lens[99] = 0, 1, 257
+    case = KI.PrefillCase("packed100", H=2, dk=dk, dv=dk, chunk=chunk, dtype=dtype, zero_h0=False)
+    d = KI.make_prefill(case, seed=9200 + dk, lengths=lens)
+    g = to_dev(d)
+    o, hT = gpu_prefill(kda, g)
+    torch.cuda.synchronize()
+    cu = [int(x) for x in d["cu_seqlens"].tolist()]
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    checked = [s for s in (1, 13, 49, 50, 64, 65, 99) if lens[s] > 0]
+    refs = {s: oracle_prefill(d, seq=s) for s in checked}
+    o_scale = max(float(np.abs(r[0]).max()) for r in refs.values())
+    s_scale = max(float(np.abs(r[1]).max()) for r in refs.values())
+    for s in checked:
+        ro, rS = refs[s]
+        eo = rel_err(o[0, cu[s]:cu[s + 1]], ro, scale=o_scale)
+        eS = rel_err(hT[s], rS, scale=s_scale)
+        _report(f"packed 100 {dtype} seq {s} (len {lens[s]})", o=eo, hT=eS)
+        assert eo <= tol and eS <= tol
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s], g["h0"][s])
+    for s in (13, 64, 99):
+        a, e = cu[s], cu[s + 1]
+        sub = {k: g[k][:, a:e].contiguous() for k in ("q", "k", "v", "z", "b")}
+        sub.update(A=g["A"], h0=g["h0"][s:s + 1].contiguous(), chunk=chunk)
+        o1, h1 = gpu_prefill(kda, sub)
+        assert torch.equal(o1[0], o[0, a:e]) and torch.equal(h1[0], hT[s])
