@@ -135,3 +135,63 @@ def test_layer_long_1m_prefix(kda):
     ratio = y_within_bar(y[0, :P][:, heads], ry, ro, pre(d["gate"]), d["norm_w"], TOL_BF16)
     report("composition", "layer long_1m y[:32768] heads 0, 7", y_err_over_bar=ratio)
     assert ratio <= 1.0
+
+
+SWITCH = {"gla": dict(erase=False), "deltanet": dict(decay=False)}
+
+
+@pytest.mark.parametrize("mode", ["gla", "deltanet"])
+def test_mode_composition_many_segments(kda, mode):
+    """The other rows of the family table on the segmented chain (GLA's chain
+    kernels, whose M columns only decay; DeltaNet on the KDA ones with
+    alpha = 1): 8,192 tokens on one head, 16 segments of 8 chunks, with the
+    slow-decay logits (GLA: alpha near 1, no erase; DeltaNet: beta ~ 3e-4),
+    every output and the final state against the oracle, after the oracle
+    shows that the last 1,024 tokens' result depends on the state composed
+    before them."""
+    case = KI.PrefillCase("slowmode", H=1, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=8192,
+                          zero_h0=False)
+    inp = _slow(KI.make_prefill(case, seed=12))
+    inp["h0"] = inp["h0"] * 25
+    d = to_dev(inp)
+    g, A = (None, None) if mode == "deltanet" else (d["z"], d["A"])
+    o, hT = kda.kda_chunk_fwd_mode(d["q"], d["k"], d["v"], g, d["b"], A, mode, initial_state=d["h0"],
+                                   chunk_size=64)
+    torch.cuda.synchronize()
+    args = lambda sl: (inp["q"][0, sl], inp["k"][0, sl], inp["v"][0, sl], inp["z"][0, sl],  # noqa: E731
+                       inp["b"][0, sl], inp["A"])
+    ro, rS = oracle.recurrence(*args(slice(None)), inp["h0"][0], **SWITCH[mode])
+    _, S_cut = oracle.recurrence(*args(slice(8192 - 1024, None)), None, **SWITCH[mode])
+    carried = float(np.abs(rS - S_cut).max() / np.abs(rS).max())
+    eo, eS = rel_err(o[0], ro), rel_err(hT[0], rS)
+    report("composition", f"{mode} slow decay H=1 T=8192", o=eo, hT=eS, carried=carried)
+    assert carried > 0.1
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_dplr_composition_many_segments(kda):
+    """The general DPLR update on its own chain kernels: 8,192 tokens on one
+    head, 16 segments of 8 chunks, slow decay (z - 7, A_h = +1) and a weak
+    low-rank correction (a scaled by 0.02), so the state composed across
+    segment boundaries carries into the checked span; every output and the
+    final state against the oracle."""
+    case = KI.PrefillCase("slowdplr", H=1, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=8192,
+                          zero_h0=False)
+    d = KI.make_dplr(case, seed=13)
+    d["z"] = d["z"] - Z_SHIFT
+    d["A"] = torch.ones_like(d["A"])
+    d["la"] = (d["la"].float() * 0.02).to(d["la"].dtype)
+    d["h0"] = d["h0"] * 25
+    g = {x: (d[x].cuda().contiguous() if d.get(x) is not None else None)
+         for x in ("q", "k", "v", "la", "lb", "z", "A", "h0")}
+    o, hT = kda.kda_dplr_chunk_fwd(g["q"], g["k"], g["v"], g["la"], g["lb"], g["z"], g["A"],
+                                   initial_state=g["h0"], chunk_size=64)
+    torch.cuda.synchronize()
+    args = lambda sl: tuple(d[x][0, sl] for x in ("q", "k", "v", "la", "lb", "z")) + (d["A"],)  # noqa: E731
+    ro, rS = oracle.recurrence_dplr_general(*args(slice(None)), d["h0"][0])
+    _, S_cut = oracle.recurrence_dplr_general(*args(slice(8192 - 1024, None)), None)
+    carried = float(np.abs(rS - S_cut).max() / np.abs(rS).max())
+    eo, eS = rel_err(o[0], ro), rel_err(hT[0], rS)
+    report("composition", "dplr slow decay H=1 T=8192", o=eo, hT=eS, carried=carried)
+    assert carried > 0.1
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
