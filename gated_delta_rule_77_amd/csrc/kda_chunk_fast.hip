@@ -67,12 +67,91 @@ __device__ __forceinline__ uint4 rows_back(uint4 prev, uint4 cur, int n16) {
     return r;
 }
 
-constexpr int kOffRK = 64 * kLdG * 4;
-constexpr int kOffRQ = kOffRK + 64 * kLdK * 2;
-constexpr int kOffFac = kOffRQ + 64 * kLdK * 2;
+constexpr int kOffRK = 64 * kLdG * 4;                    // CONV: L2Norm partial sums in step 1
+constexpr int kOffFac = kOffRK + 64 * kLdK * 2 * 2;
 constexpr int kOffBeta = kOffFac + kNFac * 128 * 4;
 constexpr int kSmemIntra = kOffBeta + 64 * 4;            // 80128 bytes: two workgroups per CU
-static_assert(3 * 64 * kLdA * 4 + kInvScr * 4 <= kOffFac, "A_kk, A_qk, N and P alias L/K.F and the row operands");
+// step 3: partial tiles [20 tiles][3 writers][64 lanes] of f32x4 over L (and
+// below the factor rows, which the partial products still read); A_kk after
+// them (the factor rows are dead by then); N and the inverse's scratch over
+// the partials once they are summed
+constexpr int kOffPart = 0;
+constexpr int kPartBytes = 20 * 3 * 64 * 16;
+constexpr int kOffAkk = kOffPart + kPartBytes;
+static_assert(kPartBytes <= kOffFac, "the partial tiles leave the factor rows intact");
+static_assert(kOffAkk + 64 * kLdA * 4 <= kOffBeta, "A_kk leaves beta intact");
+static_assert(64 * kLdA * 4 + kInvScr * 4 <= kOffAkk, "N and the inverse scratch alias the partial tiles");
+
+// Step 3 splits the ten 16x16 tile pairs (r, s), s <= r, of A_kk and of A_qk
+// by channel: wave w contracts only its own 32 channels, and the owner of a
+// tile sums the four partial tiles in a fixed order.  Owners (five tiles per
+// wave): A_kk pairs 0-2 wave 2, 3-5 wave 3, 6-7 wave 0, 8-9 wave 1; A_qk
+// pairs 0-2 wave 0, 3-5 wave 1, 6-7 wave 2, 8-9 wave 3, so that both halves
+// of each stored A_qk fragment (tiles (r, 2kb) and (r, 2kb + 1)) meet in one
+// wave.  pos: the tile's slot among its owner's five.
+__host__ __device__ constexpr int kk_owner(int p) { return p < 3 ? 2 : p < 6 ? 3 : p < 8 ? 0 : 1; }
+__host__ __device__ constexpr int kk_pos(int p) { return p < 3 ? p : p < 6 ? p - 3 : p < 8 ? p - 6 : p - 8; }
+__host__ __device__ constexpr int qk_owner(int p) { return p < 3 ? 0 : p < 6 ? 1 : p < 8 ? 2 : 3; }
+__host__ __device__ constexpr int qk_pos(int p) { return p < 3 ? p + 2 : p < 6 ? p - 1 : p < 8 ? p - 3 : p - 5; }
+
+// Step 3's sums for wave W: the four partial tiles of each tile it owns, in
+// the order (own, then writers W + 1, W + 2, W + 3), the causal masks (A_kk
+// strictly below the diagonal, A_qk on and below it), beta as A_kk's row
+// scale; A_kk to LDS in fp32 for the inverse, A_qk to the record as bf16
+// operand fragments (token block tb, k-step kb: tiles (tb, 2kb), (tb, 2kb + 1)).
+// A lane holds row 16r + n16, columns 16s + 4g4 .. + 3 of tile (r, s).
+template <int W, int MODE, bool DBG>
+__device__ __forceinline__ void reduce_tiles(const f32x4 (&own)[5], const float* sPart, float* sAkk,
+                                             const float* sBeta, uint8_t* __restrict__ rec,
+                                             float* __restrict__ dbase, int lane, int n16, int g4) {
+    constexpr int NKK = W < 2 ? 2 : 3;                             // A_kk tiles first, then A_qk
+    constexpr int KK0 = W == 0 ? 6 : W == 1 ? 8 : W == 2 ? 0 : 3;  // first A_kk pair owned
+    constexpr int QK0 = W == 0 ? 0 : W == 1 ? 3 : W == 2 ? 6 : 8;  // first A_qk pair owned
+    f32x4 qt[3];
+#pragma unroll
+    for (int i = 0; i < 5; i++) {
+        const bool kk = i < NKK;
+        const int p = kk ? KK0 + i : QK0 + i - NKK;
+        const int r = pair_row(p), s = p - r * (r + 1) / 2;
+        f32x4 t = zero4();
+        if (!kk || MODE != kModeGLA) {
+            const int tau = kk ? p : 10 + p;
+            t = own[i];
+#pragma unroll
+            for (int k = 0; k < 3; k++) t += *reinterpret_cast<const f32x4*>(sPart + ((tau * 3 + k) * 64 + lane) * 4);
+        }
+        if (s == r) {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (4 * g4 + e > n16 || (kk && 4 * g4 + e == n16)) t[e] = 0.f;
+        }
+        if (kk) {
+            const float b = sBeta[16 * r + n16];
+#pragma unroll
+            for (int e = 0; e < 4; e++) t[e] *= b;
+            *reinterpret_cast<f32x4*>(sAkk + (16 * r + n16) * kLdA + 16 * s + 4 * g4) = t;
+        } else {
+            qt[i - NKK] = t;
+        }
+        if (DBG)
+#pragma unroll
+            for (int e = 0; e < 4; e++) dbase[8192 + (kk ? 0 : 4096) + (16 * r + n16) * 64 + 16 * s + 4 * g4 + e] = t[e];
+    }
+    auto put = [&](int tb, int kb, const f32x4& lo, const f32x4& hi) {
+        *reinterpret_cast<bf16x8*>(rec + REC_A + (rec_a_frag(tb, kb) * 64 + lane) * 16) = pack_frag(lo, hi);
+    };
+    if constexpr (W == 0) {
+        put(0, 0, qt[0], zero4());
+        put(1, 0, qt[1], qt[2]);
+    } else if constexpr (W == 1) {
+        put(2, 0, qt[0], qt[1]);
+        put(2, 1, qt[2], zero4());
+    } else if constexpr (W == 2) {
+        put(3, 0, qt[0], qt[1]);
+    } else {
+        put(3, 1, qt[0], qt[1]);
+    }
+}
 
 // One workgroup per (chunk, head), 4 waves.  Work on single elements is split
 // by channel: wave w owns channels [32w, 32w + 32) of all 64 tokens, lane
@@ -115,8 +194,6 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     __shared__ __align__(16) uint8_t smem[kSmemIntra];
     float* sG = reinterpret_cast<float*>(smem);                       // [64][kLdG]
-    bf16* sRK = reinterpret_cast<bf16*>(smem + kOffRK);               // [64][kLdK]
-    bf16* sRQ = reinterpret_cast<bf16*>(smem + kOffRQ);               // [64][kLdK]
     float* sFac = reinterpret_cast<float*>(smem + kOffFac);           // [kNFac][128]
     float* sBeta = reinterpret_cast<float*>(smem + kOffBeta);         // [64]
 
@@ -296,10 +373,12 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         __syncthreads();
     }
 
-    // ---- 2. per element: row and column factors, the row operands, K.F, and
-    //      token-contiguous copies via an exact selection product: MFMA(X rows,
-    //      one-hot B) returns X in the C layout (4 consecutive tokens of one
-    //      channel per lane), MFMA(one-hot A, X rows) returns X^T in it
+    // ---- 2. per element: row and column factors, the row operands and K.F
+    //      (kept in registers: lane (n, g) of wave w holds them for token rows
+    //      16t + n, channels 32w + 8g .. + 7, the operand layout of k-step w),
+    //      and token-contiguous copies via an exact selection product: MFMA(X
+    //      rows, one-hot B) returns X in the C layout (4 consecutive tokens of
+    //      one channel per lane), MFMA(one-hot A, X rows) returns X^T in it
     bf16x8 sel[2];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -307,6 +386,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         sel[1][e] = (bf16)((8 * g4 + e == 16 + n16) ? 1.f : 0.f);
     }
     bf16x8 kgf[2][2], vf[2][2];     // (K . Gamma)^T, V^T fragments [token kstep][16-channel half]
+    bf16x8 rkr[4], rqr[4];          // rows k . E, q . E of token block t
+    float kfr[4][8];                // k . F of token block t
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
         f32x4 tkg[2][2], tkb[2][2], tv[2][2];
@@ -336,13 +417,10 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 akg[e] = (bf16)(kE * Y8[e]);
                 aq[e] = (bf16)(qE * Y8[e]);
                 akb[e] = (bf16)(kF * Z8[e]);
-                L8[e] = kF;
+                kfr[tt][e] = kF;
             }
-            // K.F over L: each lane rewrites only the elements it read
-            *reinterpret_cast<float4*>(sG + row * kLdG + cw) = make_float4(L8[0], L8[1], L8[2], L8[3]);
-            *reinterpret_cast<float4*>(sG + row * kLdG + cw + 4) = make_float4(L8[4], L8[5], L8[6], L8[7]);
-            *reinterpret_cast<bf16x8*>(sRK + row * kLdK + cw) = rk;
-            *reinterpret_cast<bf16x8*>(sRQ + row * kLdK + cw) = rq;
+            rkr[tt] = rk;
+            rqr[tt] = rq;
             f32x4 qt[2];
 #pragma unroll
             for (int cb = 0; cb < 2; cb++) {
@@ -364,71 +442,53 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 3. A_kk and A_qk tiles [LA-KDA §7.2, §7.3], balanced over the waves
-    const int pb = pair_beg(w), pe = pair_beg(w + 1);
-    f32x4 akk[3], aqk[3];
+    // ---- 3. A_kk and A_qk [LA-KDA §7.2, §7.3], split by channel: every wave
+    //      forms the partial tiles of its own 32 channels (k-step w) from its
+    //      registers; each tile's owner sums the four partials in a fixed order
+    float* sPart = reinterpret_cast<float*>(smem + kOffPart);          // [20][3][64] f32x4
+    float* sAkk = reinterpret_cast<float*>(smem + kOffAkk);            // [64][kLdA]
+    f32x4 own[5];
 #pragma unroll
-    for (int sl = 0; sl < 3; sl++) {
-        akk[sl] = zero4();
-        aqk[sl] = zero4();
-        const int p = pb + sl;
-        if (p < pe) {
-            const int r = pair_row(p), s = p - r * (r + 1) / 2;
+    for (int i = 0; i < 5; i++) own[i] = zero4();
+    auto part_out = [&](int tau, int owner, int pos, const f32x4& t) {
+        if (w == owner) own[pos] = t;
+        else *reinterpret_cast<f32x4*>(sPart + ((tau * 3 + ((w - owner - 1) & 3)) * 64 + lane) * 4) = t;
+    };
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int c0 = 32 * ks + 8 * g4;
-                const bf16x8 rk = *reinterpret_cast<const bf16x8*>(sRK + (16 * r + n16) * kLdK + c0);
-                const bf16x8 rq = *reinterpret_cast<const bf16x8*>(sRQ + (16 * r + n16) * kLdK + c0);
-                float kf[8], X8[8];
-                load8f(sG + (16 * s + n16) * kLdG + c0, kf);
-                load8f(sFac + (kFX + p) * 128 + c0, X8);
-                bf16x8 col;
+    for (int p = 0; p < 10; p++) {
+        const int r = pair_row(p), s = p - r * (r + 1) / 2;
+        float X8[8];
+        load8f(sFac + (kFX + p) * 128 + cw, X8);
+        bf16x8 col;
 #pragma unroll
-                for (int e = 0; e < 8; e++) col[e] = (bf16)(kf[e] * X8[e]);
-                if constexpr (MODE != kModeGLA) akk[sl] = mfma_bf16(rk, col, akk[sl]);
-                aqk[sl] = mfma_bf16(rq, col, aqk[sl]);
-            }
-        }
+        for (int e = 0; e < 8; e++) col[e] = (bf16)(kfr[s][e] * X8[e]);
+        // columns as the A operand: the lane receives row 16r + n, columns 16s + 4g .. + 3
+        if constexpr (MODE != kModeGLA) part_out(p, kk_owner(p), kk_pos(p), mfma_bf16(col, rkr[r], zero4()));
+        part_out(10 + p, qk_owner(p), qk_pos(p), mfma_bf16(col, rqr[r], zero4()));
     }
-    __syncthreads();   // L/K.F and the row operands are dead from here
-
-    float* sAkk = reinterpret_cast<float*>(smem);                     // [64][kLdA]
-    float* sAqk = sAkk + 64 * kLdA;
-    float* sN = sAqk + 64 * kLdA;
-    float* sP = sN + 64 * kLdA;                                       // inverse scratch
-    // causal masks and the beta row scale of A_kk; tiles above the diagonal are zero
-#pragma unroll
-    for (int sl = 0; sl < 3; sl++) {
-        const int p = pb + sl;
-        if (p < pe) {
-            const int r = pair_row(p), s = p - r * (r + 1) / 2;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int ii = 4 * g4 + e, row = 16 * r + ii, col = 16 * s + n16;
-                float vk = akk[sl][e], vq = aqk[sl][e];
-                if (s == r) {
-                    if (n16 >= ii) vk = 0.f;
-                    if (n16 > ii) vq = 0.f;
-                }
-                sAkk[row * kLdA + col] = vk * sBeta[row];
-                sAqk[row * kLdA + col] = vq;
-            }
-        }
+    __syncthreads();
+    switch (w) {
+        case 0: reduce_tiles<0, MODE, DBG>(own, sPart, sAkk, sBeta, rec, dbase, lane, n16, g4); break;
+        case 1: reduce_tiles<1, MODE, DBG>(own, sPart, sAkk, sBeta, rec, dbase, lane, n16, g4); break;
+        case 2: reduce_tiles<2, MODE, DBG>(own, sPart, sAkk, sBeta, rec, dbase, lane, n16, g4); break;
+        default: reduce_tiles<3, MODE, DBG>(own, sPart, sAkk, sBeta, rec, dbase, lane, n16, g4); break;
     }
-    for (int idx = tid; idx < 6 * 256; idx += 256) {     // tiles (r, s), s > r
+    float* sN = reinterpret_cast<float*>(smem);                         // [64][kLdA], over the partials
+    float* sP = sN + 64 * kLdA;                                         // inverse scratch
+    if (DBG)
+        for (int idx = tid; idx < 6 * 256; idx += 256) {  // A_kk and A_qk tiles (r, s), s > r, are zero
+            const int t = idx >> 8, e = idx & 255;
+            const int r = t < 3 ? 0 : t < 5 ? 1 : 2, s = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
+            const int at = (16 * r + (e >> 4)) * 64 + 16 * s + (e & 15);
+            dbase[8192 + at] = 0.f;
+            dbase[8192 + 4096 + at] = 0.f;
+        }
+    __syncthreads();   // the partials are summed: N and its scratch may overwrite them
+    for (int idx = tid; idx < 6 * 256; idx += 256) {      // N's blocks (r, s), s > r, are zero
         const int t = idx >> 8, e = idx & 255;
         const int r = t < 3 ? 0 : t < 5 ? 1 : 2, s = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
-        const int row = 16 * r + (e >> 4), col = 16 * s + (e & 15);
-        sAkk[row * kLdA + col] = 0.f;
-        sAqk[row * kLdA + col] = 0.f;
+        sN[(16 * r + (e >> 4)) * kLdA + 16 * s + (e & 15)] = 0.f;
     }
-    for (int idx = tid; idx < 4096; idx += 256) sN[(idx >> 6) * kLdA + (idx & 63)] = 0.f;
-    __syncthreads();
-    if (DBG)
-        for (int idx = tid; idx < 4096; idx += 256) {
-            dbase[8192 + idx] = sAkk[(idx >> 6) * kLdA + (idx & 63)];
-            dbase[8192 + 4096 + idx] = sAqk[(idx >> 6) * kLdA + (idx & 63)];
-        }
 
     // ---- 4. N = (I + A_kk)^{-1} in fp32, 16x16 blocks ----
     unit_lower_inverse(sAkk, sN, sP, w, n16, g4);
@@ -454,17 +514,6 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             const f32x4 t1 = {n1.x * b1.x, n1.y * b1.y, n1.z * b1.z, n1.w * b1.w};
             tf[tb][kb] = pack_frag(t0, t1);
         }
-    // A_qk rows of token block w, same k-slot order, to the record (the
-    // all-zero fragments above the diagonal are not stored)
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-        if (!rec_a_stored(w, kb)) continue;
-        const int row = 16 * w + n16, j0 = 32 * kb + 4 * g4, j1 = j0 + 16;
-        const float4 a0 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j0);
-        const float4 a1 = *reinterpret_cast<const float4*>(sAqk + row * kLdA + j1);
-        const f32x4 x0 = {a0.x, a0.y, a0.z, a0.w}, x1 = {a1.x, a1.y, a1.z, a1.w};
-        *reinterpret_cast<bf16x8*>(rec + REC_A + (rec_a_frag(w, kb) * 64 + lane) * 16) = pack_frag(x0, x1);
-    }
     // W^T = (K . Gamma)^T T^T: tiles [channel][token], stored negated as the
     // chain's A operand (token block tb, k-step w)
 #pragma unroll
