@@ -138,7 +138,7 @@ __device__ __forceinline__ void reduce_tiles(const f32x4 (&own)[5], const float*
             for (int e = 0; e < 4; e++) dbase[8192 + (kk ? 0 : 4096) + (16 * r + n16) * 64 + 16 * s + 4 * g4 + e] = t[e];
     }
     auto put = [&](int tb, int kb, const f32x4& lo, const f32x4& hi) {
-        *reinterpret_cast<bf16x8*>(rec + REC_A + (rec_a_frag(tb, kb) * 64 + lane) * 16) = pack_frag(lo, hi);
+        __builtin_nontemporal_store(pack_frag(lo, hi), reinterpret_cast<bf16x8*>(rec + REC_A + (rec_a_frag(tb, kb) * 64 + lane) * 16));
     };
     if constexpr (W == 0) {
         put(0, 0, qt[0], zero4());
@@ -364,7 +364,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             F[(kFZ + 2) * 128] = ex2(L63 - L47);
             F[(kFL + 2) * 128] = L47;
             F[(kFL + 3) * 128] = L63;
-            reinterpret_cast<float*>(rec + REC_G)[c] = ex2(L63);
+            __builtin_nontemporal_store(ex2(L63), reinterpret_cast<float*>(rec + REC_G) + c);
         }
     }
     __syncthreads();
@@ -430,14 +430,13 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 qt[cb] = mfma_bf16(sel[cb], aq, zero4());
             }
             // (Q . Gamma)^T tiles [channel][token] as the chain's A operand (k-step w)
-            *reinterpret_cast<bf16x8*>(rec + REC_Q + ((tt * 4 + w) * 64 + lane) * 16) = pack_frag(qt[0], qt[1]);
+            __builtin_nontemporal_store(pack_frag(qt[0], qt[1]), reinterpret_cast<bf16x8*>(rec + REC_Q + ((tt * 4 + w) * 64 + lane) * 16));
         }
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
             kgf[kb][cb] = pack_frag(tkg[0][cb], tkg[1][cb]);
             vf[kb][cb] = pack_frag(tv[0][cb], tv[1][cb]);
-            *reinterpret_cast<bf16x8*>(rec + REC_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16) =
-                pack_frag(tkb[0][cb], tkb[1][cb]);
+            __builtin_nontemporal_store(pack_frag(tkb[0][cb], tkb[1][cb]), reinterpret_cast<bf16x8*>(rec + REC_K + (((w * 2 + cb) * 2 + kb) * 64 + lane) * 16));
         }
     }
     __syncthreads();
@@ -525,7 +524,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 wt0 = mfma_bf16(kgf[kb][0], tf[tb][kb], wt0);
                 wt1 = mfma_bf16(kgf[kb][1], tf[tb][kb], wt1);
             }
-            *reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16) = pack_frag_neg(wt0, wt1);
+            __builtin_nontemporal_store(pack_frag_neg(wt0, wt1), reinterpret_cast<bf16x8*>(rec + REC_W + ((tb * 4 + w) * 64 + lane) * 16));
         }
     }
     // U = T V: tiles (slice 2w + cb, token block tb)
@@ -536,7 +535,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             f32x4 u = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) u = mfma_bf16(tf[tb][kb], vf[kb][cb], u);
-            *reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8) = pack4(u);
+            __builtin_nontemporal_store(pack4(u), reinterpret_cast<bf16x4*>(rec + REC_U + (((2 * w + cb) * 4 + tb) * 64 + lane) * 8));
         }
 }
 
