@@ -84,17 +84,24 @@ void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     const int n = nh / H, h = nh % H;
     __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
+    // token t's inputs are loaded during step t - 1 (as in the fold)
+    auto token = [&](TokenIn<DK, DV>& in, int t) {
+        const size_t tok = ((size_t)n * W + t) * H + h;
+        load_token<DK, DV, Tin, true, kModeKDA, false>(in, k + tok * DK, v + tok * DV, z + tok * DK,
+                                                       bl[tok], q + tok * DK);
+    };
+    TokenIn<DK, DV> cur, nxt;
+    if (W > 0) token(cur, 0);
     float4 Sv[16];
     load_state<DK, DV, false>(Sv, state + (size_t)nh * DK * DV);
     const float ea = expf(A[h]);
     for (int t = 0; t < W; t++) {
-        const size_t tok = ((size_t)n * W + t) * H + h;
+        if (t + 1 < W) token(nxt, t + 1);
         if (t > 0) __syncthreads();     // the previous step's readers of the LDS vectors are done
-        TokenIn<DK, DV> in;
-        load_token<DK, DV, Tin, true, kModeKDA, false>(in, k + tok * DK, v + tok * DV, z + tok * DK,
-                                                       bl[tok], q + tok * DK);
-        kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, in, ea, o + tok * DV, s_al, s_k,
-                                                                  s_q, s_red, s_qk);
+        kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, cur, ea,
+                                                                  o + (((size_t)n * W + t) * H + h) * DV,
+                                                                  s_al, s_k, s_q, s_red, s_qk);
+        cur = nxt;
     }
 }
 
