@@ -232,20 +232,45 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
     __shared__ __align__(16) float s_red[2][D / 16][D];
     __shared__ float s_tmp[NT >= 64 ? NT / 64 : NT];
 
+    // the token's inputs first (the convolution's carried rows, new input and
+    // taps, the gate and beta logits), then the state stream that is the cost
+    // of this kernel: the convolution and the norms wait on the former alone
+    constexpr int KPT = TokenIn<D, D>::KPT;
+    Tin xr[3][KPT][4];
+    float wt[3][KPT][4], zr[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; j++) {
+        const int i = tid + j * NT;
+        zr[j] = 0.f;
+        if (i < D) {
+#pragma unroll
+            for (int which = 0; which < 3; which++) {
+                const Tin* x = which == 0 ? q_in : which == 1 ? k_in : v_in;
+                const Tin* cs = conv_state + ((size_t)n * 3 + which) * 3 * H * D;
+#pragma unroll
+                for (int r = 0; r < 3; r++) xr[which][j][r] = cs[((size_t)r * H + h) * D + i];
+                xr[which][j][3] = x[(size_t)nh * D + i];
+#pragma unroll
+                for (int r = 0; r < 4; r++) wt[which][j][r] = conv_w[(((size_t)which * H + h) * D + i) * 4 + r];
+            }
+            zr[j] = z[(size_t)nh * D + i];
+        }
+    }
+    const float b_logit = bl[nh], ea = expf(A[h]);
     float4 Sv[16];
     load_state<D, D>(Sv, S);
 #pragma unroll
-    for (int which = 0; which < 3; which++) {
-        const Tin* x = which == 0 ? q_in : which == 1 ? k_in : v_in;
-        Tin* cs = conv_state + ((size_t)n * 3 + which) * 3 * H * D;
-        for (int i = tid; i < D; i += NT) {
-            const Tin r0 = cs[((size_t)0 * H + h) * D + i], r1 = cs[((size_t)1 * H + h) * D + i],
-                      r2 = cs[((size_t)2 * H + h) * D + i], r3 = x[(size_t)nh * D + i];
-            s_in[which][i] = swish(conv4(conv_w + (((size_t)which * H + h) * D + i) * 4, to_f32(r0),
-                                         to_f32(r1), to_f32(r2), to_f32(r3)));
-            cs[((size_t)0 * H + h) * D + i] = r1;
-            cs[((size_t)1 * H + h) * D + i] = r2;
-            cs[((size_t)2 * H + h) * D + i] = r3;
+    for (int j = 0; j < KPT; j++) {
+        const int i = tid + j * NT;
+        if (i < D) {
+#pragma unroll
+            for (int which = 0; which < 3; which++) {
+                Tin* cs = conv_state + ((size_t)n * 3 + which) * 3 * H * D;
+                s_in[which][i] = swish(conv4(wt[which][j], to_f32(xr[which][j][0]), to_f32(xr[which][j][1]),
+                                             to_f32(xr[which][j][2]), to_f32(xr[which][j][3])));
+#pragma unroll
+                for (int r = 0; r < 3; r++) cs[((size_t)r * H + h) * D + i] = xr[which][j][r + 1];
+            }
         }
     }
     __syncthreads();
@@ -262,8 +287,22 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
     }
     __syncthreads();
     TokenIn<D, D> in;
-    load_token<D, D, float, true>(in, s_in[1], s_in[2], z + (size_t)nh * D, bl[nh], s_in[0]);
-    kda_token_step<D, D, float, true>(Sv, in, expf(A[h]), s_o, s_al, s_k, s_q, s_red, s_qk);
+#pragma unroll
+    for (int j = 0; j < KPT; j++) {
+        const int i = tid + j * NT;
+        in.z[j] = in.k[j] = in.q[j] = 0.f;
+        if (i < D) {
+            in.z[j] = zr[j];
+            in.k[j] = s_in[1][i];
+            in.q[j] = s_in[0][i];
+        }
+    }
+    const int c0 = StateLayout<D, D>::col0(tid);
+#pragma unroll
+    for (int c = 0; c < 4; c++) in.v[c] = s_in[2][c0 + c];
+    in.b = b_logit;
+    // each updated state row is stored as soon as it is formed
+    kda_token_step<D, D, float, true, kModeKDA, true>(Sv, in, ea, s_o, s_al, s_k, s_q, s_red, s_qk, S);
     __syncthreads();
     float so = 0.f;
     for (int i = tid; i < D; i += NT) so = __builtin_fmaf(s_o[i], s_o[i], so);
@@ -271,7 +310,6 @@ void layer_step_kernel(const Tin* __restrict__ q_in, const Tin* __restrict__ k_i
     for (int i = tid; i < D; i += NT)
         y[(size_t)nh * D + i] =
             from_f32<Tin>(sigmoid_f<true>(to_f32(gate[(size_t)nh * D + i])) * (s_o[i] * r) * norm_w[i]);
-    store_state<D, D>(Sv, S);
 }
 
 }  // namespace
