@@ -484,27 +484,32 @@ def bench_layer(args, kda, torch, KI, call_ms, step_ms):
                         B=dc.N, zero_h0=False)
     x = KI.make_layer(lc, device=dev, seed=0, T=1)
     tok = {k: x[k][:, 0].contiguous() for k in ("q_in", "k_in", "v_in", "gate", "z", "b")}
-    st, cs = x["h0"].clone(), x["conv_state0"].clone()
+    # the core decode's rotation: DECODE_STATE_SETS sets of states stepped in
+    # turn, so that no step finds its state in the Infinity Cache
+    sts = [x["h0"].clone() for _ in range(DECODE_STATE_SETS)]
+    css = [x["conv_state0"].clone() for _ in range(DECODE_STATE_SETS)]
 
-    def step():
-        return kda.kda_layer_step(tok["q_in"], tok["k_in"], tok["v_in"], x["conv_w"], cs, tok["z"],
-                                  tok["b"], x["A"], st, tok["gate"], x["norm_w"])
-    for _ in range(2):
-        step()
+    def step(i):
+        u = i % DECODE_STATE_SETS
+        return kda.kda_layer_step(tok["q_in"], tok["k_in"], tok["v_in"], x["conv_w"], css[u], tok["z"],
+                                  tok["b"], x["A"], sts[u], tok["gate"], x["norm_w"])
+    for i in range(2 * DECODE_STATE_SETS):
+        step(i)
     torch.cuda.synchronize()
     stimes = []
-    for _ in range(16 * args.decode_reps):
+    for i in range(16 * args.decode_reps):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        step()
+        step(i)
         b.record()
         stimes.append((a, b))
     torch.cuda.synchronize()
     sms = sum(a.elapsed_time(b) for a, b in stimes) / len(stimes)
     return {
         "workload": "long_1m and decode_256 shapes with projections, convolution taps, "
-                    "carried convolution states, output-gate logits and RMSNorm weight",
+                    "carried convolution states, output-gate logits and RMSNorm weight; "
+                    f"decode steps {DECODE_STATE_SETS} sets of states in turn",
         "prefill_ms_per_call": round(ms, 4),
         "prefill_tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "prefill_vs_core_call": round(ms / call_ms, 3),
@@ -848,7 +853,7 @@ def main():
     layer = None
     if not args.no_layer:
         layer = bench_layer(args, kda, torch, KI, extra["call_ms_events"],
-                            dec["cache_warm"]["ms_per_step_mean"] if dec else float("nan"))
+                            dec["ms_per_step_mean"] if dec else float("nan"))
     family = None
     if not args.no_family:
         family = bench_family(args, kda, torch, KI, {"intra": extra["kernels_ms"]["intra"],
