@@ -678,6 +678,22 @@ __device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[
     }
 }
 
+// The gate logits of the rows this thread stores for one chunk (rows past
+// the end of the sequence read its last row; they are never stored).  The
+// caller issues them before the record prefetch of the step: a wave's loads
+// complete in order, so loads issued after the prefetch would wait for it.
+template <bool GATE>
+__device__ __forceinline__ void load_gate_rows(bf16x8 (&gpre)[4], const OutGate& og, int tok0, int len,
+                                               int H, int h, int tid) {
+    if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = i * 256 + tid, row = min(idx >> 4, len - 1), c8 = (idx & 15) * 8;
+            gpre[i] = *reinterpret_cast<const bf16x8*>(og.gate + ((size_t)(tok0 + row) * H + h) * 128 + c8);
+        }
+    }
+}
+
 // One chunk for one wave over all slices.  KDA: V~ = U - W S,
 // O = (Q . Gamma) S + A_qk V~, S <- Diag(gamma_C) S + Kbar^T V~.  DPLR:
 // X~ = Wb S, O = Q' S + Uo, S <- Diag(gamma_C) S + Abar^T X~ + Cs.
@@ -686,7 +702,7 @@ __device__ __forceinline__ void out_step(const OutFrags<NS>& f, int cid, int tok
                                          f32x4 (&accS)[NS][2], bf16* sS, bf16* sVt, bf16* sO,
                                          bf16* __restrict__ o, float* __restrict__ dbgS, int H,
                                          int h, int w, int lane, int n16, int g4, int tid,
-                                         const OutGate& og, int sb) {
+                                         const OutGate& og, int sb, const bf16x8 (&gpre)[4]) {
     constexpr bool DPLR = CK == kChainDPLR;
     if (DBG) {
 #pragma unroll
@@ -698,25 +714,6 @@ __device__ __forceinline__ void out_step(const OutFrags<NS>& f, int cid, int tok
                     const int row = 32 * w + 16 * b + 4 * g4 + e;
                     dbgS[(((size_t)cid * H + h) * 128 + row) * 128 + 16 * (sb + sl) + n16] = accS[sl][b][e];
                 }
-    }
-    // the gate logits of the rows this thread stores, issued before the
-    // chunk's products so that their latency hides under them
-    bf16x8 gpre[4];
-    if constexpr (GATE) {
-        auto gate_row = [&](int i) {
-            const int idx = i * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-            return *reinterpret_cast<const bf16x8*>(og.gate + ((size_t)(tok0 + row) * H + h) * 128 + c8);
-        };
-        if (len >= C) {            // a full chunk (uniform): no per-row test
-#pragma unroll
-            for (int i = 0; i < 4; i++) gpre[i] = gate_row(i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                gpre[i] = bf16x8{};
-                if (i * 16 + (tid >> 4) < len) gpre[i] = gate_row(i);
-            }
-        }
     }
     f32x4 accO[NS];
     // V~ and the (Q . Gamma) S part of O, four slices at a time
@@ -823,19 +820,23 @@ __device__ __forceinline__ void out_body(const uint8_t* __restrict__ recs, const
     for (int ci = 0; ci < nfull; ci += D) {
 #pragma unroll
         for (int u = 0; u < D; u++) {
+            const int t0 = (ci + u) * C;
+            bf16x8 gpre[4];
+            load_gate_rows<GATE>(gpre, og, seg_tok0 + t0, seg_len - t0, H, h, tid);
             // unconditional prefetch (index clamped) keeps the wait counts exact
             load_out_frags<CK, NS>(F[(u + D - 1) % D], rec(min(ci + u + D - 1, nch - 1)), w, lane, g4, sb);
-            const int t0 = (ci + u) * C;
             out_step<DBG, GATE, CK, NS>(F[u], c0 + ci + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt, sO, o,
-                                        dbgS, H, h, w, lane, n16, g4, tid, og, sb);
+                                        dbgS, H, h, w, lane, n16, g4, tid, og, sb, gpre);
         }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; u++)
         if (nfull + u < nch) {
             const int t0 = (nfull + u) * C;
+            bf16x8 gpre[4];
+            load_gate_rows<GATE>(gpre, og, seg_tok0 + t0, seg_len - t0, H, h, tid);
             out_step<DBG, GATE, CK, NS>(F[u], c0 + nfull + u, seg_tok0 + t0, seg_len - t0, accS, sS, sVt,
-                                        sO, o, dbgS, H, h, w, lane, n16, g4, tid, og, sb);
+                                        sO, o, dbgS, H, h, w, lane, n16, g4, tid, og, sb, gpre);
         }
 
     if (last && hT) {
