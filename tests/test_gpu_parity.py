@@ -638,6 +638,25 @@ def test_verify_then_fold_bit_identical_to_recurrent_steps(kda, dtype, dk):
     assert e <= (TOL_F32 if dtype == "fp32" else TOL_BF16)
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("fp32", 16)])
+def test_verify_single_token_window(kda, dtype, dk):
+    """A one-token window (no next token to load during the step): the
+    verify output equals one recurrent step's output bit for bit, and the
+    checkpoint is untouched."""
+    N, H, W = 5, 2, 1
+    run, steps, win = _fold_window(dtype, dk, N, H, W, seed=26)
+    A = run["A"].cuda()
+    st0 = run["state"].cuda().contiguous()
+    ck = st0.clone()
+    dev = {key: win[key].cuda().contiguous() for key in win}
+    o = kda.kda_recurrent_verify(dev["q"], dev["k"], dev["v"], dev["z"], dev["b"], A, ck)
+    sd = to_dev(steps[0])
+    cur = st0.clone()
+    ref = kda.kda_recurrent_step(sd["q"], sd["k"], sd["v"], sd["z"], sd["b"], A, cur)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, 0], ref) and torch.equal(ck, st0)
+
+
 def test_verify_reads_state_only(kda):
     """The checkpoint state is bit-for-bit unchanged by the verify pass, and
     W = 0 is a no-op."""
