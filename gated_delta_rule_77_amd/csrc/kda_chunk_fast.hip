@@ -22,7 +22,8 @@
 //               cumulative decay, A_kk and A_qk on MFMA, the fp32 triangular
 //               inverse, W, U, Q . Gamma and Kbar on MFMA.  It writes them as
 //               bf16 operand fragments already in the order the chain
-//               kernels' lanes load them.
+//               kernels' lanes load them, with nontemporal stores (the later
+//               launches read them back from HBM, never from a cache).
 //   transition  per (segment, head): the chain over the segment's chunks on
 //               the augmented state [R | M] (see the chain section below);
 //   compose     per (sequence, head): segment start states in fp32;
@@ -163,6 +164,9 @@ __device__ __forceinline__ void reduce_tiles(const f32x4 (&own)[5], const float*
 //   A_kk/A_qk tile (r, s):  rows (k|q) . E  with  columns (k . F) . X(r,s)
 //   K . Gamma = (k . E) . Y(r),  Q . Gamma = (q . E) . Y(r),  Kbar = (k . F) . Z(r)
 // (X(r,s) <= 1 off the diagonal, X(r,r) = 2^(L_s - L_e) < e^80 on it).
+// The row operands and k . F stay in the registers of the wave that formed
+// them: each wave contracts its own k-step for all ten tile pairs, and the
+// four partial tiles of a pair are summed by its owner (step 3).
 // With CONV, q, k, v are the layer's projections and step 1 applies the
 // layer's steps before the core ([LA-KDA §5.3]): the depthwise causal
 // convolution (four taps oldest first, the sequence's first three inputs from
