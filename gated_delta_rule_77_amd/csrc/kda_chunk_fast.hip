@@ -950,6 +950,37 @@ __device__ __forceinline__ void stage_store(const StageRegs& r, uint8_t* st, int
     if (t < 32) *reinterpret_cast<u32x4*>(st + TS::G + t * 16) = r.g;
 }
 
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): vm_wait(n) waits for vector memory operations only, down to n
+// outstanding; kWaitLgkm0 for LDS and scalar memory operations only
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm4 = vm_wait(4), kWaitVm6 = vm_wait(6);
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);   // LDS and scalar memory only
+
+// KDA and GLA stages are copied straight from global memory to LDS (16 bytes
+// per lane; a lane's bytes land at the instruction's LDS base + 16 lane): wave
+// w copies the 1 KiB run [1024 w, 1024 w + 1024) of each 8 KiB half of W,
+// Kbar and U, and lanes 0-31 of wave 0 the 512 bytes of gamma_C.  Six loads
+// per wave and chunk (four for GLA, which has no W), one more on wave 0.
+template <int CK>
+__device__ __forceinline__ void stage_dma(const uint8_t* __restrict__ rec, uint8_t* st, int w, int lane) {
+    static_assert(CK != kChainDPLR, "the DPLR stage is copied through registers");
+    using RL = RecLayout<false>;
+    using TS = TransStage<false>;
+    auto cp = [&](int roff, int soff) {
+        __builtin_amdgcn_global_load_lds(rec + roff + (w * 64 + lane) * 16, st + soff + w * 1024, 16, 0, 0);
+    };
+    if constexpr (CK != kChainGLA) {
+        cp(RL::W, TS::W);
+        cp(RL::W + 8192, TS::W + 8192);
+    }
+    cp(RL::K, TS::K);
+    cp(RL::K + 8192, TS::K + 8192);
+    cp(RL::U, TS::U);
+    cp(RL::U + 8192, TS::U + 8192);
+    if (w == 0 && lane < 32) __builtin_amdgcn_global_load_lds(rec + RL::G + lane * 16, st + TS::G, 16, 0, 0);
+}
+
 // gamma_C of the rows 16 RT + 4 g4 + e (e = 0..3) that lane (n16, g4) holds in
 // row tile RT.  Lane (n16, g4) has read gv0 = gamma_C[16 (n16 >> 2) + 4 g4 +
 // (n16 & 3)] and gv1 the same 64 rows on; the value of element e of tile RT
@@ -1083,10 +1114,36 @@ __device__ __forceinline__ void trans_body(const uint8_t* __restrict__ recs, int
                 const int row = 16 * rt + 4 * g4 + e, col = 16 * (s0 + j) + n16;
                 acc[rt][j][e] = (row == col - 128) ? 1.f : 0.f;
             }
-    if (nch > 0) {
-        auto rec = [&](int c) {
-            return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * RecLayout<DPLR>::BYTES;
-        };
+    auto rec = [&](int c) {
+        return recs + ((size_t)(c0 + min(c, nch - 1)) * H + h) * RecLayout<DPLR>::BYTES;
+    };
+    if constexpr (!DPLR) {
+        // chunk c sits in stage c % 3, copied there by DMA two chunks ahead;
+        // the loads are unconditional (index clamped), so that a wave's own
+        // copy of chunk c is complete once at most one chunk's loads remain
+        // (the loop issues no other vector memory operation, which the
+        // explicit wait below relies on)
+        if (nch > 0) {
+            stage_dma<CK>(rec(0), stage[0], w, lane);
+            stage_dma<CK>(rec(1), stage[1], w, lane);
+            for (int c = 0; c < nch; c++) {
+                if constexpr (CK == kChainGLA) __builtin_amdgcn_s_waitcnt(kWaitVm4);
+                else __builtin_amdgcn_s_waitcnt(kWaitVm6);
+                // every wave's copy of chunk c has landed, and every wave is
+                // done with chunk c - 1, whose stage the next copy overwrites.
+                // A plain barrier: the LDS is the CU's own, the wait above
+                // covers this wave's copies, and a fenced barrier would also
+                // wait for the next chunk's copy still in flight
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                asm volatile("" ::: "memory");   // no LDS access moves across the barrier
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                stage_dma<CK>(rec(c + 2), stage[(c + 2) % 3], w, lane);
+                trans_chunk<CK, NJ>(stage[c % 3], acc, s0, is_m, lane, g4);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup's LDS
+        }
+    } else if (nch > 0) {
         // chunk c sits in stage c & 1; its copy passes through register set c & 1
         StageRegs R0 = stage_load<CK>(rec(0), tid);
         StageRegs R1 = stage_load<CK>(rec(1), tid);
@@ -1133,7 +1190,7 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
     const int2 ss = seqsegs[sg.x];
     if (sg.w == ss.y - 1) return;          // the last segment's transition is never needed
-    __shared__ __align__(16) uint8_t stage[2][TransStage<DPLR>::BYTES];
+    __shared__ __align__(16) uint8_t stage[DPLR ? 2 : 3][TransStage<DPLR>::BYTES];
     if (chains_split(hdr, H, split_grid))
         trans_body<CK, 1>(recs, sg.y, sg.z, H, h, seg_id, half, rm, stage);
     else if (half == 0)
