@@ -899,8 +899,9 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
 // tiles): its S fragments for V~ = U - W S and its V~ fragments for the state
 // update come from its own registers (two stacked C tiles are exactly one
 // operand fragment).  Only the chunk's W, Kbar, U and gamma_C are shared: the
-// workgroup copies them into a double-buffered LDS stage, two chunks ahead
-// through registers, with one barrier per chunk.
+// workgroup copies them into LDS two chunks ahead with one barrier per chunk
+// (KDA and GLA: direct global-to-LDS loads into a ring of three stages;
+// DPLR, whose stage is larger: through registers into two stages).
 // stage of one chunk: W, Kbar, U (KDA) or Cs (DPLR) and gamma_C
 template <bool DPLR> struct TransStage {
     static constexpr int W = 0, K = 16384, U = 32768, C = 32768;
