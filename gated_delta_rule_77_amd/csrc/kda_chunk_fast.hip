@@ -36,6 +36,8 @@
 // just before block r as reference: the row factor e^{G_i - G_ref} <= 1, the
 // column factor e^{G_ref - G_j} <= 1 off the diagonal and < e^{80} on it.
 // Gamma, Kbar and gamma_C only ever carry factors <= 1.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_fast_common.hpp"
 #include "kda_internal.hpp"
@@ -1124,7 +1126,10 @@ __device__ __forceinline__ void trans_body(const uint8_t* __restrict__ recs, int
         // copy of chunk c is complete once at most one chunk's loads remain
         // (the loop issues no other vector memory operation, which the
         // explicit wait below relies on)
-        if (nch > 0) {
+        // one copy of the loop per column kind (R or M, uniform per wave), so
+        // that the step is compiled with its kind fixed
+        auto run = [&](auto m_cols) {
+            constexpr bool IM = decltype(m_cols)::value;
             stage_dma<CK>(rec(0), stage[0], w, lane);
             stage_dma<CK>(rec(1), stage[1], w, lane);
             for (int c = 0; c < nch; c++) {
@@ -1140,9 +1145,13 @@ __device__ __forceinline__ void trans_body(const uint8_t* __restrict__ recs, int
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
                 stage_dma<CK>(rec(c + 2), stage[(c + 2) % 3], w, lane);
-                trans_chunk<CK, NJ>(stage[c % 3], acc, s0, is_m, lane, g4);
+                trans_chunk<CK, NJ>(stage[c % 3], acc, s0, IM, lane, g4);
             }
             __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup's LDS
+        };
+        if (nch > 0) {
+            if (is_m) run(std::true_type{});
+            else run(std::false_type{});
         }
     } else if (nch > 0) {
         // chunk c sits in stage c & 1; its copy passes through register set c & 1
