@@ -68,11 +68,64 @@ void fold_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v, const flo
     store_state<DK, DV, false>(Sv, S);
 }
 
+// One window token as loaded for a multi-token loop: the raw elements of
+// TokenIn (converted when the step needs them), so that a token loaded a
+// step ahead is waited for only where it is used.  Every thread loads
+// (channel indices past DK are clamped and their values zeroed at use), so
+// the loads are unconditional and the compiler's wait counts exact.
+template <int DK, int DV, typename Tin> struct TokenRaw {
+    static constexpr int KPT = TokenIn<DK, DV>::KPT;
+    Tin k[KPT], q[KPT], v[4];
+    float z[KPT], b;
+};
+
+template <int DK, int DV, typename Tin, bool WITH_Q>
+__device__ __forceinline__ void load_token_raw(TokenRaw<DK, DV, Tin>& r, const Tin* __restrict__ kt,
+                                               const Tin* __restrict__ vt, const float* __restrict__ zt,
+                                               const float* __restrict__ bt, const Tin* __restrict__ qt) {
+    using SL = StateLayout<DK, DV, false>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < TokenRaw<DK, DV, Tin>::KPT; j++) {
+        const int i = min(t + j * SL::NT, DK - 1);
+        r.z[j] = zt[i];
+        r.k[j] = kt[i];
+        if (WITH_Q) r.q[j] = qt[i];
+    }
+    const int c0 = SL::col0(t);
+#pragma unroll
+    for (int c = 0; c < 4; c++) r.v[c] = vt[c0 + c];
+    r.b = *bt;
+}
+
+template <int DK, int DV, typename Tin, bool WITH_Q>
+__device__ __forceinline__ void cook_token(const TokenRaw<DK, DV, Tin>& r, TokenIn<DK, DV>& in) {
+    using SL = StateLayout<DK, DV, false>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < TokenIn<DK, DV>::KPT; j++) {
+        const bool live = t + j * SL::NT < DK;
+        in.z[j] = live ? r.z[j] : 0.f;
+        in.k[j] = live ? to_f32(r.k[j]) : 0.f;
+        in.q[j] = live && WITH_Q ? to_f32(r.q[j]) : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) in.v[c] = to_f32(r.v[c]);
+    in.b = r.b;
+}
+
+// s_waitcnt immediate for "no vector memory operation outstanding" (vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
 // Verify pass of the same draft window ([K3-ATTN §6.2]): from the checkpoint
 // state, the outputs of every window token, with exactly the decode step
 // above, the state held in registers and never written back (the accepted
 // prefix is committed afterwards by the fold).  Window layout: q, k, z
-// [N, W, H, DK]; v, o [N, W, H, DV]; b [N, W, H].
+// [N, W, H, DK]; v, o [N, W, H, DV]; b [N, W, H].  Token t + 1 is loaded
+// during step t into the other of two register sets (the loop runs two
+// tokens per turn, so no set is copied), and the state and token 0 have
+// landed before the loop: the loop never waits on a load it does not use.
 template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__((DV / 4) * (DK / 16))
 void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -82,26 +135,40 @@ void verify_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 {
     const int nh = blockIdx.x;          // sequence * H + head
     const int n = nh / H, h = nh % H;
+    if (W <= 0) return;
     __shared__ float s_al[DK], s_k[DK], s_q[DK], s_qk[DK / 16];
     __shared__ __align__(16) float s_red[2][DK / 16][DV];
-    // token t's inputs are loaded during step t - 1 (as in the fold)
-    auto token = [&](TokenIn<DK, DV>& in, int t) {
-        const size_t tok = ((size_t)n * W + t) * H + h;
-        load_token<DK, DV, Tin, true, kModeKDA, false>(in, k + tok * DK, v + tok * DV, z + tok * DK,
-                                                       bl[tok], q + tok * DK);
+    auto token = [&](TokenRaw<DK, DV, Tin>& r, int t) {     // index clamped into the window
+        const size_t tok = ((size_t)n * W + min(t, W - 1)) * H + h;
+        load_token_raw<DK, DV, Tin, true>(r, k + tok * DK, v + tok * DV, z + tok * DK, bl + tok, q + tok * DK);
     };
-    TokenIn<DK, DV> cur, nxt;
-    if (W > 0) token(cur, 0);
+    TokenRaw<DK, DV, Tin> ra, rb;
+    token(ra, 0);
     float4 Sv[16];
     load_state<DK, DV, false>(Sv, state + (size_t)nh * DK * DV);
     const float ea = expf(A[h]);
-    for (int t = 0; t < W; t++) {
-        if (t + 1 < W) token(nxt, t + 1);
-        if (t > 0) __syncthreads();     // the previous step's readers of the LDS vectors are done
-        kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, cur, ea,
-                                                                  o + (((size_t)n * W + t) * H + h) * DV,
-                                                                  s_al, s_k, s_q, s_red, s_qk);
-        cur = nxt;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    for (int t = 0;; t += 2) {
+        token(rb, t + 1);
+        {
+            if (t > 0) __syncthreads();
+            TokenIn<DK, DV> in;
+            cook_token<DK, DV, Tin, true>(ra, in);
+            kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, in, ea,
+                                                                      o + (((size_t)n * W + t) * H + h) * DV,
+                                                                      s_al, s_k, s_q, s_red, s_qk);
+        }
+        if (t + 1 >= W) break;
+        token(ra, t + 2);
+        {
+            __syncthreads();
+            TokenIn<DK, DV> in;
+            cook_token<DK, DV, Tin, true>(rb, in);
+            kda_token_step<DK, DV, Tin, true, kModeKDA, false, false>(Sv, in, ea,
+                                                                      o + (((size_t)n * W + t + 1) * H + h) * DV,
+                                                                      s_al, s_k, s_q, s_red, s_qk);
+        }
+        if (t + 2 >= W) break;
     }
 }
 
