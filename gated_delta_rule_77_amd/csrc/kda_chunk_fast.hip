@@ -1210,11 +1210,11 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
 // Segment starts, fp32: per (sequence, head, 16 columns), S_start(0) = h0 and
 // S_start(j+1) = M_j S_start(j) + R_j, sequentially over the segments.  A
 // sequence without chunks gets hT = h0 here.  M_j is staged in LDS; wave w
-// computes state rows [32w, 32w + 32) with fp32 MFMA, each lane holding the
-// C-tile elements (rows 32w + 16b + 4g + e, column 16*slice + n).
+// (of 8) computes state rows [16w, 16w + 16) with fp32 MFMA, each lane
+// holding the C-tile elements (rows 16w + 4g4 + e, column 16*slice + n16).
 // grid: ceil(N*H / 8) * 64 blocks; the 8 slices of one (sequence, head) are
 // 8 blocks apart (same XCD), so they read M_j and R_j through one L2.
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(512)
 void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ h0,
                     const float* __restrict__ rm, float* __restrict__ sstart,
                     float* __restrict__ hT, int N, int H)
@@ -1228,79 +1228,54 @@ void compose_kernel(const int2* __restrict__ seqsegs, const float* __restrict__ 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int col = 16 * sl + n16;
+    const int row0 = 16 * w + 4 * g4;          // this lane's rows: row0 + e
     __shared__ __align__(16) float sM[128 * 132];
     __shared__ float sSt[128 * 17];
 
-    f32x4 x[2];
+    f32x4 x;
 #pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = 32 * w + 16 * b + 4 * g4 + e;
-            x[b][e] = h0 ? h0[((size_t)p * 128 + row) * 128 + col] : 0.f;
-        }
+    for (int e = 0; e < 4; e++) x[e] = h0 ? h0[((size_t)p * 128 + row0 + e) * 128 + col] : 0.f;
     const int2 ss = seqsegs[n];
     if (ss.y == 0) {
         if (hT)
 #pragma unroll
-            for (int b = 0; b < 2; b++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int row = 32 * w + 16 * b + 4 * g4 + e;
-                    hT[((size_t)p * 128 + row) * 128 + col] = x[b][e];
-                }
+            for (int e = 0; e < 4; e++) hT[((size_t)p * 128 + row0 + e) * 128 + col] = x[e];
         return;
     }
     for (int j = 0; j < ss.y; j++) {
         const size_t seg = (size_t)(ss.x + j);
 #pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = 32 * w + 16 * b + 4 * g4 + e;
-                sstart[((seg * H + h) * 128 + row) * 128 + col] = x[b][e];
-            }
+        for (int e = 0; e < 4; e++) sstart[((seg * H + h) * 128 + row0 + e) * 128 + col] = x[e];
         if (j == ss.y - 1) break;
         const float* RM = rm + (seg * H + h) * 128 * 256;
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; e++) r[e] = RM[(size_t)(row0 + e) * 256 + col];
         __syncthreads();                       // previous step done with sM, sSt
 #pragma unroll
-        for (int i = 0; i < 16; i++) {         // M = columns 128..255 of [R | M]
-            const int idx = i * 256 + tid;     // float4 index over 128 rows x 32 float4
+        for (int i = 0; i < 8; i++) {          // M = columns 128..255 of [R | M]
+            const int idx = i * 512 + tid;     // float4 index over 128 rows x 32 float4
             const int row = idx >> 5, c4 = idx & 31;
             *reinterpret_cast<float4*>(sM + row * 132 + 4 * c4) =
                 *reinterpret_cast<const float4*>(RM + (size_t)row * 256 + 128 + 4 * c4);
         }
 #pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) sSt[(32 * w + 16 * b + 4 * g4 + e) * 17 + n16] = x[b][e];
+        for (int e = 0; e < 4; e++) sSt[(row0 + e) * 17 + n16] = x[e];
         __syncthreads();
         // the contraction over 128 rows in four independent quarters (four
-        // short accumulation chains per tile instead of one of 32), summed
-        // in a fixed order
-        f32x4 part[2][4];
+        // short accumulation chains instead of one of 32), summed in a fixed
+        // order
+        const float* Ab = sM + (16 * w + n16) * 132;
+        f32x4 part[4];
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
-            const float* Ab = sM + (32 * w + 16 * b + n16) * 132;
+        for (int qk = 0; qk < 4; qk++) {
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int qk = 0; qk < 4; qk++) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int ks = 8 * qk; ks < 8 * qk + 8; ks++)
-                    acc = mfma_f32(Ab[4 * ks + g4], sSt[(4 * ks + g4) * 17 + n16], acc);
-                part[b][qk] = acc;
-            }
+            for (int ks = 8 * qk; ks < 8 * qk + 8; ks++)
+                acc = mfma_f32(Ab[4 * ks + g4], sSt[(4 * ks + g4) * 17 + n16], acc);
+            part[qk] = acc;
         }
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
-            f32x4 acc;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = 32 * w + 16 * b + 4 * g4 + e;
-                acc[e] = RM[(size_t)row * 256 + col];
-            }
-            x[b] = acc + ((part[b][0] + part[b][1]) + (part[b][2] + part[b][3]));
-        }
+        x = r + ((part[0] + part[1]) + (part[2] + part[3]));
     }
 }
 
@@ -1326,7 +1301,7 @@ hipError_t launch_chain(const ChunkArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[0], a.stream)) != hipSuccess) return e;
     const unsigned cblk = (unsigned)(((long long)a.N * a.H + 7) / 8 * 64);
-    hipLaunchKernelGGL(compose_kernel, dim3(cblk), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL(compose_kernel, dim3(cblk), dim3(512), 0, a.stream,
                        seqsegs, a.h0, (const float*)rm, sstart, a.hT, a.N, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.ev5 && (e = hipEventRecord(a.ev5[1], a.stream)) != hipSuccess) return e;
