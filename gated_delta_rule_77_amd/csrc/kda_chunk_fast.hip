@@ -585,6 +585,20 @@ __device__ __forceinline__ bool chains_split(const int* __restrict__ hdr, int H,
     return split_grid && (long long)hdr[1] * H <= kSplitMaxChains;
 }
 
+// Block b of a split grid: the two halves of a chain are 8 blocks apart, so
+// that the round-robin dispatch of blocks to the 8 XCDs puts them on one XCD
+// and both read the chain's chunk records through one L2 (the grid is a
+// multiple of 16; blocks past the last chain find no segment and return).
+__device__ __forceinline__ void split_block(int b, bool split, int& chain, int& half) {
+    if (split) {
+        half = (b >> 3) & 1;
+        chain = ((b >> 4) << 3) | (b & 7);
+    } else {
+        half = 0;
+        chain = b;
+    }
+}
+
 constexpr int kOutNS = 8;       // 16-column slices
 constexpr int kOutDepth = 3;    // record prefetch ring depth (chunks)
 constexpr int kLdO = 136;       // bf16 output staging rows [64][kLdO]
@@ -870,8 +884,8 @@ void seg_out_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ c
                     int split_grid)
 {
     constexpr bool CAN_SPLIT = !DBG && !GATE && CK != kChainDPLR;
-    const int ways = CAN_SPLIT && split_grid ? 2 : 1;
-    const int half = blockIdx.x % ways, chain = blockIdx.x / ways;
+    int chain, half;
+    split_block(blockIdx.x, CAN_SPLIT && split_grid, chain, half);
     const int seg_id = chain / H, h = chain % H;
     if (seg_id >= hdr[1]) return;
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
@@ -1193,8 +1207,8 @@ void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__
                       float* __restrict__ rm, int split_grid)
 {
     constexpr bool DPLR = CK == kChainDPLR;
-    const int ways = split_grid ? 2 : 1;
-    const int half = blockIdx.x % ways, chain = blockIdx.x / ways;
+    int chain, half;
+    split_block(blockIdx.x, split_grid != 0, chain, half);
     const int seg_id = chain / H, h = chain % H;
     if (seg_id >= hdr[1]) return;
     const int4 sg = segs[seg_id];          // (sequence, first chunk, chunks, index in sequence)
@@ -1295,7 +1309,7 @@ hipError_t launch_chain(const ChunkArgs& a) {
     // segment capacity is small; otherwise the grids keep one per chain
     const long long chains = (long long)a.L.seg_cap * a.H;
     const int split_grid = chains <= 2 * kSplitMaxChains ? 1 : 0;
-    const dim3 gc((unsigned)chains), gc2((unsigned)(chains * (split_grid ? 2 : 1)));
+    const dim3 gc((unsigned)chains), gc2((unsigned)(split_grid ? (2 * chains + 15) / 16 * 16 : chains));
     hipLaunchKernelGGL((seg_trans_kernel<CK>), gc2, dim3(512), 0, a.stream, (const uint8_t*)recs,
                        segs, seqsegs, hdr, a.H, rm, split_grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
