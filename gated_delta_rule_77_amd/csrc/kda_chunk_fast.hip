@@ -188,7 +188,12 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const float* __restrict__ conv_w, const bf16* __restrict__ cs0,
                        float l2_eps)
 {
-    const int cid = blockIdx.x / H, h = blockIdx.x % H;   // heads fastest: whole input rows
+    // heads fastest (whole input rows), and the H heads of a chunk on one XCD:
+    // blocks go to the 8 XCDs round-robin, so block 8 s + x takes chunk
+    // 8 (s / H) + x, head s % H, and the heads read the chunk's beta row
+    // (H values per token) through one L2.  The grid is a multiple of 8 H.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int cid = (slot / H) * 8 + xcd, h = slot % H;
     if (cid >= hdr[0]) return;
     const int4 cd = chunks[cid];
     const int tok0 = cd.y, len = cd.z;
@@ -1345,7 +1350,7 @@ hipError_t launch_fast(const ChunkArgs& a) {
     const int* hdr = reinterpret_cast<const int*>(a.ws);
     const int4* chunks = reinterpret_cast<const int4*>(a.ws + a.L.off_chunks);
     uint8_t* recs = a.ws + a.L.off_recs;
-    const dim3 gi((unsigned)((long long)a.L.cap * a.H));
+    const dim3 gi((unsigned)(((long long)a.L.cap + 7) / 8 * 8 * a.H));
     const bf16* cs0 = static_cast<const bf16*>(a.conv_state0);
 #define KDA_INTRA(DBG, CONV, MODE, DBGP)                                                      \
     hipLaunchKernelGGL((fast_intra_kernel<DBG, CONV, MODE>), gi, dim3(256), 0, a.stream,         \
