@@ -113,8 +113,11 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     a.conv_state0 = conv_state0;
     a.l2_eps = l2_eps;
     a.mode = mode;
+    // equal-length sequences on the MFMA path: the bookkeeping is planned here
+    // and written by the intra launch (no launch of its own)
+    if (fast && !cu) a.fx = plan_fixed(N, T, chunk, H, L, a.ws);
     hipError_t e = ev ? hipEventRecord(ev[0], a.stream) : hipSuccess;
-    if (e == hipSuccess) e = launch_prep(a);
+    if (e == hipSuccess && !a.fx.on) e = launch_prep(a);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], a.stream);
     if (e == hipSuccess) e = fast ? launch_fast(a) : launch_generic(a, dtype == KDA_BF16);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], a.stream);

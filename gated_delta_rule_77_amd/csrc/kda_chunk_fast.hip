@@ -186,7 +186,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const int* __restrict__ hdr, const int4* __restrict__ chunks, int H,
                        uint8_t* __restrict__ recs, float* __restrict__ dbg,
                        const float* __restrict__ conv_w, const bf16* __restrict__ cs0,
-                       float l2_eps)
+                       float l2_eps, FixedPlan fx)
 {
     // heads fastest (whole input rows), and the H heads of a chunk on one XCD:
     // blocks go to the 8 XCDs round-robin, so block 8 s + x takes chunk
@@ -194,8 +194,18 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // (H values per token) through one L2.  The grid is a multiple of 8 H.
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int cid = (slot / H) * 8 + xcd, h = slot % H;
-    if (cid >= hdr[0]) return;
-    const int4 cd = chunks[cid];
+    // equal-length sequences: the chunk follows from its index, and workgroup
+    // 0 writes the bookkeeping tables for the later launches
+    int4 cd;
+    if (fx.on) {
+        if (blockIdx.x == 0) write_fixed_tables(fx, threadIdx.x, 256);
+        if (cid >= fx.total) return;
+        const int n = cid / fx.cps, j = cid - n * fx.cps;
+        cd = make_int4(n, n * fx.T + j * fx.C, min(fx.C, fx.T - j * fx.C), j * fx.C);
+    } else {
+        if (cid >= hdr[0]) return;
+        cd = chunks[cid];
+    }
     const int tok0 = cd.y, len = cd.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1355,7 +1365,7 @@ hipError_t launch_fast(const ChunkArgs& a) {
 #define KDA_INTRA(DBG, CONV, MODE, DBGP)                                                      \
     hipLaunchKernelGGL((fast_intra_kernel<DBG, CONV, MODE>), gi, dim3(256), 0, a.stream,         \
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.z, a.b, a.A, hdr, \
-                       chunks, a.H, recs, DBGP, a.conv_w, cs0, a.l2_eps)
+                       chunks, a.H, recs, DBGP, a.conv_w, cs0, a.l2_eps, a.fx)
     // the debug and layer variants exist for KDA only (the API enforces it)
     if (a.dbg_intra) KDA_INTRA(true, false, kModeKDA, a.dbg_intra);
     else if (a.conv_w) KDA_INTRA(false, true, kModeKDA, (float*)nullptr);

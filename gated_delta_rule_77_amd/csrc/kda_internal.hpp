@@ -141,6 +141,53 @@ inline WsLayout ws_layout(int B, int T, int H, int dk, int dv, int N, int C, boo
 // logits unread).
 constexpr int kModeKDA = 0, kModeGLA = 1, kModeDeltaNet = 2;
 
+// Chunk bookkeeping of N sequences of T tokens each (no cu_seqlens), planned
+// on the host by the rule of the bookkeeping launch (kda_prep.hip): the intra
+// launch then derives each workgroup's chunk from its index, and its
+// workgroup 0 writes the tables the chain launches read, so that launch is
+// not needed.
+struct FixedPlan {
+    int on;                          // 0: the tables come from the bookkeeping launch
+    int N, T, C, cps;                // sequences, tokens each, chunk size, chunks each
+    int total, per, nseg;            // chunks; chunks per segment; segments per sequence
+    int nseg_total, cap, seg_cap;    // segments (clamped to seg_cap); capacities
+    int* hdr; int2* seqs; int2* seqsegs; int4* chunks; int4* segs;   // workspace tables
+};
+
+// host: the plan of a batch without cu_seqlens on the MFMA path
+FixedPlan plan_fixed(int N, int T, int C, int H, const WsLayout& L, uint8_t* ws);
+
+// The tables of a fixed plan (the same values the bookkeeping launch
+// writes), by the nt threads of one workgroup
+__device__ inline void write_fixed_tables(const FixedPlan& p, int tid, int nt) {
+    if (tid == 0) {
+        p.hdr[0] = p.total;
+        p.hdr[1] = p.nseg_total;
+        p.hdr[2] = p.per;
+    }
+    for (int s = tid; s < p.N; s += nt) {
+        p.seqs[s] = make_int2(s * p.cps, p.cps);
+        const int f = min(s * p.nseg, p.seg_cap);
+        p.seqsegs[s] = make_int2(f, max(0, min(p.nseg, p.seg_cap - f)));
+    }
+    for (int c = tid; c < p.cap; c += nt) {
+        if (c >= p.total) {
+            p.chunks[c] = make_int4(-1, 0, 0, 0);
+        } else {
+            const int n = c / p.cps, j = c - n * p.cps;
+            p.chunks[c] = make_int4(n, n * p.T + j * p.C, min(p.C, p.T - j * p.C), j * p.C);
+        }
+    }
+    for (int g = tid; g < p.seg_cap; g += nt) {
+        if (g >= p.nseg_total) {
+            p.segs[g] = make_int4(-1, 0, 0, 0);
+        } else {
+            const int n = g / p.nseg, j = g - n * p.nseg;
+            p.segs[g] = make_int4(n, n * p.cps + j * p.per, min(p.per, p.cps - j * p.per), j);
+        }
+    }
+}
+
 struct ChunkArgs {
     const void* q; const void* k; const void* v;
     const float* z; const float* b; const float* A;
@@ -159,6 +206,7 @@ struct ChunkArgs {
     const float* conv_w; const void* conv_state0; float l2_eps;
     int mode;                  // kModeKDA, kModeGLA or kModeDeltaNet
     const void* la; const void* lb;   // general DPLR only: the low-rank pair a, b [.., DK]
+    FixedPlan fx;              // MFMA path without cu_seqlens: tables written by the intra launch
 };
 
 // launchers (return hipError_t of the launches)

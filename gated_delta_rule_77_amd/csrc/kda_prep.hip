@@ -1,7 +1,11 @@
 // Chunk bookkeeping for kda_chunk_fwd, done on the device so the host never
 // reads cu_seqlens.  Chunks restart at every sequence start and are numbered
 // sequence by sequence in token order; a sequence shorter than a multiple of
-// the chunk size ends in a short chunk.
+// the chunk size ends in a short chunk.  A batch without cu_seqlens on the
+// MFMA path is planned on the host instead (plan_fixed), and the intra launch
+// writes its tables.
+#include <algorithm>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -281,6 +285,42 @@ void prep_small_kernel(const int* __restrict__ cu, int N, int Tfix, int Ttot, in
     for (int c = t; c < cap; c += 1024) fill_chunk(c, cu, N, Tfix, Ttot, C, total, s_seqs, chunks);
     if (min_seg > 0)
         for (int g = t; g < seg_cap; g += 1024) fill_seg(g, N, nseg_total, per, s_seqs, s_seqsegs, segs);
+}
+
+// The bookkeeping of N sequences of T tokens each, on the host: every
+// sequence has the same chunk count, so the per-sequence scans are products
+// and the segment length is found by the search of the kernels above on the
+// same integers.
+FixedPlan plan_fixed(int N, int T, int C, int H, const WsLayout& L, uint8_t* ws) {
+    FixedPlan p{};
+    p.on = 1;
+    p.N = N; p.T = T; p.C = C;
+    p.cps = (T + C - 1) / C;
+    p.cap = L.cap; p.seg_cap = L.seg_cap;
+    const long long total = std::min((long long)N * p.cps, (long long)L.cap);
+    p.total = (int)total;
+    auto count = [&](long long per) { return (long long)N * ((p.cps + per - 1) / per); };
+    const int max_nc = p.cps;
+    const long long nonempty = count(std::max(max_nc, 1));
+    const long long target = std::max((long long)seg_target(H), nonempty);
+    long long lo = std::max((long long)L.seg_chunks, (total + target - 1) / target);
+    long long hi = target > nonempty ? (total + (target - nonempty) - 1) / (target - nonempty)
+                                     : (long long)max_nc;
+    hi = std::max(hi, lo);
+    if (count(lo) <= target) hi = lo;
+    while (lo < hi) {
+        const long long mid = lo + (hi - lo) / 2;
+        if (count(mid) <= target) hi = mid; else lo = mid + 1;
+    }
+    p.per = (int)lo;
+    p.nseg = (p.cps + p.per - 1) / p.per;
+    p.nseg_total = (int)std::min((long long)N * p.nseg, (long long)L.seg_cap);
+    p.hdr = reinterpret_cast<int*>(ws);
+    p.seqs = reinterpret_cast<int2*>(ws + L.off_seqs);
+    p.seqsegs = reinterpret_cast<int2*>(ws + L.off_seqsegs);
+    p.chunks = reinterpret_cast<int4*>(ws + L.off_chunks);
+    p.segs = reinterpret_cast<int4*>(ws + L.off_segs);
+    return p;
 }
 
 hipError_t launch_prep(const ChunkArgs& a) {

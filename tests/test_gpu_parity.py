@@ -336,6 +336,53 @@ def test_batch_of_fixed_length_sequences(kda):
         assert torch.equal(o1[0], o[bi]) and torch.equal(h1[0], hT[bi])
 
 
+def _table_regions(B, T, H, N, C=64):
+    """Byte ranges of the workspace's bookkeeping: the header (3 int32), the
+    chunk table (cap int4), the sequence and sequence-segment tables (N int2
+    each) and the segment table (seg_cap int4), each region 256-byte aligned
+    after the 256-byte header (the workspace layout the library documents)."""
+    al = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    cap = B * ((T + C - 1) // C) + N
+    nseg = 1 if H >= 256 else 256 // H
+    per = max((cap + nseg - 1) // nseg, 8)
+    per = min(per, cap) if cap > 0 else 1
+    seg_cap = (cap + per - 1) // per + max(N, 1)
+    off_seqs = al(256 + cap * 16)
+    off_seqsegs = al(off_seqs + max(N, 1) * 8)
+    off_segs = al(off_seqsegs + max(N, 1) * 8)
+    return [(0, 12), (256, 256 + cap * 16), (off_seqs, off_seqs + N * 8),
+            (off_seqsegs, off_seqsegs + N * 8), (off_segs, off_segs + seg_cap * 16)]
+
+
+@pytest.mark.parametrize("B,T,H", [(3, 640, 2), (2, 4096, 16), (5, 128, 1), (1, 2560, 12),
+                                   (80, 64, 1), (4, 0, 2)])
+def test_fixed_batch_tables_equal_packed(kda, B, T, H):
+    """B equal-length sequences without cu_seqlens (the chunk and segment
+    tables planned on the host and written by the intra launch) against the
+    same tokens packed with cu_seqlens = 0, T, 2T, ... (the tables written by
+    the bookkeeping launch).  With T a multiple of the chunk both calls use
+    one workspace layout: the header and the chunk, sequence and segment
+    tables agree byte for byte, the outputs and final states bit for bit."""
+    case = KI.PrefillCase("fixedplan", H=H, dk=128, dv=128, chunk=64, dtype="bf16", B=B, T=T,
+                          zero_h0=False)
+    d = to_dev(KI.make_prefill(case, seed=33))
+    nbytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, 128, 128, B, 64, torch.bfloat16)
+    assert nbytes == kda.kda_chunk_fwd_workspace_bytes(1, B * T, H, 128, 128, B, 64, torch.bfloat16)
+    ws_f = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws_p = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    o_f, h_f = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["b"], d["A"],
+                                 initial_state=d["h0"], chunk_size=64, workspace=ws_f)
+    flat = lambda x: x.reshape(1, B * T, *x.shape[2:]).contiguous()   # noqa: E731
+    cu = (torch.arange(B + 1, dtype=torch.int32, device="cuda") * T).contiguous()
+    o_p, h_p = kda.kda_chunk_fwd(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["z"]), flat(d["b"]),
+                                 d["A"], initial_state=d["h0"], cu_seqlens=cu, chunk_size=64,
+                                 workspace=ws_p)
+    torch.cuda.synchronize()
+    for a, e in _table_regions(B, T, H, B):
+        assert torch.equal(ws_f[a:e], ws_p[a:e]), f"bookkeeping bytes [{a}, {e}) differ"
+    assert torch.equal(o_f.reshape(1, B * T, H, 128), o_p) and torch.equal(h_f, h_p)
+
+
 def test_split_prefill_equals_single_pass(kda):
     """prefill(T1) then prefill(T2) from the returned state == prefill(T1 + T2)."""
     case = KI.PrefillCase("split", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=300,
