@@ -674,7 +674,7 @@ struct OutGate {
 };
 
 // 64 rows x 256 bytes of O (or, with GATE, of Sigmoid(gate) * RMSNorm(O)),
-// 16 bytes per lane; with NS = 4 the 128 bytes of the workgroup's column half
+// 16 bytes per lane, stored nontemporally (written once, read by the caller); with NS = 4 the 128 bytes of the workgroup's column half
 // (columns 16 sb ..), staged in sO's first 64 columns.  FULL: every row is
 // inside the sequence (a uniform test by the caller), so the stores need no
 // per-row test.
@@ -704,11 +704,12 @@ __device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[
                 bf16x8 yv;
 #pragma unroll
                 for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
-                *reinterpret_cast<bf16x8*>(o + off) = yv;
+                __builtin_nontemporal_store(yv, reinterpret_cast<bf16x8*>(o + off));
             }
         } else {
             if (FULL || row < len)
-                *reinterpret_cast<uint4*>(o + off) = *reinterpret_cast<const uint4*>(sO + row * kLdO + c8);
+                __builtin_nontemporal_store(*reinterpret_cast<const bf16x8*>(sO + row * kLdO + c8),
+                                            reinterpret_cast<bf16x8*>(o + off));
         }
     }
 }
