@@ -97,7 +97,8 @@ inline int seg_target(int H) { return H >= 256 ? 1 : 256 / H; }
 // the whole capacity, and at least 8 chunks (512 tokens), below which the
 // serial composition of segment starts costs more than the shorter chains
 // save.  The device picks the length from the actual sequence lengths
-// (prep_kernel), never below this, so cap / min + N segments always fit.
+// (prep_kernel; plan_fixed on the host for equal lengths), never below this,
+// so cap / min + N segments always fit.
 inline int pick_seg_chunks(int cap, int H) {
     const long long nseg = seg_target(H);
     long long per = (cap + nseg - 1) / nseg;

@@ -203,7 +203,9 @@ KDA_API kda_status_t kda_chunk_fwd_debug(const void* q, const void* k, const voi
  * Diagnostic variant of kda_chunk_fwd that also records caller-created HIP
  * events on `stream` around its kernels, so a caller can time each stage on
  * the stream the kernels run on: events[0] before the chunk bookkeeping,
- * events[1] after it, events[2] after the intra-chunk kernel (gate, A_kk,
+ * events[1] after it (the two are back to back for equal-length batches on
+ * the MFMA path, whose tables the intra-chunk kernel writes), events[2]
+ * after the intra-chunk kernel (gate, A_kk,
  * A_qk, triangular inverse, W, U), events[3] after the state-chain kernel
  * (inter-chunk state and outputs).  `events` points to n_events >= 4
  * hipEvent_t handles (as void*).  With n_events >= 6 on the MFMA path,
