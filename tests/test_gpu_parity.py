@@ -355,7 +355,7 @@ def _table_regions(B, T, H, N, C=64):
 
 
 @pytest.mark.parametrize("B,T,H", [(3, 640, 2), (2, 4096, 16), (5, 128, 1), (1, 2560, 12),
-                                   (80, 64, 1), (4, 0, 2)])
+                                   (80, 64, 1), (4, 0, 2), (7, 320, 40), (2, 192, 300)])
 def test_fixed_batch_tables_equal_packed(kda, B, T, H):
     """B equal-length sequences without cu_seqlens (the chunk and segment
     tables planned on the host and written by the intra launch) against the
