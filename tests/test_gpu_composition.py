@@ -137,6 +137,51 @@ def test_layer_long_1m_prefix(kda):
     assert ratio <= 1.0
 
 
+def _rel_err_dev(x, ref, rows=1 << 18):
+    """max|x - ref| / max|ref| on the device, in slices along the token axis
+    (the tensors are too large to upcast whole)."""
+    num = den = 0.0
+    for a in range(0, ref.shape[1], rows):
+        xs = x[:, a:a + rows].float()
+        rs = ref[:, a:a + rows].float()
+        num = max(num, float((xs - rs).abs().max()))
+        den = max(den, float(rs.abs().max()))
+    return num / den
+
+
+def test_long_4m_split_consistency(kda):
+    """4,194,304 tokens on 12 heads: 6.4e9 elements per input tensor, past
+    32-bit element offsets, and 21 segments of 3,121 chunks per head.  With
+    the slow-decay gates the call must equal two calls of 2,097,152 tokens
+    joined by the returned state (the second half's outputs and the final
+    state, to the bf16 bar), and the state handed over must matter: the
+    second half's first 4,096 outputs move by more than 10% of their largest
+    value when the second call starts from zero instead."""
+    case = KI.PrefillCase("long_4m", H=12, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=1 << 22,
+                          zero_h0=False)
+    d = _slow(KI.make_prefill(case, device="cuda", seed=5))
+    T, Th = d["T"], d["T"] // 2
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, T, 12, 128, 128, 1, 64, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    run = lambda a, e, h0: kda.kda_chunk_fwd(d["q"][:, a:e], d["k"][:, a:e], d["v"][:, a:e],  # noqa: E731
+                                             d["z"][:, a:e], d["b"][:, a:e], d["A"], initial_state=h0,
+                                             chunk_size=64, workspace=ws)
+    o, hT = run(0, T, d["h0"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(hT).all()
+    _, h_mid = run(0, Th, d["h0"])
+    o2, h2 = run(Th, T, h_mid)
+    o0, _ = run(Th, Th + 4096, None)
+    torch.cuda.synchronize()
+    eo = _rel_err_dev(o2, o[:, Th:])
+    eS = float((h2 - hT).abs().max() / hT.abs().max())
+    head = o2[:, :4096].float()
+    carried = float((head - o0.float()).abs().max() / head.abs().max())
+    report("composition", "4M tokens, one call vs two halves", o_second_half=eo, hT=eS, carried=carried)
+    assert carried > 0.1, "the state at the split carries too little to pin the hand-over"
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
 SWITCH = {"gla": dict(erase=False), "deltanet": dict(decay=False)}
 
 
