@@ -182,6 +182,31 @@ def test_decode_config(kda):
         assert rel_err(st[n, h], S) <= TOL_BF16
 
 
+def test_decode_large_batch_sampled(kda):
+    """One decode step on 32,768 sequences x 12 heads: a 24 GiB fp32 state of
+    6.4e9 elements, so state offsets pass 32 bits.  Sampled (sequence, head)
+    pairs, the first and the last included, against the oracle's step from
+    the same drawn state; every output and the whole new state finite."""
+    N, H = 32768, 12
+    case = KI.DecodeCase("decode_big", N=N, H=H, dk=128, dv=128, steps=1)
+    run = KI.make_decode(case, device="cuda", seed=3)
+    picks = [(0, 0), (N - 1, H - 1), (N // 2, 5), (21845, 7), (N - 2, 0)]
+    before = {p: run["state"][p].double().cpu().numpy() for p in picks}
+    s = run["steps"][0]
+    o = kda.kda_recurrent_step(s["q"], s["k"], s["v"], s["z"], s["b"], run["A"], run["state"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(run["state"]).all()
+    worst = 0.0
+    for n, h in picks:
+        one = lambda x: x[n:n + 1, h:h + 1].cpu()   # noqa: E731
+        o_ref, S_ref = oracle.decode_step(one(s["q"]), one(s["k"]), one(s["v"]), one(s["z"]),
+                                          one(s["b"]), run["A"][h:h + 1].cpu(), before[(n, h)][None, None])
+        eo, eS = rel_err(o[n, h].cpu(), o_ref[0, 0]), rel_err(run["state"][n, h].cpu(), S_ref[0, 0])
+        worst = max(worst, eo, eS)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16
+    _report("decode 32768 x 12 sampled", worst=worst)
+
+
 # ------------------------------------------------------------- smaller cases
 
 @pytest.mark.parametrize("dtype,dk,chunk,T,H", [
