@@ -580,7 +580,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // from the chunk record).
 //
 // Output launch: workgroup = (segment, head), 4 waves, all 128 columns, so
-// each record byte is read once.  Wave w computes V~ and O rows
+// each record byte is read once (a split chain's two halves each read the
+// record, through one L2).  Wave w computes V~ and O rows
 // [16w, 16w + 16) and owns state rows [32w, 32w + 32) as 8 pairs of fp32 C
 // tiles (one pair per 16-column slice).  The bf16 copy of wave w's tiles is
 // exactly the B fragment of k-step w.
@@ -888,7 +889,8 @@ __device__ __forceinline__ void out_body(const uint8_t* __restrict__ recs, const
 }
 
 // grid: seg_cap * H blocks, block = (segment, head), times 2 (the column
-// halves) when split_grid.  With GATE the rows stored are the layer's gated
+// halves, placed by split_block, the grid rounded up to a multiple of 16)
+// when split_grid.  With GATE the rows stored are the layer's gated
 // RMSNorm of O instead of O; the gated, debug and DPLR outputs never split.
 template <bool DBG, bool GATE, int CK>
 __global__ __launch_bounds__(256, 1)
@@ -1214,8 +1216,9 @@ __device__ __forceinline__ void trans_body(const uint8_t* __restrict__ recs, int
             }
 }
 
-// grid: seg_cap * H blocks, block = (segment, head), times 2 (the halves)
-// when split_grid
+// grid: seg_cap * H blocks, block = (segment, head), times 2 (the halves,
+// placed by split_block, the grid rounded up to a multiple of 16) when
+// split_grid
 template <int CK>
 __global__ __launch_bounds__(512, 1)
 void seg_trans_kernel(const uint8_t* __restrict__ recs, const int4* __restrict__ segs,
