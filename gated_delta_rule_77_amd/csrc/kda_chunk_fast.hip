@@ -74,6 +74,18 @@ constexpr int kOffRK = 64 * kLdG * 4;                    // CONV: L2Norm partial
 constexpr int kOffFac = kOffRK + 64 * kLdK * 2 * 2;
 constexpr int kOffBeta = kOffFac + kNFac * 128 * 4;
 constexpr int kSmemIntra = kOffBeta + 64 * 4;            // 80128 bytes: two workgroups per CU
+// 16 bytes per lane from global memory straight to LDS: lane l's bytes land
+// at lds + 16 l (lds is the same for the whole wave)
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// CONV, step 1 (before the factor rows are written): the chunk's gate logits
+// [64][128] after the L2Norm partial sums, the head's taps over the factor rows
+constexpr int kOffZ = kOffRK + 2 * 64 * 4 * 4;
+constexpr int kOffConvW = kOffFac;
+static_assert(kOffZ + 64 * 128 * 4 <= kOffFac, "the gate logits leave the factor rows intact");
+static_assert(kOffConvW + 3 * 128 * 16 <= kOffBeta, "the taps leave beta intact");
 // step 3: partial tiles [20 tiles][3 writers][64 lanes] of f32x4 over L (and
 // below the factor rows, which the partial products still read); A_kk after
 // them (the factor rows are dead by then); N and the inverse's scratch over
@@ -231,19 +243,21 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     uint4 kr[4], qr[4], vr[4];
     float qkf[2][4][8];              // CONV: q, k after Swish, before the L2Norm
     // the beta logits, issued with the first loads so that their latency hides
-    // under the gate scan (wave 0 turns them into beta before the barrier)
+    // under the gate scan (wave 0 turns them into beta before the barrier);
+    // with CONV after the other loads of step 1, just before its first barrier
     float blx = 0.f;
-    if (tid < 64) blx = bl[(size_t)(tok0 + min(tid, lastrow)) * H + h];
+    auto load_beta_logits = [&]() {
+        if (tid < 64) blx = bl[(size_t)(tok0 + min(tid, lastrow)) * H + h];
+    };
+    if constexpr (!CONV) load_beta_logits();
     // the gate logits (thread = channel c, rows 32 half .. 32 half + 31),
-    // likewise issued first; with CONV after the convolution, whose registers
-    // leave no room for them before it
+    // likewise issued first (with CONV they go to LDS beside the
+    // convolution's loads: its registers leave no room for them)
     const int c = tid & 127, half = tid >> 7;
     float lr[32];
-    auto load_gate_logits = [&]() {
+    if constexpr (MODE != kModeDeltaNet && !CONV)
 #pragma unroll
         for (int i = 0; i < 32; i++) lr[i] = z[base + roff(32 * half + i) + c];
-    };
-    if constexpr (MODE != kModeDeltaNet && !CONV) load_gate_logits();
     float* sL2 = reinterpret_cast<float*>(smem + kOffRK);   // CONV: [2][64 rows][4 waves], free in step 1
     if constexpr (!CONV) {
 #pragma unroll
@@ -254,41 +268,67 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             vr[tt] = *reinterpret_cast<const uint4*>(v + base + off);
         }
     } else {
+        // every load of the step is issued before any arithmetic, with no
+        // branch between them (the halo rows from in-bounds addresses,
+        // zeroed afterwards): the three convolutions then wait once
         const int n = cd.x, p0 = cd.w;       // sequence, position of row 0 within it
+        // the head's taps, [3 inputs][128 channels] float4, and the chunk's
+        // gate logits are copied straight to LDS (16 bytes per lane, landing
+        // at the instruction's LDS base + 16 lane): wave w < 3 copies the taps
+        // of input w, every wave 16 rows of logits, two per instruction
+        float4* sW = reinterpret_cast<float4*>(smem + kOffConvW);
+        if (w < 3)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                copy16_to_lds(conv_w + (((size_t)w * H + h) * 128 + 64 * j + lane) * 4, sW + 128 * w + 64 * j);
+        if constexpr (MODE != kModeDeltaNet) {
+            float* sZ = reinterpret_cast<float*>(smem + kOffZ);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int r0 = 16 * w + 2 * i;
+                copy16_to_lds(z + base + roff(r0 + (lane >> 5)) + 4 * (lane & 31), sZ + r0 * 128);
+            }
+        }
+        // xr[X][0]: lanes 13..15 hold the three rows before the chunk (block
+        // -1), from the sequence or, before its start, from the carried state
+        // (zeros without one); xr[X][1 + t]: this lane's row of block t
+        uint4 xr[3][5];
+        const int src = p0 + n16 - 16;       // position in the sequence of the halo row
+        const bool from_seq = src >= 0, from_cs = !from_seq && cs0 != nullptr && src >= -3;
+        const bool halo = n16 >= 13 && (from_seq || from_cs);
 #pragma unroll
         for (int X = 0; X < 3; X++) {
             const bf16* xin = X == 0 ? q : X == 1 ? k : v;
+            const bf16* hp = from_seq ? xin + ((size_t)(tok0 + n16 - 16) * H + h) * 128 + cw
+                           : from_cs ? cs0 + ((((size_t)n * 3 + X) * 3 + (3 + src)) * H + h) * 128 + cw
+                                     : xin + base + roff(n16) + cw;
+            xr[X][0] = *reinterpret_cast<const uint4*>(hp);
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++)
+                xr[X][tt + 1] = *reinterpret_cast<const uint4*>(xin + base + roff(16 * tt + n16) + cw);
+        }
+        load_beta_logits();
+        __syncthreads();
+#pragma unroll
+        for (int X = 0; X < 3; X++) {
+            // one input at a time: the taps of the next are not read early
+            __builtin_amdgcn_sched_barrier(0);
+            if (!halo) xr[X][0] = make_uint4(0, 0, 0, 0);
             float wt[8][4];
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float4 w4 = *reinterpret_cast<const float4*>(conv_w + (((size_t)X * H + h) * 128 + cw + e) * 4);
+                const float4 w4 = sW[X * 128 + cw + e];
                 wt[e][0] = w4.x; wt[e][1] = w4.y; wt[e][2] = w4.z; wt[e][3] = w4.w;
             }
-            // every lane loads its own row of each block once; lanes 13..15 also
-            // hold the three rows before the chunk (block -1), from the sequence
-            // or, before its start, from the carried state (zeros without one)
-            uint4 xr[5];
-            xr[0] = make_uint4(0, 0, 0, 0);
-            if (n16 >= 13) {
-                const int src = p0 + n16 - 16;     // position in the sequence
-                if (src >= 0)
-                    xr[0] = *reinterpret_cast<const uint4*>(xin + ((size_t)(tok0 + n16 - 16) * H + h) * 128 + cw);
-                else if (cs0)
-                    xr[0] = *reinterpret_cast<const uint4*>(
-                        cs0 + ((((size_t)n * 3 + X) * 3 + (3 + src)) * H + h) * 128 + cw);
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; tt++)
-                xr[tt + 1] = *reinterpret_cast<const uint4*>(xin + base + roff(16 * tt + n16) + cw);
 #pragma unroll
             for (int tt = 0; tt < 4; tt++) {
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) y[e] = 0.f;
                 // tap j (oldest first) reads the row 3 - j before this lane's row
-                const uint4 taps[4] = {rows_back<3>(xr[tt], xr[tt + 1], n16),
-                                       rows_back<2>(xr[tt], xr[tt + 1], n16),
-                                       rows_back<1>(xr[tt], xr[tt + 1], n16), xr[tt + 1]};
+                const uint4 taps[4] = {rows_back<3>(xr[X][tt], xr[X][tt + 1], n16),
+                                       rows_back<2>(xr[X][tt], xr[X][tt + 1], n16),
+                                       rows_back<1>(xr[X][tt], xr[X][tt + 1], n16), xr[X][tt + 1]};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const bf16x8 xv = __builtin_bit_cast(bf16x8, taps[j]);
@@ -311,7 +351,8 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     }
                     ss += __shfl_xor(ss, 16, 64);      // the 4 lanes of this row in the wave
                     ss += __shfl_xor(ss, 32, 64);
-                    if (g4 == 0) sL2[(X * 64 + 16 * tt + n16) * 4 + w] = ss;
+                    // the four lanes of the row hold the same sum: all store it
+                    sL2[(X * 64 + 16 * tt + n16) * 4 + w] = ss;
                 }
             }
         }
@@ -320,7 +361,11 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         float a2 = 0.f;                                 // e^{-e^A z} = 2^(a2 z)
         if constexpr (MODE != kModeDeltaNet) {
             a2 = -expf(A[h]) * kLog2e;
-            if constexpr (CONV) load_gate_logits();
+            if constexpr (CONV) {
+                const float* sZ = reinterpret_cast<const float*>(smem + kOffZ);
+#pragma unroll
+                for (int i = 0; i < 32; i++) lr[i] = sZ[(32 * half + i) * 128 + c];
+            }
         }
         float run = 0.f;
 #pragma unroll
@@ -343,7 +388,7 @@ void fast_intra_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
             for (int tt = 0; tt < 4; tt++) {
                 const float4 p4 = *reinterpret_cast<const float4*>(sL2 + (X * 64 + 16 * tt + n16) * 4);
-                const float inv = 1.f / sqrtf(((p4.x + p4.y) + (p4.z + p4.w)) + l2_eps);
+                const float inv = __builtin_amdgcn_rsqf(((p4.x + p4.y) + (p4.z + p4.w)) + l2_eps);
                 bf16x8 o8;
 #pragma unroll
                 for (int e = 0; e < 8; e++) o8[e] = (bf16)(qkf[X][tt][e] * inv);
@@ -699,12 +744,17 @@ __device__ __forceinline__ void store_rows(const bf16* sO, const bf16x8 (&gpre)[
             }
 #pragma unroll
             for (int m = 8; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);   // the row's 16 lanes
-            const float r = 1.f / sqrtf(ss * (1.f / 128.f) + og.eps);
+            // hardware reciprocal square root and reciprocal (about 1 ulp;
+            // the result is rounded to bf16)
+            const float r = __builtin_amdgcn_rsqf(ss * (1.f / 128.f) + og.eps);
             if (FULL || row < len) {
                 const bf16x8 gt = gpre[i];
                 bf16x8 yv;
 #pragma unroll
-                for (int e = 0; e < 8; e++) yv[e] = (bf16)(sigmoid_f<false>((float)gt[e]) * (ov[e] * r) * og.w[e]);
+                for (int e = 0; e < 8; e++) {
+                    const float sg = __builtin_amdgcn_rcpf(1.f + ex2(-(float)gt[e] * kLog2e));
+                    yv[e] = (bf16)(sg * (ov[e] * r) * og.w[e]);
+                }
                 __builtin_nontemporal_store(yv, reinterpret_cast<bf16x8*>(o + off));
             }
         } else {
