@@ -114,6 +114,15 @@ def test_layer_fwd_without_states(kda):
     _check_layer(kda, data, TOL_BF16, "no states")
 
 
+def test_layer_fwd_equal_length_batch(kda):
+    """Several equal-length sequences of several chunks without cu_seqlens
+    (the host-planned chunk tables): each chunk's convolution reaches back into
+    its own sequence, or for a first chunk into that sequence's carried state."""
+    case = KI.PrefillCase("layer", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=3, zero_h0=False)
+    data = KI.make_layer(case, T=200, seed=47)
+    _check_layer(kda, data, TOL_BF16, "equal-length batch")
+
+
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("fp32", 16, 16)])
 def test_layer_fwd_varlen_short_and_empty(kda, dtype, d, chunk):
     """Packed sequences including ones shorter than the convolution (their
