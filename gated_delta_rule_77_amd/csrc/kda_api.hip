@@ -1,5 +1,6 @@
 // C ABI of libkda: argument validation, workspace sizing and dispatch.
 // Declarations and the contract of every entry point are in include/kda.h.
+#include <initializer_list>
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
 
@@ -41,6 +42,16 @@ hipError_t noalloc_scratch(void** out) {
 }
 
 bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// every pointer given that is not NULL is 16-byte aligned, as the header
+// requires of tensor pointers: the kernels move rows with 16-byte loads,
+// stores and direct-to-LDS copies, so a misaligned tensor is refused here,
+// before anything is enqueued
+bool aligned16(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+    return true;
+}
 
 bool mode_ok(int m) { return m == kModeKDA || m == kModeGLA || m == kModeDeltaNet; }
 static_assert(KDA_MODE_KDA == kModeKDA && KDA_MODE_GLA == kModeGLA &&
@@ -93,6 +104,7 @@ kda_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     const bool gated = mode != kModeDeltaNet;    // DeltaNet reads no gate logits
     if (tokens > 0 && (!q || !k || !v || (gated && !z) || !b || !o)) return KDA_ERR_INVALID_ARG;
     if (gated && !A) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q, k, v, z, o, h0, hT, gate, conv_w, conv_state0})) return KDA_ERR_INVALID_ARG;
     const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
     const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, fast);
     if (L.total == 0) return KDA_ERR_INVALID_ARG;
@@ -156,7 +168,7 @@ extern "C" {
 const char* kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
-        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (a NULL or misaligned pointer, or a size out of range)";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: shape or dtype not supported";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, too small or misaligned";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
@@ -260,6 +272,7 @@ kda_status_t kda_recurrent_step_mode(const void* q, const void* k, const void* v
     const bool gated = mode != KDA_MODE_DELTANET;
     if (!q || !k || !v || (gated && (!g_logits || !A)) || !beta_logits || !state || !o)
         return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q, k, v, g_logits, state, o})) return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_decode(q, k, v, g_logits, beta_logits, A, state, o, N, H, dk, dv,
                                  dtype == KDA_BF16, static_cast<hipStream_t>(stream), mode);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -305,6 +318,7 @@ kda_status_t run_dplr(const void* q, const void* k, const void* v, const void* a
     if ((long long)B * T > 0 && (!q || !k || !v || !a || !b || !g_logits || !o))
         return KDA_ERR_INVALID_ARG;
     if (!A) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q, k, v, a, b, g_logits, o, h0, hT})) return KDA_ERR_INVALID_ARG;
     const bool fast = use_fast_path(dk, dv, chunk, dtype == KDA_BF16);
     const WsLayout L = ws_layout(B, T, H, dk, dv, N, chunk, fast, true);
     if (L.total == 0) return KDA_ERR_INVALID_ARG;
@@ -363,6 +377,7 @@ kda_status_t kda_dplr_recurrent_step(const void* q, const void* k, const void* v
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !a || !b || !g_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q, k, v, a, b, g_logits, state, o})) return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_dplr_decode(q, k, v, a, b, g_logits, A, state, o, N, H, dk,
                                       dtype == KDA_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -390,6 +405,8 @@ kda_status_t kda_layer_fwd(const void* q_in, const void* k_in, const void* v_in,
     if (tokens > 0 && (!q_in || !k_in || !v_in || !g_logits || !beta_logits || !gate || !y))
         return KDA_ERR_INVALID_ARG;
     if (!A || !conv_w || !norm_w) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q_in, k_in, v_in, conv_w, conv_state0, conv_stateT, g_logits, gate, y, h0, hT}))
+        return KDA_ERR_INVALID_ARG;
     const LayerWs W = layer_ws(B, T, H, d, N, chunk, dtype);
     if (W.total == 0) return KDA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < W.total) return KDA_ERR_WORKSPACE;
@@ -440,6 +457,8 @@ kda_status_t kda_layer_step(const void* q_in, const void* k_in, const void* v_in
     if (!q_in || !k_in || !v_in || !conv_w || !conv_state || !g_logits || !beta_logits || !A ||
         !state || !gate || !norm_w || !y)
         return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q_in, k_in, v_in, conv_w, conv_state, g_logits, state, gate, y}))
+        return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_layer_step(q_in, k_in, v_in, conv_w, conv_state, g_logits, beta_logits, A,
                                      state, gate, norm_w, l2_eps, rms_eps, y, N, H, d,
                                      dtype == KDA_BF16, static_cast<hipStream_t>(stream));
@@ -457,6 +476,7 @@ kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v,
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0 || W == 0) return KDA_OK;
     if (!q || !k || !v || !g_logits || !beta_logits || !A || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({q, k, v, g_logits, state, o})) return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_verify(q, k, v, g_logits, beta_logits, A, state, o, N, W, H, dk, dv,
                                  dtype == KDA_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -472,6 +492,7 @@ kda_status_t kda_recurrent_fold(const void* k, const void* v, const float* g_log
     if (!decode_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (N == 0 || W == 0) return KDA_OK;
     if (!k || !v || !g_logits || !beta_logits || !A || !n_accept || !state) return KDA_ERR_INVALID_ARG;
+    if (!aligned16({k, v, g_logits, state})) return KDA_ERR_INVALID_ARG;
     hipError_t e = launch_fold(k, v, g_logits, beta_logits, A, n_accept, state, N, W, H, dk, dv,
                                dtype == KDA_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

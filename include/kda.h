@@ -27,8 +27,10 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
- *     the stated row-major layout and 16-byte aligned.  The library never
- *     allocates, frees or keeps them.
+ *     the stated row-major layout and 16-byte aligned (the entry points refuse
+ *     a misaligned row tensor -- q, k, v, o, y, gate logits, states, taps --
+ *     with KDA_ERR_INVALID_ARG).  The library never allocates, frees or keeps
+ *     them.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; nothing synchronises the host.
  *     No entry point allocates memory, synchronises or clears memory with a
@@ -63,7 +65,8 @@ extern "C" {
 
 typedef enum {
     KDA_OK = 0,
-    KDA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative or inconsistent size   */
+    KDA_ERR_INVALID_ARG = 1,   /* NULL or misaligned pointer, negative or       */
+                               /* inconsistent size                             */
     KDA_ERR_UNSUPPORTED = 2,   /* (d_k, d_v, chunk, dtype) not compiled in      */
     KDA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required     */
     KDA_ERR_HIP = 4,           /* a kernel launch failed                         */

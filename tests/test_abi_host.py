@@ -337,3 +337,62 @@ def test_work_item_and_offset_limits_are_validated(L):
     lw.restype = ctypes.c_size_t
     assert lw(1, 100000000, 1, 16, 1, 16, 0) == 0
     assert lw(1, 1000000, 1, 16, 1, 16, 0) > 0
+
+
+def test_misaligned_row_tensors_are_refused(L):
+    """The header requires 16-byte aligned tensor pointers; the entry points
+    refuse a misaligned row tensor before anything is enqueued (an aligned
+    call with too small a workspace gets as far as the workspace check)."""
+    vp, i, sz, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    full = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, b=FAKE, A=FAKE, o=FAKE, ws=FAKE, wsb=16)
+    assert _chunk(L, **full) == 3
+    assert _chunk(L, **dict(full, q=FAKE + 8)) == 1
+    assert _chunk(L, **dict(full, o=FAKE + 4)) == 1
+    assert _chunk(L, **dict(full, z=FAKE + 4)) == 1
+    assert _chunk(L, **dict(full, h0=FAKE + 8)) == 1
+    assert _chunk(L, **dict(full, hT=FAKE + 12)) == 1
+    assert _chunk(L, **dict(full, b=FAKE + 4)) == 3       # beta logits: 4-byte reads only
+
+    step = L.kda_recurrent_step
+    step.restype = i
+    step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+    ok = [FAKE] * 8
+    assert step(*(ok[:6] + [FAKE + 4, FAKE]), 4, 2, 128, 128, 1, None) == 1      # state
+    assert step(*([FAKE + 2] + ok[1:]), 4, 2, 128, 128, 1, None) == 1            # q
+
+    fold = L.kda_recurrent_fold
+    fold.restype = i
+    fold.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    assert fold(*([FAKE] * 6 + [FAKE + 4]), 4, 7, 2, 128, 128, 1, None) == 1
+
+    ver = L.kda_recurrent_verify
+    ver.restype = i
+    ver.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    assert ver(*([FAKE] * 7 + [FAKE + 8]), 4, 7, 2, 128, 128, 1, None) == 1        # o
+
+    lstep = L.kda_layer_step
+    lstep.restype = i
+    lstep.argtypes = [vp] * 11 + [fl, fl, vp] + [i] * 4 + [vp]
+    assert lstep(*([FAKE] * 4 + [FAKE + 8] + [FAKE] * 6), 1e-6, 1e-5, FAKE, 4, 2, 128, 1, None) == 1
+
+    lfwd = L.kda_layer_fwd
+    lfwd.restype = i
+    lfwd.argtypes = [vp] * 13 + [fl, fl] + [i] * 7 + [vp, vp, vp, sz, vp]
+    lp = [FAKE] * 10 + [None, FAKE, FAKE]
+    assert lfwd(*lp, 1e-6, 1e-5, 1, 64, 2, 16, 1, 16, 0, FAKE, None, FAKE, 16, None) == 3
+    assert lfwd(*([FAKE + 8] + lp[1:]), 1e-6, 1e-5, 1, 64, 2, 16, 1, 16, 0, FAKE, None, FAKE, 16,
+                None) == 1
+    assert lfwd(*(lp[:3] + [FAKE + 4] + lp[4:]), 1e-6, 1e-5, 1, 64, 2, 16, 1, 16, 0, FAKE, None,
+                FAKE, 16, None) == 1                                             # taps
+
+    dch = L.kda_dplr_chunk_fwd
+    dch.restype = i
+    dch.argtypes = [vp] * 9 + [i] * 8 + [vp, vp, vp, sz, vp]
+    dp = [FAKE] * 7 + [None, None]
+    assert dch(*dp, 1, 64, 2, 16, 16, 1, 16, 0, FAKE, None, FAKE, 16, None) == 3
+    assert dch(*(dp[:3] + [FAKE + 8] + dp[4:]), 1, 64, 2, 16, 16, 1, 16, 0, FAKE, None, FAKE, 16,
+               None) == 1
+    dst = L.kda_dplr_recurrent_step
+    dst.restype = i
+    dst.argtypes = [vp] * 9 + [i] * 5 + [vp]
+    assert dst(*([FAKE] * 7 + [FAKE + 4, FAKE]), 4, 2, 128, 128, 1, None) == 1

@@ -350,6 +350,27 @@ def test_zero_tokens_copies_state(kda):
     assert o.numel() == 0 and torch.equal(hT, inp["h0"])
 
 
+def test_misaligned_tensor_is_refused(kda):
+    """A contiguous view that starts 4 bytes into its storage is refused by
+    the library's 16-byte alignment check (no kernel is launched), and the
+    aligned call on the same values runs."""
+    case = KI.PrefillCase("align", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=64,
+                          zero_h0=False)
+    inp = to_dev(KI.make_prefill(case, seed=2))
+    n = inp["q"].numel()
+    buf = torch.empty(n + 8, dtype=inp["q"].dtype, device=inp["q"].device)
+    buf[2:2 + n].copy_(inp["q"].reshape(-1))
+    q_mis = buf[2:2 + n].view(inp["q"].shape)
+    assert q_mis.is_contiguous() and q_mis.data_ptr() % 16 == 4
+    with pytest.raises(kda.KdaError, match="misaligned"):
+        kda.kda_chunk_fwd(q_mis, inp["k"], inp["v"], inp["z"], inp["b"], inp["A"],
+                          initial_state=inp["h0"])
+    o, hT = kda.kda_chunk_fwd(q_mis.clone(), inp["k"], inp["v"], inp["z"], inp["b"], inp["A"],
+                              initial_state=inp["h0"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_batch_of_fixed_length_sequences(kda):
     """B > 1 without cu_seqlens equals separate calls per sequence."""
     case = KI.PrefillCase("batch", H=2, dk=128, dv=128, chunk=64, dtype="bf16", B=3, T=100,
