@@ -350,6 +350,42 @@ def test_zero_tokens_copies_state(kda):
     assert o.numel() == 0 and torch.equal(hT, inp["h0"])
 
 
+def test_malformed_offsets_are_clamped(kda):
+    """cu_seqlens that break 0 = cu[0] <= ... <= cu[N] = T are clamped into
+    [0, T] on the device (the header's contract).  With T = 200 and cu = [0,
+    120, 60, 500, 10] the sequences are [0, 120), empty, [60, 200) and empty:
+    the final states are defined (each sequence reads only its own tokens) and
+    held to the oracle, the empty ones return h0 exactly, and the output rows
+    that only sequence 0 covers match it (rows two sequences cover are
+    unspecified, but finite).  With cu = [0, 200, 0, 200, 0, 200] three
+    sequences cover every token, 12 chunks against a capacity of 9: the chunks
+    past the capacity are dropped, and the call stays in its buffers."""
+    case = KI.PrefillCase("badcu", H=2, dk=128, dv=128, chunk=64, dtype="bf16", zero_h0=False)
+    inp = KI.make_prefill(case, seed=3, lengths=[50, 50, 50, 50])
+    d = to_dev(inp)
+    d["cu_seqlens"] = torch.tensor([0, 120, 60, 500, 10], dtype=torch.int32, device="cuda")
+    o, hT = gpu_prefill(kda, d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hT).all()
+    q, k, v, z, b = (inp[x][0] for x in ("q", "k", "v", "z", "b"))
+    ro0, rS0 = oracle.recurrence(q[:120], k[:120], v[:120], z[:120], b[:120], inp["A"], inp["h0"][0])
+    _, rS2 = oracle.recurrence(q[60:], k[60:], v[60:], z[60:], b[60:], inp["A"], inp["h0"][2])
+    e0, eo, e2 = rel_err(hT[0], rS0), rel_err(o[0, :60], ro0[:60]), rel_err(hT[2], rS2)
+    _report("malformed cu_seqlens", hT0=e0, o0=eo, hT2=e2)
+    assert e0 <= TOL_BF16 and eo <= TOL_BF16 and e2 <= TOL_BF16
+    assert torch.equal(hT[1], d["h0"][1]) and torch.equal(hT[3], d["h0"][3])
+    inp5 = KI.make_prefill(case, seed=4, lengths=[40] * 5)
+    d5 = to_dev(inp5)
+    d5["cu_seqlens"] = torch.tensor([0, 200, 0, 200, 0, 200], dtype=torch.int32, device="cuda")
+    o, hT = gpu_prefill(kda, d5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hT).all()
+    assert torch.equal(hT[1], d5["h0"][1]) and torch.equal(hT[3], d5["h0"][3])
+    _, rS0 = oracle.recurrence(*(inp5[x][0] for x in ("q", "k", "v", "z", "b")), inp5["A"],
+                               inp5["h0"][0])
+    assert rel_err(hT[0], rS0) <= TOL_BF16
+
+
 def test_misaligned_tensor_is_refused(kda):
     """A contiguous view that starts 4 bytes into its storage is refused by
     the library's 16-byte alignment check (no kernel is launched), and the
